@@ -1,0 +1,312 @@
+#!/usr/bin/env python3
+"""Benchmark of the trellis dequantize-and-multiply hot path on one MI355X.
+
+Workload (the headline): the axis-1 trellis GEMV of the Qwen MLP up
+projection, in 5120 -> out 17408, T 256, L 12, M 1, bf16 activations, f32
+scales, a 4096-entry f32 codebook, seeded uniform random u32 codes. One step
+is one GEMV call (codebook staging, code streaming, window decode, codebook
+gather, scale + bf16 rounding, MFMA dot, reduction, bf16 store). The value is
+the effective HBM bandwidth on packed-code bytes for k = 2; k = 3 and k = 4 are
+timed the same way and reported beside it.
+
+Inputs are resident in HBM before timing starts. Calls rotate over enough
+distinct input sets (>= 2 x 256 MB of codes) that the 256 MB Infinity Cache
+cannot hold them, so the figure is HBM-bound, not cache-bound.
+
+Timing: HIP events recorded on the stream the kernels are launched on (torch's
+current stream, which the binding passes to the C ABI), around exactly K
+back-to-back calls after W warm-up calls, bracketed by device synchronisation.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--extra] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
+MALL_BYTES = 256 << 20
+QWEN_IN, QWEN_OUT = 5120, 17408
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_qwen_up_k2.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "dequant_gemm_trellis_amd", "csrc", f)
+                  for f in ("axis1.hip", "common.hpp")]
+METRIC = "µs/call and effective HBM GB/s, trellis GEMV 5120→17408 k=2/3/4, M=1"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+class Sets:
+    """Rotating device-resident input sets for one projection shape."""
+
+    def __init__(self, shape, M, cfg, n_sets, T, torch, dev, proj0=0):
+        import numpy as np
+
+        from dequant_gemm_trellis_amd import synth
+
+        self.shape, self.M = shape, M
+        self.items = []
+        for i in range(n_sets):
+            p = synth.make_problem(shape, M, cfg, proj=proj0 + i)
+            codes = torch.from_numpy(p.codes.view(np.int32)).to(dev)
+            scales = torch.from_numpy(p.scales).to(dev)
+            x = torch.from_numpy(p.x.view(np.int16)).to(dev).view(torch.bfloat16)
+            if M == 1:
+                x = x.reshape(-1)
+            lut = T.lut_upload(p.lut, device=dev)
+            self.items.append((x, codes, scales, lut))
+            if i == 0:
+                self.first = p
+        self.code_bytes = self.items[0][1].numel() * 4
+
+
+def n_sets_for(code_bytes: int) -> int:
+    return max(2, math.ceil(2 * MALL_BYTES / code_bytes))
+
+
+def time_calls(torch, launch, n_items, steps, warmup):
+    """ms per call over exactly `steps` back-to-back calls (events on the
+    current stream, synchronised on both sides)."""
+    for i in range(warmup):
+        launch(i % n_items)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        launch(i % n_items)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def gemv_bench(T, torch, dev, k, steps, warmup):
+    from dequant_gemm_trellis_amd import synth
+
+    shape = synth.Shape(1, 256, 12, k, QWEN_IN, QWEN_OUT)
+    code_bytes = shape.rows * shape.words_per_row * 4
+    sets = Sets(shape, 1, synth.CONFIG_IDS["qwen_up_gemv"], n_sets_for(code_bytes), T, torch, dev)
+    y = torch.empty(QWEN_OUT, dtype=torch.bfloat16, device=dev)
+    geom = T.Geometry.of(shape)
+
+    def launch(i):
+        x, codes, scales, lut = sets.items[i]
+        T.gemv(x, codes, scales, lut, geom, y=y)
+
+    ms = time_calls(torch, launch, len(sets.items), steps, warmup)
+    warm = time_calls(torch, lambda i: launch(0), 1, max(steps // 4, 10), 5)
+    res = {"us_per_call": ms * 1e3, "gbps": code_bytes / (ms * 1e-3) / 1e9,
+           "frac_hbm": code_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "code_bytes": code_bytes, "rotation_sets": len(sets.items),
+           "us_per_call_mall_resident": warm * 1e3}
+    first = sets.first
+    del sets
+    torch.cuda.empty_cache()
+    return res, first
+
+
+def extra_bench(T, torch, dev, steps, warmup):
+    """Other workloads: axis-0 scatter k=3, prefill M=5/8/16/32, MLP k=4 M=1/32."""
+    from dequant_gemm_trellis_amd import synth
+
+    out = {}
+    C = synth.CONFIG_IDS
+    sh = synth.Shape(0, 256, 12, 3, QWEN_OUT, QWEN_IN)
+    cb = sh.rows * sh.words_per_row * 4
+    sets = Sets(sh, 1, C["qwen_down_scatter"], n_sets_for(cb), T, torch, dev)
+    ws = torch.empty(T.workspace_bytes(sh, 1, T.OP_GEMV_SCATTER) // 4, dtype=torch.float32,
+                     device=dev)
+    y = torch.empty(QWEN_IN, dtype=torch.bfloat16, device=dev)
+    g = T.Geometry.of(sh)
+    ms = time_calls(torch, lambda i: T.gemv_scatter(*sets.items[i], g, workspace=ws, y=y),
+                    len(sets.items), steps, warmup)
+    out["scatter_qwen_down_k3"] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
+    del sets
+    for k in (2, 3, 4):
+        sh = synth.Shape(1, 256, 12, k, QWEN_IN, QWEN_OUT)
+        cb = sh.rows * sh.words_per_row * 4
+        for M in (5, 8, 16, 32):
+            sets = Sets(sh, M, C["qwen_up_prefill"], n_sets_for(cb), T, torch, dev)
+            y = torch.empty((M, QWEN_OUT), dtype=torch.bfloat16, device=dev)
+            g = T.Geometry.of(sh)
+            ms = time_calls(torch, lambda i: T.prefill(*sets.items[i], g, y=y),
+                            len(sets.items), steps, warmup)
+            flops = 2.0 * M * QWEN_IN * QWEN_OUT
+            out[f"prefill_qwen_up_k{k}_M{M}"] = {
+                "us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9,
+                "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+            del sets
+    for M in (1, 32):
+        shapes = [synth.Shape(1, 256, 12, 4, QWEN_IN, QWEN_OUT),
+                  synth.Shape(1, 256, 12, 4, QWEN_IN, QWEN_OUT),
+                  synth.Shape(0, 256, 12, 4, QWEN_OUT, QWEN_IN)]
+        cb = 3 * shapes[0].rows * shapes[0].words_per_row * 4
+        n = n_sets_for(cb)
+        projs = [Sets(s, M, C["qwen_mlp"], n, T, torch, dev, proj0=10 * j)
+                 for j, s in enumerate(shapes)]
+        geoms = [T.Geometry.of(s) for s in shapes]
+        ys = [torch.empty((M, s.out_features), dtype=torch.bfloat16, device=dev) for s in shapes]
+        ws = torch.empty(max(T.workspace_bytes(shapes[2], M, T.OP_PREFILL), 16) // 4,
+                         dtype=torch.float32, device=dev)
+
+        def mlp(i):
+            for j in range(3):
+                x, codes, scales, lut = projs[j].items[i]
+                if M == 1:
+                    if j < 2:
+                        T.gemv(x, codes, scales, lut, geoms[j], y=ys[j].reshape(-1))
+                    else:
+                        T.gemv_scatter(x, codes, scales, lut, geoms[j],
+                                       workspace=ws[: T.workspace_bytes(shapes[2], 1,
+                                                                        T.OP_GEMV_SCATTER) // 4],
+                                       y=ys[j].reshape(-1))
+                else:
+                    T.prefill(x, codes, scales, lut, geoms[j], workspace=ws, y=ys[j])
+
+        ms = time_calls(torch, mlp, n, max(steps // 3, 10), warmup)
+        out[f"mlp_k4_M{M}"] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
+        del projs
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(p, seconds: float):
+    """The oracle (single-threaded C, float64 accumulation) on whole output rows
+    of the same k = 2 GEMV, repeated in 2176-row chunks until `seconds` pass;
+    scaled to a full call."""
+    import oracle
+
+    s = p.shape
+    chunk = 2176
+    rows_done, t0 = 0, time.perf_counter()
+    while True:
+        r0 = rows_done % s.rows
+        r1 = min(s.rows, r0 + chunk)
+        oracle.fused_f64(p.x, p.codes[r0:r1], p.scales[r0:r1], p.lut, 1, s.T, s.L, s.k,
+                         s.in_features, r1 - r0)
+        rows_done += r1 - r0
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_call = el * s.rows / rows_done
+    code_bytes = s.rows * s.words_per_row * 4
+    return {"value": code_bytes / per_call / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "us_per_call": per_call * 1e6,
+            "sample": f"{rows_done} output rows x 5120 inputs of the k=2 GEMV "
+                      f"({el:.1f} s), scaled to the full 17408-row call; "
+                      f"host has {os.cpu_count()} logical cores"}
+
+
+def traffic_entry():
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--extra", action="store_true", help="also time scatter, prefill and MLP")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only-k", type=int, default=0, help="time only this k (profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the multi-GPU sharding is a design "
+              "note (see the design document), so --gpus must be 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not os.path.exists(os.path.join(ROOT, "dequant_gemm_trellis_amd", "libtrellis.so")):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    from dequant_gemm_trellis_amd import trellis as T
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    per_k, first = {}, None
+    for k in ((args.only_k,) if args.only_k else (2, 3, 4)):
+        log(f"bench: gemv k={k} steps={args.steps} warmup={args.warmup}")
+        per_k[str(k)], p = gemv_bench(T, torch, dev, k, args.steps, args.warmup)
+        if k == 2:
+            first = p
+        log(f"bench: gemv k={k}: {json.dumps(per_k[str(k)])}")
+    head = per_k.get("2") or next(iter(per_k.values()))
+
+    extra = None
+    if args.extra:
+        log("bench: extra workloads")
+        extra = extra_bench(T, torch, dev, max(args.steps // 4, 20), 10)
+
+    cpu = None
+    if not args.no_cpu and first is not None:
+        log("bench: oracle cpu baseline")
+        cpu = cpu_baseline(first, args.cpu_seconds)
+
+    achieved = head["gbps"]
+    line = {
+        "metric": METRIC,
+        "value": round(achieved, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["us_per_call"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded uniform u32 codes, N(0,1) f32 codebook, U[0.5,1.5) f32 "
+                "scales, N(0,1) bf16 x)",
+        "config": {"workload": "trellis GEMV qwen-mlp up-projection, axis 1, in 5120 -> out "
+                               "17408, T 256, L 12, k 2 (k 3/4 in per_k), M 1",
+                   "k": 2, "M": 1, "in_features": QWEN_IN, "out_features": QWEN_OUT,
+                   "rotation_sets": head["rotation_sets"]},
+        "per_k": per_k,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_entry(),
+                     "kernel": "axis1_mma_kernel<2,1>",
+                     "bytes_per_launch": head["code_bytes"]},
+        "cpu_baseline": cpu,
+    }
+    if extra is not None:
+        line["extra"] = extra
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

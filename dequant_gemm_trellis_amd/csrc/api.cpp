@@ -1,0 +1,169 @@
+// C-ABI entry points of libtrellis.so: argument validation on the host, then
+// kernel launches on the caller's stream. Nothing is enqueued unless every
+// check passes. Semantics of each entry point are documented in trellis.h.
+//
+// Pages cited: diff views of "@mlx-bun/inference" 0.0.0-stage -> 1.0.0;
+// page 60 tiled-prefill.ts and wide-prefill.ts reject unsupported geometry
+// (T 256, L 12, k 2/3/4, cols a multiple of 256, row-contiguous layout)
+// before any launch; page 59 scatter.ts fixes 128 row splits.
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "trellis.h"
+
+namespace {
+
+constexpr int32_t kMaxFeatures = 1 << 24;
+constexpr uint64_t kMaxWeights = 1ull << 40;
+
+struct Dims {
+    int rows, cols, nb;
+};
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_geometry(const trellis_geometry* g, Dims* d) {
+    if (!g) return TRELLIS_ERR_NULL;
+    if (g->axis != 0 && g->axis != 1) return TRELLIS_ERR_GEOMETRY;
+    if (g->T != 256 || g->L != 12) return TRELLIS_ERR_GEOMETRY;
+    if (g->k < 2 || g->k > 4) return TRELLIS_ERR_GEOMETRY;
+    if (g->in_features < 1 || g->out_features < 1) return TRELLIS_ERR_GEOMETRY;
+    if (g->in_features > kMaxFeatures || g->out_features > kMaxFeatures) return TRELLIS_ERR_GEOMETRY;
+    d->rows = g->axis == 1 ? g->out_features : g->in_features;
+    d->cols = g->axis == 1 ? g->in_features : g->out_features;
+    if (d->cols % g->T != 0) return TRELLIS_ERR_GEOMETRY;
+    if (static_cast<uint64_t>(d->rows) * static_cast<uint64_t>(d->cols) > kMaxWeights)
+        return TRELLIS_ERR_GEOMETRY;
+    d->nb = d->cols / g->T;
+    return TRELLIS_OK;
+}
+
+// Operand checks shared by the compute entry points.
+int check_operands(const void* codes, const float* scales, const float* lut) {
+    if (!codes || !scales || !lut) return TRELLIS_ERR_NULL;
+    if (!aligned(codes, 16) || !aligned(lut, 16) || !aligned(scales, 4)) return TRELLIS_ERR_ALIGN;
+    return TRELLIS_OK;
+}
+
+int check_io(const void* x, const void* y) {
+    if (!x || !y) return TRELLIS_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(y, 16)) return TRELLIS_ERR_ALIGN;
+    return TRELLIS_OK;
+}
+
+// Row splits of the axis-0 kernel: 128 for the scatter GEMV (page 59
+// scatter.ts); for the prefill, 128 up to M = 16 and 64 above, which keeps the
+// float32 partial traffic near 10 MB at the 17408 x 5120 shape.
+int axis0_splits(int M, int op) {
+    if (op == TRELLIS_OP_GEMV_SCATTER) return TRELLIS_SCATTER_SPLITS;
+    return M > 16 ? 64 : 128;
+}
+
+size_t axis0_workspace(const Dims& d, int M, int op) {
+    return static_cast<size_t>(trellis::axis0_split_groups(axis0_splits(M, op))) *
+           static_cast<size_t>(M) * static_cast<size_t>(d.cols) * sizeof(float);
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? TRELLIS_OK : TRELLIS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int trellis_lut_upload(const float* host_lut, int32_t entries, float* dev_lut, hipStream_t stream) {
+    if (!host_lut || !dev_lut) return TRELLIS_ERR_NULL;
+    if (entries != 4096) return TRELLIS_ERR_LUT;
+    if (!aligned(dev_lut, 16)) return TRELLIS_ERR_ALIGN;
+    for (int i = 0; i < entries; ++i)
+        if (!isfinite(host_lut[i])) return TRELLIS_ERR_LUT;
+    const size_t bytes = static_cast<size_t>(entries) * sizeof(float);
+    if (hipMemcpyAsync(dev_lut, host_lut, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
+        return TRELLIS_ERR_HIP;
+    return status_of(hipStreamSynchronize(stream));
+}
+
+int trellis_gemv(const uint16_t* x, const uint32_t* codes, const float* scales, const float* lut,
+                 const trellis_geometry* g, uint16_t* y, hipStream_t stream) {
+    Dims d;
+    int st = check_geometry(g, &d);
+    if (st) return st;
+    if (g->axis != 1) return TRELLIS_ERR_GEOMETRY;
+    if ((st = check_operands(codes, scales, lut)) || (st = check_io(x, y))) return st;
+    return status_of(trellis::launch_axis1(x, 1, codes, scales, lut, y, d.rows, d.nb, g->k, stream));
+}
+
+int trellis_gemv_scatter(const uint16_t* x, const uint32_t* codes, const float* scales,
+                         const float* lut, const trellis_geometry* g, float* workspace,
+                         size_t workspace_bytes, uint16_t* y, hipStream_t stream) {
+    Dims d;
+    int st = check_geometry(g, &d);
+    if (st) return st;
+    if (g->axis != 0) return TRELLIS_ERR_GEOMETRY;
+    if ((st = check_operands(codes, scales, lut)) || (st = check_io(x, y))) return st;
+    if (!workspace) return TRELLIS_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return TRELLIS_ERR_ALIGN;
+    if (workspace_bytes < axis0_workspace(d, 1, TRELLIS_OP_GEMV_SCATTER)) return TRELLIS_ERR_WORKSPACE;
+    return status_of(trellis::launch_axis0(x, 1, codes, scales, lut, workspace, y, d.rows, d.cols,
+                                           axis0_splits(1, TRELLIS_OP_GEMV_SCATTER), g->k, stream));
+}
+
+int trellis_prefill(const uint16_t* x, int32_t M, const uint32_t* codes, const float* scales,
+                    const float* lut, const trellis_geometry* g, float* workspace,
+                    size_t workspace_bytes, uint16_t* y, hipStream_t stream) {
+    Dims d;
+    int st = check_geometry(g, &d);
+    if (st) return st;
+    if (M < 0 || M > TRELLIS_MAX_M) return TRELLIS_ERR_GEOMETRY;
+    if (M == 0) return TRELLIS_OK;
+    if ((st = check_operands(codes, scales, lut)) || (st = check_io(x, y))) return st;
+    if (g->axis == 1)
+        return status_of(trellis::launch_axis1(x, M, codes, scales, lut, y, d.rows, d.nb, g->k, stream));
+    if (!workspace) return TRELLIS_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return TRELLIS_ERR_ALIGN;
+    if (workspace_bytes < axis0_workspace(d, M, TRELLIS_OP_PREFILL)) return TRELLIS_ERR_WORKSPACE;
+    return status_of(trellis::launch_axis0(x, M, codes, scales, lut, workspace, y, d.rows, d.cols,
+                                           axis0_splits(M, TRELLIS_OP_PREFILL), g->k, stream));
+}
+
+size_t trellis_workspace_bytes(const trellis_geometry* g, int32_t M, int32_t op) {
+    Dims d;
+    if (check_geometry(g, &d)) return static_cast<size_t>(-1);
+    switch (op) {
+    case TRELLIS_OP_GEMV:
+        return (g->axis == 1 && M == 1) ? 0 : static_cast<size_t>(-1);
+    case TRELLIS_OP_GEMV_SCATTER:
+        return (g->axis == 0 && M == 1) ? axis0_workspace(d, 1, op) : static_cast<size_t>(-1);
+    case TRELLIS_OP_PREFILL:
+        if (M < 0 || M > TRELLIS_MAX_M) return static_cast<size_t>(-1);
+        return (g->axis == 1 || M == 0) ? 0 : axis0_workspace(d, M, op);
+    default:
+        return static_cast<size_t>(-1);
+    }
+}
+
+int trellis_expand(const uint32_t* codes, const float* scales, const float* lut,
+                   const trellis_geometry* g, uint16_t* w, hipStream_t stream) {
+    Dims d;
+    int st = check_geometry(g, &d);
+    if (st) return st;
+    if ((st = check_operands(codes, scales, lut))) return st;
+    if (!w) return TRELLIS_ERR_NULL;
+    if (!aligned(w, 16)) return TRELLIS_ERR_ALIGN;
+    return status_of(trellis::launch_expand(codes, scales, lut, w, d.rows, d.nb, g->k, stream));
+}
+
+const char* trellis_strerror(int status) {
+    switch (status) {
+    case TRELLIS_OK: return "success";
+    case TRELLIS_ERR_NULL: return "a required pointer is null";
+    case TRELLIS_ERR_GEOMETRY: return "unsupported geometry, axis or batch size for this operation";
+    case TRELLIS_ERR_ALIGN: return "a pointer is not aligned as required (16 bytes; scales 4)";
+    case TRELLIS_ERR_LUT: return "codebook must hold 4096 finite float32 entries";
+    case TRELLIS_ERR_WORKSPACE: return "workspace missing or too small";
+    case TRELLIS_ERR_HIP: return "HIP runtime error while enqueuing work";
+    default: return "unknown trellis status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+/*
+ * trellis.h -- C ABI of libtrellis.so: fused trellis-dequantize-and-multiply
+ * for bitshift-trellis-coded weights on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (diff views of the npm package "@mlx-bun/inference",
+ * 0.0.0-stage -> 1.0.0; page 60: src/kernels/trellis/tiled-prefill.ts,
+ * vector-expand.ts, wide-prefill.ts; page 59: scatter.ts, splitk-prefill.ts):
+ *
+ *   A projection is stored as a matrix [rows][cols] of k-bit codes, cut into
+ *   blocks of T = 256 weights along each row. Axis 1 stores [out][in]
+ *   (y = x W^T); axis 0 stores [in][out] (y = x W), the storage convention of
+ *   tiled-prefill.ts's weight-tile decode.
+ *
+ *   Codes: uint32 words, row-major [rows][cols/T][T*k/32]. The block is a
+ *   T*k-bit string, LSB-first within a word, words ascending. Weight t of a
+ *   block reads the L = 12 bits starting at bit (T-1-t)*k, wrapping to bit 0
+ *   of the same block (tail-biting). That window indexes a 4096-entry float32
+ *   codebook; the entry times the row's float32 scale is rounded to float32
+ *   and then to bf16 (round-to-nearest-even):
+ *       W[r][c] = bf16( fl32( LUT[window(r, c)] * scales[r] ) )
+ *   (page 60 tiled-prefill.ts weight-tile decode and wide-prefill.ts; page 59
+ *   scatter.ts rounds the scaled value before its multiply-add).
+ *   On axis 0 the scale belongs to the stored row, i.e. the input feature.
+ *
+ *   Outputs are bf16, accumulated in float32. The summation order inside a
+ *   call is fixed, so repeated calls give identical bits.
+ *
+ * Conventions for every compute entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller; the library
+ *     allocates nothing and keeps no reference after the call returns.
+ *   - x, codes, lut, y and workspace must be 16-byte aligned; scales 4-byte.
+ *     Arrays are dense and row-major (no strides).
+ *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
+ *     without waiting. All validation happens on the host before anything is
+ *     enqueued: on a negative status nothing was enqueued. A kernel fault
+ *     shows up at the caller's next synchronisation.
+ *   - Geometry accepted: axis in {0, 1}, T = 256, L = 12, k in {2, 3, 4},
+ *     1 <= in_features, out_features <= 2^24, and cols % 256 == 0 (cols is
+ *     in_features on axis 1, out_features on axis 0).
+ */
+#ifndef TRELLIS_H
+#define TRELLIS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Shape of one coded projection (the pages' TrellisGeometry fields). */
+typedef struct trellis_geometry {
+    int32_t axis;          /* 1: stored [out][in], y = x W^T; 0: stored [in][out], y = x W */
+    int32_t T;             /* weights per block; must be 256 */
+    int32_t L;             /* window width in bits; must be 12 */
+    int32_t k;             /* bits per weight: 2, 3 or 4 */
+    int32_t in_features;
+    int32_t out_features;
+} trellis_geometry;
+
+/* Status codes (0 = success, negative = nothing enqueued). */
+enum {
+    TRELLIS_OK = 0,
+    TRELLIS_ERR_NULL = -1,       /* a required pointer is null */
+    TRELLIS_ERR_GEOMETRY = -2,   /* axis, T, L, k, feature counts or M not supported by this op */
+    TRELLIS_ERR_ALIGN = -3,      /* a pointer is not aligned as required */
+    TRELLIS_ERR_LUT = -4,        /* codebook size is not 2^L, or an entry is not finite */
+    TRELLIS_ERR_WORKSPACE = -5,  /* workspace missing or smaller than trellis_workspace_bytes() */
+    TRELLIS_ERR_HIP = -6         /* the HIP runtime reported an error while enqueuing */
+};
+
+/* Operation selector for trellis_workspace_bytes(). */
+enum {
+    TRELLIS_OP_GEMV = 0,
+    TRELLIS_OP_GEMV_SCATTER = 1,
+    TRELLIS_OP_PREFILL = 2
+};
+
+/* Number of row splits of the axis-0 scatter GEMV (page 59 scatter.ts uses
+ * 128 split-K row ranges of ceil(rows/128) rows each). */
+#define TRELLIS_SCATTER_SPLITS 128
+
+/* Largest activation batch accepted by trellis_prefill (page 60
+ * tiled-prefill.ts serves M = 5..32). */
+#define TRELLIS_MAX_M 32
+
+/*
+ * Copy a host codebook of `entries` float32 values into the caller's device
+ * buffer `dev_lut` (4 * entries bytes, 16-byte aligned). The codebook plays
+ * the part of the pages' precise host LUT (page 59 scatter.ts stages `lut`
+ * into threadgroup memory). entries must be 4096 (2^L with L = 12) and every
+ * entry finite, else TRELLIS_ERR_LUT. The copy is ordered on `stream`; the
+ * call waits for it, so `host_lut` may be freed on return.
+ */
+int trellis_lut_upload(const float *host_lut, int32_t entries, float *dev_lut,
+                       hipStream_t stream);
+
+/*
+ * Axis-1 GEMV, one activation row (decode step):
+ *   y[n] = bf16( sum_{k < in} x[k] * W[n][k] ),  n < out.
+ * x: bf16 [in]; codes: uint32 [out][in*k/32]; scales: float32 [out];
+ * lut: float32 [4096] on the device; y: bf16 [out]. g->axis must be 1.
+ * Weights as in page 60 wide-prefill.ts (decode, round to bf16, dot, float
+ * accumulation, bf16 store).
+ */
+int trellis_gemv(const uint16_t *x, const uint32_t *codes, const float *scales,
+                 const float *lut, const trellis_geometry *g, uint16_t *y,
+                 hipStream_t stream);
+
+/*
+ * Axis-0 "scatter" GEMV, one activation row (page 59 scatter.ts):
+ *   partial[s][n] = sum over stored rows r in split s of x[r] * W[r][n]
+ *   y[n]          = bf16( sum_{s=0..127} partial[s][n] ),  s ascending.
+ * Split s covers rows [s*R', min(in, (s+1)*R')) with R' = ceil(in/128).
+ * x: bf16 [in]; codes: uint32 [in][out*k/32]; scales: float32 [in];
+ * lut: float32 [4096]; y: bf16 [out]. g->axis must be 0.
+ * workspace: float32 scratch of at least
+ * trellis_workspace_bytes(g, 1, TRELLIS_OP_GEMV_SCATTER) bytes; its contents
+ * on entry do not matter and are overwritten.
+ */
+int trellis_gemv_scatter(const uint16_t *x, const uint32_t *codes, const float *scales,
+                         const float *lut, const trellis_geometry *g, float *workspace,
+                         size_t workspace_bytes, uint16_t *y, hipStream_t stream);
+
+/*
+ * Small-batch GEMM (prefill), M activation rows, 0 <= M <= 32 (M = 0 is a
+ * no-op that returns TRELLIS_OK):
+ *   axis 1: y[m][n] = bf16( sum_k x[m][k] * W[n][k] )   (page 60 tiled-prefill.ts)
+ *   axis 0: y[m][n] = bf16( sum_r x[m][r] * W[r][n] )   (page 59 splitk-prefill.ts:
+ *           row splits with float32 partials, then an ordered sum)
+ * x: bf16 [M][in]; y: bf16 [M][out]; codes/scales/lut as for the GEMVs.
+ * workspace: float32 scratch of trellis_workspace_bytes(g, M, TRELLIS_OP_PREFILL)
+ * bytes (0 on axis 1, where workspace may be null).
+ */
+int trellis_prefill(const uint16_t *x, int32_t M, const uint32_t *codes, const float *scales,
+                    const float *lut, const trellis_geometry *g, float *workspace,
+                    size_t workspace_bytes, uint16_t *y, hipStream_t stream);
+
+/*
+ * Workspace bytes an operation needs for geometry g and batch M (0 if it
+ * needs none). Returns (size_t)-1 if g, M or op is not supported.
+ */
+size_t trellis_workspace_bytes(const trellis_geometry *g, int32_t M, int32_t op);
+
+/*
+ * Diagnostic export of the decoded weights (page 60 vector-expand.ts):
+ *   w[r][c] = bf16( fl32( LUT[window(r, c)] * scales[r] ) ),  w is bf16 [rows][cols].
+ * Uses the same decoder as the fused operations. Not on the hot path.
+ */
+int trellis_expand(const uint32_t *codes, const float *scales, const float *lut,
+                   const trellis_geometry *g, uint16_t *w, hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char *trellis_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRELLIS_H */

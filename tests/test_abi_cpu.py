@@ -1,0 +1,178 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function include/trellis.h declares, and rejects bad arguments on the host
+before touching the HIP runtime (nothing is enqueued on error). No compute
+call is made here; fake device addresses are only ever passed alongside an
+argument the host checks reject.
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "trellis.h")
+LIB = os.path.join(ROOT, "dequant_gemm_trellis_amd", "libtrellis.so")
+
+
+@pytest.fixture(scope="module")
+def T():
+    if not os.path.exists(LIB):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    from dequant_gemm_trellis_amd import trellis
+
+    return trellis
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(trellis_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_scatter", "trellis_prefill"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(T):
+    lib = T.raw()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(T.EXPORTED)
+    nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (trellis_\w+)$", nm, flags=re.M))
+    assert exported == set(declared_functions())
+
+
+def test_library_does_not_link_torch(T):
+    out = subprocess.run(["ldd", LIB], capture_output=True, text=True).stdout
+    assert "torch" not in out and "c10" not in out
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced (every call below fails validation)
+
+
+def geom(T, axis=1, Tb=256, L=12, k=2, i=512, o=256):
+    return T.Geometry(axis, Tb, L, k, i, o)
+
+
+def call_gemv(T, g, x=FAKE, codes=FAKE, scales=FAKE, lut=FAKE, y=FAKE):
+    return T.raw().trellis_gemv(C.c_void_p(x), C.c_void_p(codes), C.c_void_p(scales),
+                                C.c_void_p(lut), C.byref(g) if g is not None else None,
+                                C.c_void_p(y), C.c_void_p(0))
+
+
+@pytest.mark.parametrize("field,value", [("axis", 2), ("axis", -1), ("T", 128), ("L", 11),
+                                         ("k", 1), ("k", 5), ("in_features", 0),
+                                         ("out_features", 0), ("in_features", 300),
+                                         ("in_features", (1 << 24) + 256)])
+def test_gemv_rejects_bad_geometry(T, field, value):
+    g = geom(T)
+    setattr(g, field, value)
+    assert call_gemv(T, g) == T.ERR_GEOMETRY
+
+
+def test_gemv_rejects_wrong_axis(T):
+    assert call_gemv(T, geom(T, axis=0, i=256, o=512)) == T.ERR_GEOMETRY
+
+
+def test_gemv_rejects_null(T):
+    assert call_gemv(T, None) == T.ERR_NULL
+    for arg in ("x", "codes", "scales", "lut", "y"):
+        assert call_gemv(T, geom(T), **{arg: 0}) == T.ERR_NULL, arg
+
+
+@pytest.mark.parametrize("arg,addr", [("x", FAKE + 2), ("codes", FAKE + 4), ("lut", FAKE + 8),
+                                      ("y", FAKE + 2), ("scales", FAKE + 2)])
+def test_gemv_rejects_misaligned(T, arg, addr):
+    assert call_gemv(T, geom(T), **{arg: addr}) == T.ERR_ALIGN
+
+
+def test_scatter_validation(T):
+    lib = T.raw()
+    g = geom(T, axis=0, i=17408, o=5120, k=3)
+    need = T.workspace_bytes(g, 1, T.OP_GEMV_SCATTER)
+    assert need > 0 and need % 16 == 0
+
+    def call(g, ws=FAKE, nbytes=need):
+        return lib.trellis_gemv_scatter(C.c_void_p(FAKE), C.c_void_p(FAKE), C.c_void_p(FAKE),
+                                        C.c_void_p(FAKE), C.byref(g), C.c_void_p(ws), nbytes,
+                                        C.c_void_p(FAKE), C.c_void_p(0))
+
+    assert call(g, nbytes=need - 4) == T.ERR_WORKSPACE
+    assert call(g, ws=0) == T.ERR_WORKSPACE
+    assert call(g, ws=FAKE + 4, nbytes=need) == T.ERR_ALIGN
+    assert call(geom(T, axis=1, i=5120, o=17408)) == T.ERR_GEOMETRY
+    assert call(geom(T, axis=0, i=17408, o=5000)) == T.ERR_GEOMETRY
+
+
+def test_prefill_validation(T):
+    lib = T.raw()
+
+    def call(M, g, ws=0, nbytes=0, x=FAKE):
+        return lib.trellis_prefill(C.c_void_p(x), M, C.c_void_p(FAKE), C.c_void_p(FAKE),
+                                   C.c_void_p(FAKE), C.byref(g), C.c_void_p(ws), nbytes,
+                                   C.c_void_p(FAKE), C.c_void_p(0))
+
+    g1 = geom(T, axis=1, i=5120, o=17408)
+    assert call(33, g1) == T.ERR_GEOMETRY
+    assert call(-1, g1) == T.ERR_GEOMETRY
+    assert call(0, g1, x=0) == T.OK  # M = 0: nothing to do, nothing enqueued
+    g0 = geom(T, axis=0, i=17408, o=5120, k=4)
+    need = T.workspace_bytes(g0, 32, T.OP_PREFILL)
+    assert need > 0
+    assert call(32, g0, ws=FAKE, nbytes=need - 1) == T.ERR_WORKSPACE
+    assert call(32, g0) == T.ERR_WORKSPACE
+    assert T.workspace_bytes(g1, 32, T.OP_PREFILL) == 0
+
+
+def test_workspace_bytes(T):
+    g0 = geom(T, axis=0, i=17408, o=5120, k=3)
+    # 128 splits summed four at a time inside the kernel: 32 float32 partial rows
+    assert T.workspace_bytes(g0, 1, T.OP_GEMV_SCATTER) == 32 * 5120 * 4
+    assert T.workspace_bytes(geom(T), 1, T.OP_GEMV) == 0
+    with pytest.raises(T.TrellisError):
+        T.workspace_bytes(geom(T), 2, T.OP_GEMV)
+    with pytest.raises(T.TrellisError):
+        T.workspace_bytes(geom(T, k=7), 1, T.OP_GEMV)
+    with pytest.raises(T.TrellisError):
+        T.workspace_bytes(geom(T), 1, 9)
+
+
+def test_lut_upload_validation(T):
+    lib = T.raw()
+    good = np.zeros(4096, dtype=np.float32)
+
+    def up(h, n, dev=FAKE):
+        return lib.trellis_lut_upload(C.c_void_p(h.ctypes.data) if h is not None else None, n,
+                                      C.c_void_p(dev), C.c_void_p(0))
+
+    assert up(good, 4095) == T.ERR_LUT
+    bad = good.copy()
+    bad[17] = np.inf
+    assert up(bad, 4096) == T.ERR_LUT
+    bad[17] = np.nan
+    assert up(bad, 4096) == T.ERR_LUT
+    assert up(good, 4096, FAKE + 4) == T.ERR_ALIGN
+    assert up(None, 4096) == T.ERR_NULL
+
+
+def test_expand_validation(T):
+    lib = T.raw()
+    g = geom(T)
+    assert lib.trellis_expand(C.c_void_p(FAKE), C.c_void_p(FAKE), C.c_void_p(FAKE), C.byref(g),
+                              None, C.c_void_p(0)) == T.ERR_NULL
+    assert lib.trellis_expand(C.c_void_p(FAKE), C.c_void_p(FAKE), C.c_void_p(FAKE), C.byref(g),
+                              C.c_void_p(FAKE + 2), C.c_void_p(0)) == T.ERR_ALIGN
+
+
+def test_strerror(T):
+    for s in (T.OK, T.ERR_NULL, T.ERR_GEOMETRY, T.ERR_ALIGN, T.ERR_LUT, T.ERR_WORKSPACE,
+              T.ERR_HIP):
+        assert T.strerror(s) and T.strerror(s) != T.strerror(-99)

@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: decoded weights bit-exact; one-hot activations and integer codebooks
+bit-exact (a single product, or sums exact in float32, leave one correct bf16
+answer); random activations within max relative error 1e-2 (the floored gate
+in helpers.gate); repeated calls bit-identical. Sizes: tiny and ragged shapes
+compared in full; the 5120 x 17408 shapes compared on sampled rows/columns
+that the oracle computes one by one, in the launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dequant_gemm_trellis_amd import synth
+from helpers import (QWEN_IN, QWEN_OUT, SAMPLE_ROWS, TOL, Dev, bf16_bits, bf16_to_f64, gate,
+                     row_subset, say, with_x)
+
+pytestmark = pytest.mark.gpu
+CFG = synth.CONFIG_IDS
+L = 12
+
+
+def oracle_y(p, n_begin=0, n_end=None):
+    s = p.shape
+    return oracle.fused_f64(p.x, p.codes, p.scales, p.lut, s.axis, s.T, s.L, s.k,
+                            s.in_features, s.out_features, n_begin, n_end)
+
+
+def oracle_W(p):
+    s = p.shape
+    return oracle.expand(p.codes, p.scales, p.lut, s.axis, s.T, s.L, s.k, s.in_features,
+                         s.out_features)
+
+
+def run(T, d, op=None):
+    """Dispatch by op: gemv (axis 1, M=1), scatter (axis 0, M=1) or prefill."""
+    if op == "gemv":
+        y = T.gemv(d.x.reshape(-1), d.codes, d.scales, d.lut, d.shape)
+    elif op == "scatter":
+        y = T.gemv_scatter(d.x.reshape(-1), d.codes, d.scales, d.lut, d.shape)
+    else:
+        y = T.prefill(d.x, d.codes, d.scales, d.lut, d.shape)
+    torch.cuda.synchronize()
+    return y.reshape(d.p.M, -1)
+
+
+# --------------------------------------------------------------- expand
+@pytest.mark.parametrize("axis,i,o", [(1, 512, 256), (1, 768, 300), (0, 300, 512), (0, 37, 256)])
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_expand_bit_exact_small(gpu_lib, axis, i, o, k):
+    T = gpu_lib
+    shape = synth.Shape(axis, 256, L, k, i, o)
+    p = synth.make_problem(shape, 1, CFG["test"], proj=100 + k)
+    say(f"expand small axis={axis} in={i} out={o} k={k}")
+    d = Dev(p, T)
+    W = bf16_bits(T.expand(d.codes, d.scales, d.lut, shape))
+    assert np.array_equal(W, oracle_W(p))
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_expand_bit_exact_qwen_sampled(gpu_lib, k):
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, k, QWEN_IN, QWEN_OUT)
+    p = synth.make_problem(shape, 1, CFG["qwen_up_gemv"])
+    say(f"expand qwen-up k={k} (all rows on GPU, sampled rows checked)")
+    d = Dev(p, T)
+    W = bf16_bits(T.expand(d.codes, d.scales, d.lut, shape))
+    assert np.array_equal(W[SAMPLE_ROWS], oracle_W(row_subset(p, SAMPLE_ROWS)))
+
+
+# ----------------------------------------------------------------- GEMV
+@pytest.mark.parametrize("i,o", [(512, 256), (768, 300), (256, 17), (1024, 1)])
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_gemv_small(gpu_lib, i, o, k):
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, k, i, o)
+    p = synth.make_problem(shape, 1, CFG["tiny_gemv"] if (i, o) == (512, 256) else CFG["test"])
+    say(f"gemv small in={i} out={o} k={k}")
+    y = bf16_to_f64(run(T, Dev(p, T), op="gemv"))
+    assert gate(y, oracle_y(p)) <= TOL
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_gemv_qwen_sampled(gpu_lib, k):
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, k, QWEN_IN, QWEN_OUT)
+    p = synth.make_problem(shape, 1, CFG["qwen_up_gemv"])
+    say(f"gemv qwen-up k={k}")
+    y = bf16_to_f64(run(T, Dev(p, T), op="gemv"))
+    ref = oracle_y(row_subset(p, SAMPLE_ROWS))
+    assert gate(y[:, SAMPLE_ROWS], ref) <= TOL
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_gemv_one_hot_columns_bit_exact(gpu_lib, k):
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, k, QWEN_IN, QWEN_OUT)
+    p = synth.make_problem(shape, 1, CFG["qwen_up_gemv"])
+    d = Dev(p, T)
+    W = oracle_W(row_subset(p, SAMPLE_ROWS))
+    for col in (0, 1, 255, 256, 2047, 4000, QWEN_IN - 1):
+        say(f"gemv one-hot k={k} col={col}")
+        x = synth.one_hot_x(1, QWEN_IN, [col])
+        d.x.copy_(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16))
+        y = bf16_bits(run(T, d, op="gemv"))[0]
+        assert np.array_equal(y[SAMPLE_ROWS], W[:, col])
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_gemv_integer_codebook_bit_exact(gpu_lib, k):
+    """Integer codebook, scales in {0.5, 1, 2}, integer x: every partial sum is
+    exact in float32, so the bf16 output is unique whatever the order."""
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, k, QWEN_IN, 2048)
+    g = np.random.default_rng(7 + k)
+    p0 = synth.make_problem(shape, 1, CFG["test"], proj=200 + k)
+    xi = g.integers(-3, 4, (1, QWEN_IN)).astype(np.float32)
+    p = synth.Problem(shape, 1, p0.codes, synth.integer_lut(),
+                      g.choice(np.array([0.5, 1.0, 2.0], np.float32), shape.rows),
+                      synth.to_bf16_bits(xi))
+    say(f"gemv integer codebook k={k}")
+    y = bf16_bits(run(T, Dev(p, T), op="gemv"))
+    exact = oracle_y(p)
+    assert np.all(np.abs(exact) < 2**24)
+    assert np.array_equal(y, synth.to_bf16_bits(exact.astype(np.float32)))
+
+
+def test_gemv_deterministic(gpu_lib):
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, 3, QWEN_IN, QWEN_OUT)
+    d = Dev(synth.make_problem(shape, 1, CFG["qwen_up_gemv"]), T)
+    say("gemv determinism k=3")
+    a = bf16_bits(run(T, d, op="gemv"))
+    b = bf16_bits(run(T, d, op="gemv"))
+    assert np.array_equal(a, b)
+
+
+# -------------------------------------------------------------- scatter
+@pytest.mark.parametrize("i,o", [(512, 256), (1000, 512), (17, 256), (4096, 768)])
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_scatter_small(gpu_lib, i, o, k):
+    T = gpu_lib
+    shape = synth.Shape(0, 256, L, k, i, o)
+    p = synth.make_problem(shape, 1, CFG["test"], proj=300 + k)
+    say(f"scatter small in={i} out={o} k={k}")
+    y = bf16_to_f64(run(T, Dev(p, T), op="scatter"))
+    assert gate(y, oracle_y(p)) <= TOL
+
+
+@pytest.mark.parametrize("k", [3, 2, 4])
+def test_scatter_qwen_down_sampled(gpu_lib, k):
+    T = gpu_lib
+    shape = synth.Shape(0, 256, L, k, QWEN_OUT, QWEN_IN)
+    p = synth.make_problem(shape, 1, CFG["qwen_down_scatter"])
+    say(f"scatter qwen-down k={k}")
+    y = bf16_to_f64(run(T, Dev(p, T), op="scatter"))
+    for a, b in ((0, 48), (2536, 2584), (QWEN_IN - 48, QWEN_IN)):
+        ref = oracle_y(p, a, b)[:, a:b]
+        assert gate(y[:, a:b], ref) <= TOL, (a, b)
+
+
+def test_scatter_one_hot_rows_bit_exact(gpu_lib):
+    T = gpu_lib
+    shape = synth.Shape(0, 256, L, 3, QWEN_OUT, QWEN_IN)
+    p = synth.make_problem(shape, 1, CFG["qwen_down_scatter"])
+    d = Dev(p, T)
+    for r in (0, 135, 136, 9000, QWEN_OUT - 1):
+        say(f"scatter one-hot row={r}")
+        x = synth.one_hot_x(1, QWEN_OUT, [r])
+        d.x.copy_(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16))
+        y = bf16_bits(run(T, d, op="scatter"))[0]
+        assert np.array_equal(y, oracle_W(row_subset(p, np.array([r])))[0])
+
+
+def test_scatter_integer_codebook_bit_exact(gpu_lib):
+    T = gpu_lib
+    shape = synth.Shape(0, 256, L, 3, 4096, 1024)
+    g = np.random.default_rng(77)
+    p0 = synth.make_problem(shape, 1, CFG["test"], proj=400)
+    xi = g.integers(-3, 4, (1, shape.in_features)).astype(np.float32)
+    p = synth.Problem(shape, 1, p0.codes, synth.integer_lut(),
+                      g.choice(np.array([0.5, 1.0, 2.0], np.float32), shape.rows),
+                      synth.to_bf16_bits(xi))
+    say("scatter integer codebook k=3")
+    y = bf16_bits(run(T, Dev(p, T), op="scatter"))
+    exact = oracle_y(p)
+    assert np.array_equal(y, synth.to_bf16_bits(exact.astype(np.float32)))
+
+
+def test_scatter_deterministic(gpu_lib):
+    T = gpu_lib
+    shape = synth.Shape(0, 256, L, 3, QWEN_OUT, QWEN_IN)
+    d = Dev(synth.make_problem(shape, 1, CFG["qwen_down_scatter"]), T)
+    say("scatter determinism k=3")
+    assert np.array_equal(bf16_bits(run(T, d, op="scatter")), bf16_bits(run(T, d, op="scatter")))
+
+
+# -------------------------------------------------------------- prefill
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 16, 17, 32])
+@pytest.mark.parametrize("axis", [1, 0])
+def test_prefill_small(gpu_lib, M, axis):
+    T = gpu_lib
+    k = 2 + M % 3
+    shape = synth.Shape(axis, 256, L, k, 768 if axis else 1000, 300 if axis else 512)
+    p = synth.make_problem(shape, M, CFG["test"], proj=500 + axis)
+    say(f"prefill small axis={axis} M={M} k={k}")
+    y = bf16_to_f64(run(T, Dev(p, T)))
+    assert y.shape == (M, shape.out_features)
+    assert gate(y, oracle_y(p)) <= TOL
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("M", [5, 8, 16, 32])
+def test_prefill_qwen_up_sampled(gpu_lib, M, k):
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, k, QWEN_IN, QWEN_OUT)
+    p = synth.make_problem(shape, M, CFG["qwen_up_prefill"])
+    say(f"prefill qwen-up M={M} k={k}")
+    y = bf16_to_f64(run(T, Dev(p, T)))
+    ref = oracle_y(row_subset(p, SAMPLE_ROWS))
+    assert gate(y[:, SAMPLE_ROWS], ref) <= TOL
+
+
+def test_prefill_one_hot_rows_bit_exact(gpu_lib):
+    """Each activation row one-hot: output row m is column cols[m] of W."""
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, 4, QWEN_IN, QWEN_OUT)
+    cols = [0, 17, 255, 256, 1023, 2500, 5119, 64, 128, 3, 777, 4096, 300, 301, 2, 1,
+            4000, 4001, 11, 12, 13, 14, 15, 16, 2047, 2048, 3071, 3072, 5000, 5001, 5002, 999]
+    p0 = synth.make_problem(shape, 32, CFG["qwen_up_prefill"])
+    p = with_x(p0, synth.one_hot_x(32, QWEN_IN, cols))
+    say("prefill one-hot M=32 k=4")
+    y = bf16_bits(run(T, Dev(p, T)))
+    W = oracle_W(row_subset(p, SAMPLE_ROWS))
+    for m, c in enumerate(cols):
+        assert np.array_equal(y[m, SAMPLE_ROWS], W[:, c]), (m, c)
+
+
+@pytest.mark.parametrize("M", [5, 8, 32])
+def test_prefill_axis0_qwen_down_sampled(gpu_lib, M):
+    T = gpu_lib
+    shape = synth.Shape(0, 256, L, 4, QWEN_OUT, QWEN_IN)
+    p = synth.make_problem(shape, M, CFG["qwen_mlp"], proj=2)
+    say(f"prefill axis0 qwen-down M={M} k=4")
+    y = bf16_to_f64(run(T, Dev(p, T)))
+    for a, b in ((0, 32), (QWEN_IN - 32, QWEN_IN)):
+        assert gate(y[:, a:b], oracle_y(p, a, b)[:, a:b]) <= TOL, (a, b)
+
+
+def test_prefill_deterministic(gpu_lib):
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, 2, QWEN_IN, QWEN_OUT)
+    d = Dev(synth.make_problem(shape, 32, CFG["qwen_up_prefill"]), T)
+    say("prefill determinism M=32 k=2")
+    assert np.array_equal(bf16_bits(run(T, d)), bf16_bits(run(T, d)))
+
+
+# ------------------------------------------------------ MLP (k=4, M=1/32)
+@pytest.mark.parametrize("M", [1, 32])
+def test_mlp_projections_sampled(gpu_lib, M):
+    """Gate and up (axis 1) and down (axis 0), each with its own codebook."""
+    T = gpu_lib
+    for proj, axis in ((0, 1), (1, 1), (2, 0)):
+        shape = (synth.Shape(1, 256, L, 4, QWEN_IN, QWEN_OUT) if axis
+                 else synth.Shape(0, 256, L, 4, QWEN_OUT, QWEN_IN))
+        p = synth.make_problem(shape, M, CFG["qwen_mlp"], proj=proj)
+        say(f"mlp proj={proj} axis={axis} M={M}")
+        d = Dev(p, T)
+        op = None if M > 1 else ("gemv" if axis else "scatter")
+        y = bf16_to_f64(run(T, d, op=op))
+        if axis:
+            assert gate(y[:, SAMPLE_ROWS], oracle_y(row_subset(p, SAMPLE_ROWS))) <= TOL
+        else:
+            assert gate(y[:, :40], oracle_y(p, 0, 40)[:, :40]) <= TOL
