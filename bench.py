@@ -38,7 +38,7 @@ MALL_BYTES = 256 << 20
 QWEN_IN, QWEN_OUT = 5120, 17408
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_qwen_up_k2.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "dequant_gemm_trellis_amd", "csrc", f)
-                  for f in ("axis1.hip", "common.hpp")]
+                  for f in ("gemv.hip", "common.hpp")]
 METRIC = "µs/call and effective HBM GB/s, trellis GEMV 5120→17408 k=2/3/4, M=1"
 
 
@@ -235,6 +235,9 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only-k", type=int, default=0, help="time only this k (profiling runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain device copy of 512 MiB (scales the FETCH_SIZE/WRITE_SIZE "
+                         "counters of the traffic figure) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -255,6 +258,16 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        n = 512 << 20
+        src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n}), flush=True)
+        return 0
 
     per_k, first = {}, None
     for k in ((args.only_k,) if args.only_k else (2, 3, 4)):
@@ -298,7 +311,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_entry(),
-                     "kernel": "axis1_mma_kernel<2,1>",
+                     "kernel": "gemv_kernel<2>",
                      "bytes_per_launch": head["code_bytes"]},
         "cpu_baseline": cpu,
     }

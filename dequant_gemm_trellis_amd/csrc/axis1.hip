@@ -31,48 +31,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Words of one 64-weight run (run index c counts t upwards; cp = 3 - c counts
-// bit position upwards) plus the wrapped next word.
-template <int K>
-__device__ __forceinline__ void load_run64(const uint32_t* __restrict__ block, int cp,
-                                           uint32_t (&w)[2 * K + 1]) {
-    constexpr int wpb = Bits<K>::wpb;
-    const uint32_t* p = block + 2 * K * cp;
-    if constexpr (K == 2) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else if constexpr (K == 3) {
-        const uint2 a = *reinterpret_cast<const uint2*>(p);
-        const uint2 b = *reinterpret_cast<const uint2*>(p + 2);
-        const uint2 c = *reinterpret_cast<const uint2*>(p + 4);
-        w[0] = a.x; w[1] = a.y; w[2] = b.x; w[3] = b.y; w[4] = c.x; w[5] = c.y;
-    } else {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(p);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(p + 4);
-        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-    }
-    const int nxt = 2 * K * (cp + 1);
-    w[2 * K] = block[nxt == wpb ? 0 : nxt];
-}
-
-// B fragment S (0..7) of a run: weights t = 64c + 8S + e, e = 0..7, packed two
-// per dword (low half first). Weight t is local symbol q = 63 - 8S - e, whose
-// window starts at local bit q * k.
-template <int K, int S>
-__device__ __forceinline__ u32x4 run_fragment(const uint32_t (&w)[2 * K + 1],
-                                              const float* __restrict__ lut_s, float scale) {
-    u32x4 r;
-    static_for<0, 4>([&](auto dc) {
-        constexpr int d = decltype(dc)::value;
-        constexpr int q0 = 63 - 8 * S - 2 * d;
-        const float v0 = lds_lut(lut_s, lut_byte_offset<q0 * K>(w));
-        const float v1 = lds_lut(lut_s, lut_byte_offset<(q0 - 1) * K>(w));
-        r[d] = pack_weights(v0, v1, scale);
-    });
-    return r;
-}
-
 // One block of a wave: 8 B fragments, each multiplied against MT A fragments
 // (x rows m = 16 mt + j). Row m of A only feeds row m of D, so lanes whose m
 // is at or past M may carry any finite row of x: their D rows are never
@@ -85,7 +43,7 @@ __device__ __forceinline__ void block_mma(const uint32_t (&w)[2 * K + 1],
                                           floatx4 (&acc)[MT]) {
     static_for<0, 8>([&](auto sc) {
         constexpr int S = decltype(sc)::value;
-        const bf16x8 bfrag = as_bf16x8(run_fragment<K, S>(w, lut_s, scale));
+        const bf16x8 bfrag = as_bf16x8(run64_fragment<K, S, false>(w, lut_s, scale));
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(xrow0 + 8 * S);
         acc[0] = mfma16x16x32(as_bf16x8(a0), bfrag, acc[0]);
         if constexpr (MT == 2) {
@@ -174,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(
     uint16_t* dst = w + static_cast<size_t>(row) * nb * kT + b * kT + 64 * c;
     static_for<0, 8>([&](auto sc) {
         constexpr int S = decltype(sc)::value;
-        *reinterpret_cast<u32x4*>(dst + 8 * S) = run_fragment<K, S>(wr, lut_s, scale);
+        *reinterpret_cast<u32x4*>(dst + 8 * S) = run64_fragment<K, S, false>(wr, lut_s, scale);
     });
 }
 

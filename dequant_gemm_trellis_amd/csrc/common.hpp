@@ -47,29 +47,40 @@ __device__ __forceinline__ void static_for(F&& f) {
     }
 }
 
-// Byte offset into the LDS codebook of the window that starts at bit O of a
-// little-endian word array: ((bits >> O) & 0xFFF) * 4, formed as
-// (bits >> (O - 2)) & 0x3FFC so the x4 costs nothing. O is a template
-// constant, so every word index is known at compile time and the array stays
-// in registers; the words read are w[(O-2)/32] and, if the window crosses a
-// word boundary, the next one.
-template <int O, int N>
-__device__ __forceinline__ uint32_t lut_byte_offset(const uint32_t (&w)[N]) {
-    if constexpr (O < 2) {
-        return (w[0] << (2 - O)) & 0x3FFCu;
+// Bit field of a little-endian word array, pre-scaled for LDS addressing:
+// ((bits >> O) & (2^WIDTH - 1)) << SHIFT, formed as one shift or funnel shift
+// plus one mask. O is a template constant, so every word index is known at
+// compile time and the array stays in registers.
+template <int O, int WIDTH, int SHIFT, int N>
+__device__ __forceinline__ uint32_t field_offset(const uint32_t (&w)[N]) {
+    constexpr uint32_t mask = ((1u << WIDTH) - 1u) << SHIFT;
+    if constexpr (O < SHIFT) {
+        static_assert(O + WIDTH <= 32, "field must sit in word 0");
+        return (w[0] << (SHIFT - O)) & mask;
     } else {
-        constexpr int s = O - 2, wi = s >> 5, sh = s & 31;
-        if constexpr (sh + 14 <= 32) {
-            return (w[wi] >> sh) & 0x3FFCu;
+        constexpr int s = O - SHIFT, wi = s >> 5, sh = s & 31;
+        if constexpr (sh + WIDTH + SHIFT <= 32) {
+            return (w[wi] >> sh) & mask;
         } else {
-            static_assert(wi + 1 < N, "window runs past the loaded words");
-            return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & 0x3FFCu;
+            static_assert(wi + 1 < N, "field runs past the loaded words");
+            return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & mask;
         }
     }
 }
 
+// Byte offset into the LDS codebook (4-byte entries) of the 12-bit window
+// that starts at bit O.
+template <int O, int N>
+__device__ __forceinline__ uint32_t lut_byte_offset(const uint32_t (&w)[N]) {
+    return field_offset<O, kL, 2>(w);
+}
+
 __device__ __forceinline__ float lds_lut(const float* lut_s, uint32_t byte_off) {
     return *reinterpret_cast<const float*>(reinterpret_cast<const char*>(lut_s) + byte_off);
+}
+
+__device__ __forceinline__ floatx2 lds_pair(const float* tab, uint32_t byte_off) {
+    return *reinterpret_cast<const floatx2*>(reinterpret_cast<const char*>(tab) + byte_off);
 }
 
 // Two decoded weights packed as bf16x2 (low half = first): each is the float32
@@ -78,6 +89,112 @@ __device__ __forceinline__ uint32_t pack_weights(float v0, float v1, float scale
     floatx2 p = {v0 * scale, v1 * scale};
     bf16x2 h = __builtin_convertvector(p, bf16x2);
     return __builtin_bit_cast(uint32_t, h);
+}
+
+// ---------------------------------------------------------------------------
+// 64-weight runs. Weight t of a 256-weight block sits at bit (255 - t) k of
+// the block's bit string, so the run of weights [64c, 64c + 64) is the
+// contiguous bit range [64 (3 - c) k, 64 (4 - c) k) -- exactly 2k words,
+// starting at word 2k cp with cp = 3 - c -- plus the up to 11 window bits that
+// spill into the next word (word 0 of the same block after the last word: the
+// tail-biting wrap). Inside the run, weight 64c + i is local symbol
+// q = 63 - i, whose window starts at local bit q k.
+// STREAM marks the loads non-temporal: the codes are read exactly once.
+template <typename T, bool STREAM>
+__device__ __forceinline__ T load_words(const T* p) {
+    if constexpr (STREAM) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <int K, bool STREAM = false>
+__device__ __forceinline__ void load_run64(const uint32_t* __restrict__ block, int cp,
+                                           uint32_t (&w)[2 * K + 1]) {
+    constexpr int wpb = Bits<K>::wpb;
+    const uint32_t* p = block + 2 * K * cp;
+    if constexpr (K == 2) {
+        const u32x4 v = load_words<u32x4, STREAM>(reinterpret_cast<const u32x4*>(p));
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if constexpr (K == 3) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 a = load_words<u32x2, STREAM>(reinterpret_cast<const u32x2*>(p));
+        const u32x2 b = load_words<u32x2, STREAM>(reinterpret_cast<const u32x2*>(p + 2));
+        const u32x2 c = load_words<u32x2, STREAM>(reinterpret_cast<const u32x2*>(p + 4));
+        w[0] = a.x; w[1] = a.y; w[2] = b.x; w[3] = b.y; w[4] = c.x; w[5] = c.y;
+    } else {
+        const u32x4 a = load_words<u32x4, STREAM>(reinterpret_cast<const u32x4*>(p));
+        const u32x4 b = load_words<u32x4, STREAM>(reinterpret_cast<const u32x4*>(p + 4));
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
+    const int nxt = 2 * K * (cp + 1);
+    w[2 * K] = load_words<uint32_t, STREAM>(block + (nxt == wpb ? 0 : nxt));
+}
+
+// Entries of the k = 2 pair table: entry F (the 14-bit union of the windows
+// of an adjacent pair of weights, which overlap by 10 bits) holds
+// (LUT[F >> 2], LUT[F & 0xFFF]), the values of the earlier and the later weight.
+constexpr int kPairEntries = 1 << 14;
+
+// B fragment S (0..7) of a 64-weight run: weights 64c + 8S + e, e = 0..7,
+// packed two per dword, low half first (the MFMA operand layout). The fetch
+// is split from the pack so callers can keep several fragments' gathers in
+// flight: gather_run64 issues the LDS reads (4 pair-table reads when PAIR,
+// else 8 codebook reads), pack_fragment turns the values into the operand.
+// Pair j of the fragment is weights 2j, 2j + 1: local symbols q0 = 63 - 8S - 2j
+// (the earlier weight) and q0 - 1.
+template <bool PAIR>
+struct Gathered {
+    floatx2 v[4];  // v[j] = values of the earlier and the later weight of pair j
+};
+
+template <int K, int S, bool PAIR>
+__device__ __forceinline__ Gathered<PAIR> gather_run64(const uint32_t (&w)[2 * K + 1],
+                                                       const float* __restrict__ tab) {
+    static_assert(!PAIR || K == 2, "pair table only for k = 2");
+    Gathered<PAIR> g;
+    static_for<0, 4>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        constexpr int q0 = 63 - 8 * S - 2 * d;
+        if constexpr (PAIR) {
+            // the 14-bit union starts at the later weight's window, bit 2 (q0 - 1)
+            g.v[d] = lds_pair(tab, field_offset<2 * (q0 - 1), 14, 3>(w));
+        } else {
+            g.v[d].x = lds_lut(tab, lut_byte_offset<q0 * K>(w));
+            g.v[d].y = lds_lut(tab, lut_byte_offset<(q0 - 1) * K>(w));
+        }
+    });
+    return g;
+}
+
+template <bool PAIR>
+__device__ __forceinline__ u32x4 pack_fragment(const Gathered<PAIR>& g, float scale) {
+    u32x4 r;
+    static_for<0, 4>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        r[d] = pack_weights(g.v[d].x, g.v[d].y, scale);
+    });
+    return r;
+}
+
+template <int K, int S, bool PAIR>
+__device__ __forceinline__ u32x4 run64_fragment(const uint32_t (&w)[2 * K + 1],
+                                                const float* __restrict__ tab, float scale) {
+    return pack_fragment<PAIR>(gather_run64<K, S, PAIR>(w, tab), scale);
+}
+
+// Build the k = 2 pair table in LDS from the codebook in global memory.
+template <int NTHREADS>
+__device__ __forceinline__ void stage_pair_table(float* __restrict__ tab,
+                                                 const float* __restrict__ lut) {
+    const float4* lut4 = reinterpret_cast<const float4*>(lut);
+    float4* dst = reinterpret_cast<float4*>(tab);
+    for (int grp = threadIdx.x; grp < kPairEntries / 4; grp += NTHREADS) {
+        // F = 4 grp + i, i = 0..3: F >> 2 = grp and F & 0xFFF = 4 (grp & 1023) + i
+        const float a = lut[grp];
+        const float4 b = lut4[grp & 1023];
+        dst[2 * grp] = float4{a, b.x, a, b.y};
+        dst[2 * grp + 1] = float4{a, b.z, a, b.w};
+    }
 }
 
 __device__ __forceinline__ uint16_t round_bf16(float f) {

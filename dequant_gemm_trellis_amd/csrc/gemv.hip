@@ -1,0 +1,254 @@
+// Axis-1 trellis GEMV (one activation row) for gfx950:
+//   y[n] = bf16( sum_k x[k] * bf16( fl32( LUT[window(n, k)] * scales[n] ) ) ).
+//
+// Pages cited: diff views of "@mlx-bun/inference" 0.0.0-stage -> 1.0.0,
+// page 60: wide-prefill.ts (axis-1 GEMV: decode each weight, round it to bf16,
+// dot with the activations, float accumulation, bf16 store) and the
+// tiled-prefill.ts weight-tile decode (window of weight t at bit (T-1-t)*k,
+// wrapping inside the block).
+//
+// What bounds this kernel on MI355X is the codebook gather, not HBM: every
+// weight needs one random read of the 4096-entry table, and random LDS reads
+// bank-conflict. A wave-wide random ds_read costs about the same whether it
+// moves 4 or 8 bytes per lane, so for k = 2 the kernel reads a pair table
+// instead (one gather per two weights; see stage_pair_table). For k = 3 and 4
+// the pair index would be 15/16 bits (256/512 KB) and does not fit in LDS, so
+// those read the 16 KB codebook directly.
+//
+// Work mapping. The grid is persistent: one 1024-thread workgroup per compute
+// unit, workgroup g owning rows [g N / G, (g+1) N / G), so every CU gets the
+// same number of rows. A unit of work is one 256-weight block of one row, and
+// units are numbered block-major inside a row chunk: the 16 units a wave takes
+// together are 16 rows of one block, so the lanes that share a run index c
+// read the same activations (broadcast reads of the LDS copy; numbered
+// row-major, each lane reads its own 128 B of activations per unit and the
+// LDS, already the bottleneck, spends about a third more time).
+// Lane l = 16 c + j takes the 64-weight run c of the unit in its column j.
+// The run's 64 weights form eight 8-weight B fragments of
+// v_mfma_f32_16x16x32_bf16 and the A fragment of the same lane carries the 8
+// matching activations. Then D[j][j] sums exactly the four lanes of column j
+// -- that unit's dot product -- while the off-diagonal entries mix units and
+// are ignored: the matrix core does the multiply-adds and the 4-lane
+// reduction, leaving the VALU to the decode. Unit partials go to LDS and each
+// row is summed over its blocks in ascending order, so the result does not
+// depend on timing.
+//
+// The activations are staged in LDS once per workgroup (each lane needs 128 B
+// of them per unit; served from the cache hierarchy instead, they cost
+// several times the code traffic). Block b starts at byte 528 b, a stride of
+// 132 words (4 mod 64), which keeps the reads of a wave that straddles two
+// blocks on disjoint banks.
+//
+// Code words are prefetched two steps ahead into registers: measured under
+// load, a memory round trip takes longer than one step of decode.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace trellis {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kUnitsPerStep = kWaves * 16;
+constexpr int kPartialCap = 2048;    // unit partials held in LDS per row chunk
+constexpr int kXStride = 528;        // bytes per staged activation block (512 + 16)
+
+template <int K>
+struct GemvLds {
+    static constexpr bool pair = K == 2;
+    static constexpr int tab_floats = pair ? 2 * kPairEntries : kLutEntries;
+    // activation bytes that fit beside the table and the partials in 160 KB
+    static constexpr int x_bytes = pair ? 24576 : 65536;
+    static constexpr int max_blocks = x_bytes / kXStride;
+};
+
+// Code words of one step for one lane, plus the unit's block and the
+// row-major index (row * nb + block) of its partial.
+template <int K>
+struct Step {
+    uint32_t w[2 * K + 1];
+    float scale;
+    uint32_t b;
+    uint32_t slot;
+};
+
+struct XFrag {
+    u32x4 v[8];
+};
+
+struct Ctx {
+    const uint32_t* codes;   // first word of the row chunk
+    const float* scales;     // scale of the chunk's first row
+    int nb;                  // blocks per row
+    int cr;                  // rows in the chunk
+    uint32_t magic;          // ceil(2^31 / cr): u / cr == mulhi(2u, magic) for u < 2^11
+    int cp;                  // 3 - c: bit-position order of this lane's run
+};
+
+__device__ __forceinline__ uint32_t div_magic(int d) {
+    // u / d == mulhi(2u, ceil(2^31 / d)) exactly while u * d < 2^31 (u < 2048 here)
+    return static_cast<uint32_t>(((1ull << 31) + d - 1) / d);
+}
+
+// Unit u of the chunk (block-major): block u / cr, chunk row u % cr.
+template <int K>
+__device__ __forceinline__ void load_step(Step<K>& st, const Ctx& cx, int u, int U) {
+    constexpr int wpb = Bits<K>::wpb;
+    const uint32_t uu = static_cast<uint32_t>(u < U ? u : U - 1);  // idle lanes re-read a valid unit
+    const uint32_t b = __umulhi(uu << 1, cx.magic);
+    const uint32_t rl = uu - b * static_cast<uint32_t>(cx.cr);
+    st.b = b;
+    st.slot = rl * static_cast<uint32_t>(cx.nb) + b;
+    load_run64<K>(cx.codes + st.slot * wpb, cx.cp, st.w);
+    st.scale = cx.scales[rl];
+}
+
+__device__ __forceinline__ XFrag load_x(const char* __restrict__ xs, uint32_t b, int c) {
+    XFrag xf;
+    const u32x4* p = reinterpret_cast<const u32x4*>(xs + b * kXStride + 128 * c);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) xf.v[s] = p[s];
+    return xf;
+}
+
+// One unit: eight fragments, software-pipelined so the LDS gathers of the next
+// two fragments are in flight while one is packed and multiplied.
+// D[j][j] of the 16x16 MFMA tile sits in lane 16 (j / 4) + j, register j % 4.
+template <int K>
+__device__ __forceinline__ void run_step(const Step<K>& st, const char* __restrict__ xs,
+                                         const float* __restrict__ tab, float* __restrict__ part,
+                                         int u, int U, int j, int c) {
+    constexpr bool P = GemvLds<K>::pair;
+    const XFrag xf = load_x(xs, st.b, c);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    Gathered<P> g0 = gather_run64<K, 0, P>(st.w, tab);
+    Gathered<P> g1 = gather_run64<K, 1, P>(st.w, tab);
+    static_for<0, 8>([&](auto sc) {
+        constexpr int S = decltype(sc)::value;
+        Gathered<P> g2;
+        if constexpr (S + 2 < 8) g2 = gather_run64<K, S + 2, P>(st.w, tab);
+        const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g0, st.scale));
+        acc = mfma16x16x32(as_bf16x8(xf.v[S]), bfrag, acc);
+        g0 = g1;
+        if constexpr (S + 2 < 8) g1 = g2;
+    });
+    if (c == (j >> 2) && u < U) {
+        const int v = j & 3;
+        part[st.slot] = v == 0 ? acc[0] : v == 1 ? acc[1] : v == 2 ? acc[2] : acc[3];
+    }
+}
+
+template <int K>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
+    const float* __restrict__ scales, const float* __restrict__ lut,
+    uint16_t* __restrict__ y, int N, int nb) {
+    constexpr int wpb = Bits<K>::wpb;
+    __shared__ __attribute__((aligned(16))) float tab[GemvLds<K>::tab_floats];
+    __shared__ __attribute__((aligned(16))) char xs[GemvLds<K>::x_bytes];
+    __shared__ float part[kPartialCap];
+
+    const int G = gridDim.x, g = blockIdx.x;
+    const int r0 = static_cast<int>(static_cast<long>(g) * N / G);
+    const int r1 = static_cast<int>(static_cast<long>(g + 1) * N / G);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, c = lane >> 4;
+    const int chunk_rows = kPartialCap / nb;
+    const int my = wave * 16 + j;  // this lane's column slot within a step
+
+    Ctx cx{codes + static_cast<size_t>(r0) * nb * wpb, scales + r0, nb, 1, 0u, 3 - c};
+    Step<K> sa, sb, sc;
+    int CR = min(r1 - r0, chunk_rows), U = CR * nb;
+    if (CR > 0) {
+        cx.cr = CR;
+        cx.magic = div_magic(CR);
+        load_step<K>(sa, cx, my, U);
+        load_step<K>(sb, cx, my + kUnitsPerStep, U);
+    }
+    if constexpr (GemvLds<K>::pair)
+        stage_pair_table<kThreads>(tab, lut);
+    else
+        stage_lut<kThreads>(tab, lut);
+    for (int i = tid; i < nb * 32; i += kThreads)  // 16-byte chunks of x, 32 per block
+        *reinterpret_cast<u32x4*>(xs + (i >> 5) * kXStride + (i & 31) * 16) =
+            reinterpret_cast<const u32x4*>(x)[i];
+    __syncthreads();
+
+    for (int cr0 = r0; cr0 < r1; cr0 += chunk_rows) {
+        CR = min(r1 - cr0, chunk_rows);
+        U = CR * nb;
+        if (cr0 != r0) {
+            cx.codes = codes + static_cast<size_t>(cr0) * nb * wpb;
+            cx.scales = scales + cr0;
+            cx.cr = CR;
+            cx.magic = div_magic(CR);
+            load_step<K>(sa, cx, my, U);
+            load_step<K>(sb, cx, my + kUnitsPerStep, U);
+        }
+        // Three register sets rotate, so the code words of the next two steps
+        // are in flight while one step is decoded. Every load is
+        // unconditional (past the end it re-reads a valid unit) and only the
+        // decode steps are guarded: the memory-counter waits the compiler
+        // places must hold on every path, so a conditional load, or a loop
+        // exit between loads, makes it wait for the prefetch too.
+        for (int u0 = 0; u0 < U; u0 += 3 * kUnitsPerStep) {
+            const int ua = u0 + my;
+            load_step<K>(sc, cx, ua + 2 * kUnitsPerStep, U);
+            run_step<K>(sa, xs, tab, part, ua, U, j, c);
+            load_step<K>(sa, cx, ua + 3 * kUnitsPerStep, U);
+            if (u0 + kUnitsPerStep < U) run_step<K>(sb, xs, tab, part, ua + kUnitsPerStep, U, j, c);
+            load_step<K>(sb, cx, ua + 4 * kUnitsPerStep, U);
+            if (u0 + 2 * kUnitsPerStep < U)
+                run_step<K>(sc, xs, tab, part, ua + 2 * kUnitsPerStep, U, j, c);
+        }
+        __syncthreads();
+        for (int r = tid; r < CR; r += kThreads) {
+            const float* pr = part + r * nb;
+            float s = 0.f;
+            for (int q = 0; q < nb; ++q) s += pr[q];
+            y[cr0 + r] = round_bf16(s);
+        }
+        __syncthreads();
+    }
+}
+
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <int K>
+hipError_t launch_gemv_k(const uint16_t* x, const uint32_t* codes, const float* scales,
+                         const float* lut, uint16_t* y, int N, int nb, hipStream_t st) {
+    const int G = N < cu_count() ? N : cu_count();
+    return launch_kernel(gemv_kernel<K>, dim3(G), dim3(kThreads), st, x, codes, scales, lut, y,
+                         N, nb);
+}
+
+}  // namespace
+
+int gemv_max_blocks(int k) {
+    return k == 2 ? GemvLds<2>::max_blocks : GemvLds<4>::max_blocks;
+}
+
+hipError_t launch_gemv(const uint16_t* x, const uint32_t* codes, const float* scales,
+                       const float* lut, uint16_t* y, int N, int nb, int k, hipStream_t st) {
+    switch (k) {
+    case 2: return launch_gemv_k<2>(x, codes, scales, lut, y, N, nb, st);
+    case 3: return launch_gemv_k<3>(x, codes, scales, lut, y, N, nb, st);
+    case 4: return launch_gemv_k<4>(x, codes, scales, lut, y, N, nb, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace trellis

@@ -35,7 +35,7 @@
  *     enqueued: on a negative status nothing was enqueued. A kernel fault
  *     shows up at the caller's next synchronisation.
  *   - Geometry accepted: axis in {0, 1}, T = 256, L = 12, k in {2, 3, 4},
- *     1 <= in_features, out_features <= 2^24, and cols % 256 == 0 (cols is
+ *     1 <= in_features, out_features <= 2^19, and cols % 256 == 0 (cols is
  *     in_features on axis 1, out_features on axis 0).
  */
 #ifndef TRELLIS_H

@@ -71,7 +71,8 @@ def call_gemv(T, g, x=FAKE, codes=FAKE, scales=FAKE, lut=FAKE, y=FAKE):
 @pytest.mark.parametrize("field,value", [("axis", 2), ("axis", -1), ("T", 128), ("L", 11),
                                          ("k", 1), ("k", 5), ("in_features", 0),
                                          ("out_features", 0), ("in_features", 300),
-                                         ("in_features", (1 << 24) + 256)])
+                                         ("in_features", (1 << 19) + 256),
+                                         ("out_features", (1 << 19) + 1)])
 def test_gemv_rejects_bad_geometry(T, field, value):
     g = geom(T)
     setattr(g, field, value)

@@ -72,9 +72,13 @@ def test_expand_bit_exact_qwen_sampled(gpu_lib, k):
 
 
 # ----------------------------------------------------------------- GEMV
-@pytest.mark.parametrize("i,o", [(512, 256), (768, 300), (256, 17), (1024, 1)])
+@pytest.mark.parametrize("i,o", [(512, 256), (768, 300), (256, 17), (1024, 1), (12288, 300),
+                                 (32768, 40)])
 @pytest.mark.parametrize("k", [2, 3, 4])
 def test_gemv_small(gpu_lib, i, o, k):
+    """Small and ragged shapes; 12288 and 32768 inputs exceed the activations
+    the persistent kernel stages in LDS (for k = 2, resp. all k) and take the
+    general axis-1 kernel."""
     T = gpu_lib
     shape = synth.Shape(1, 256, L, k, i, o)
     p = synth.make_problem(shape, 1, CFG["tiny_gemv"] if (i, o) == (512, 256) else CFG["test"])
