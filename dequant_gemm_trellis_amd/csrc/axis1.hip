@@ -1,112 +1,270 @@
-// Axis-1 trellis kernels for gfx950: the fused decode + bf16 MFMA kernel that
-// serves both the M = 1 GEMV and the M <= 32 prefill, and the diagnostic
-// expand kernel. Both decode through the same fragment builder.
+// Axis-1 trellis kernels for gfx950: the fused decode + bf16 MFMA kernel for
+// several activation rows (1 <= M <= 32; also the M = 1 GEMV when a row is too
+// long for the activation-staging GEMV kernel), and the diagnostic expand
+// kernel. Both decode through the same fragment builder.
 //
 // Pages cited: diff views of "@mlx-bun/inference" 0.0.0-stage -> 1.0.0,
 // page 60: tiled-prefill.ts (axis-1 tile decode + matrix multiply, bf16
 // rounding of each weight), wide-prefill.ts (axis-1 multi-vector GEMV),
 // vector-expand.ts (whole-matrix decode).
 //
-// Work mapping (one 64-lane wavefront):
-//   lane l -> stored row n0 + (l % 16), run c = l / 16 of the current block.
+// Fragment mapping (one 64-lane wavefront, v_mfma_f32_16x16x32_bf16):
+//   lane l -> row j = l % 16 of a 16-row group, run c = l / 16 of a block.
 //   Run c holds weights t in [64c, 64c + 64) of a 256-weight block. Weight t
 //   sits at bit (255 - t) * k, so the run is the contiguous bit range
 //   [64 (3 - c) k, 64 (4 - c) k) -- exactly 2k words -- plus the 11 window
 //   bits that spill into the next word (the block's word 0 for the last run:
-//   the tail-biting wrap). Each lane therefore loads 2k + 1 words, coalesced
-//   across the 4 runs of a row.
-//   The 64 weights of a run become eight 8-weight B fragments of
-//   v_mfma_f32_16x16x32_bf16 (B[k][n], k = 8 c + e within the instruction);
-//   the A fragment is the matching 8 activations of row m = l % 16. Because
-//   A and B index k identically, the hardware's k order inside the
-//   instruction does not matter.
-//   A workgroup (4 waves) owns 16 output rows; wave w takes blocks
-//   w, w + 4, ... and the four partial tiles are summed in LDS in a fixed
-//   order, so results are deterministic.
+//   the tail-biting wrap), taken from the lane that holds the next run.
+//   The 64 weights of a run become eight 8-weight B fragments (B[k][n],
+//   k = 8 c + e within the instruction); the A fragment is the matching 8
+//   activations of row m = 16 mt + j. Because A and B index k identically,
+//   the hardware's k order inside the instruction does not matter.
+//
+// Work mapping. The grid is persistent (one workgroup per compute unit),
+// workgroup g owning rows [g N / G, (g+1) N / G), at most kGroups
+// 16-row groups. A task is one group x one 256-weight block; the workgroup's
+// tasks are numbered block-major (all groups of block 0, then block 1, ...)
+// and each wave takes a contiguous range of them. A wave thus meets only one
+// or two blocks and loads their activation fragments once, reusing them for
+// every group: fetched per task instead, those loads touch 16 rows x 4 runs =
+// 64 cache lines per instruction and, measured, dominate the kernel from
+// M = 16 up. Each wave keeps one accumulator tile per group; at the end the
+// per-wave tiles are summed in LDS in wave order (deterministic), reusing the
+// table's space. Lanes of rows past the workgroup's range decode all-zero
+// words, so their gathers all hit one LDS address.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace trellis {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // expand kernel
+constexpr int kGroups = 5;     // 16-row groups per prefill workgroup (80 rows)
 
-// One block of a wave: 8 B fragments, each multiplied against MT A fragments
-// (x rows m = 16 mt + j). Row m of A only feeds row m of D, so lanes whose m
-// is at or past M may carry any finite row of x: their D rows are never
-// stored, and no masking is needed.
+// Prefill workgroup size: 16 waves for one M tile; 8 for two, whose second
+// set of accumulators and activation fragments needs the larger register
+// budget of two waves per SIMD.
+template <int MT>
+struct PrefillShape {
+    static constexpr int threads = MT == 1 ? 1024 : 512;
+    static constexpr int waves = threads / kWave;
+};
+
+// Per-wave activation slot: the eight A fragments of each M tile, in lane
+// order, 16-byte chunks; chunk (S, c, j) sits at S * kSlotChunks + 17 c + j, a
+// skew that keeps both the transposing writes and the lane-order reads off
+// shared banks.
+constexpr int kSlotChunks = 67;
+
+template <int MT>
+struct PrefillLds {
+    static constexpr int waves = PrefillShape<MT>::waves;
+    static constexpr int slot_chunks = MT * 8 * kSlotChunks;
+    static constexpr int decode_floats = kLutEntries + waves * slot_chunks * 4;
+    static constexpr int part_floats = waves * kGroups * 256;  // one M tile of wave partials
+    static constexpr int floats = decode_floats > part_floats ? decode_floats : part_floats;
+};
+
+struct TaskCtx {
+    const uint32_t* codes;
+    const float* scales;
+    int nb, gc, r0, r1, j, cp;
+};
+
+template <int K>
+struct Task {
+    uint32_t w[2 * K + 1];
+    float scale;
+    int b, g;    // block and row group: uniform across the wave
+    bool valid;  // this lane's row lies in the workgroup's range
+};
+
+// Load task tau's code words (2k per lane) and scale. Past the wave's last
+// task it re-reads that task: every load is unconditional, so the compiler's
+// memory-counter waits never have to cover a skipped load.
+template <int K>
+__device__ __forceinline__ void load_task(Task<K>& t, const TaskCtx& cx, int tau, int tau_end) {
+    constexpr int wpb = Bits<K>::wpb;
+    const int tc = tau < tau_end ? tau : tau_end - 1;
+    const int b = tc / cx.gc;
+    const int g = tc - b * cx.gc;
+    const int row = cx.r0 + 16 * g + cx.j;
+    t.valid = row < cx.r1;
+    const int rc = t.valid ? row : cx.r1 - 1;
+    t.b = b;
+    t.g = g;
+    load_run64_words<K>(cx.codes + (static_cast<size_t>(rc) * cx.nb + b) * wpb, cx.cp, t.w);
+    t.scale = cx.scales[rc];
+}
+
+template <int MT>
+struct XFrags {
+    u32x4 v[MT][8];
+};
+
+// Activation fragments of block b for a wave: A fragment S of lane (j, c) is
+// x[m = 16 mt + j][256 b + 64 c + 8 S .. + 8] (weights 64 c + 8 S + e are the
+// ones that lane decodes). Fetched directly, each
+// instruction would touch 64 cache lines (16 rows x 4 runs), which measured
+// as the dominant cost; instead the wave reads the 16 rows x 512 bytes
+// coalesced (rows 2i and 2i + 1 per instruction, one 16-byte chunk per lane),
+// transposes through its LDS slot and reads back its fragments.
+template <int MT>
+__device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__ slot,
+                                             const uint16_t* const (&xrows)[MT][8], int b,
+                                             int lane, int j, int c) {
+    u32x4 raw[MT][8];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            raw[mt][i] = *reinterpret_cast<const u32x4*>(xrows[mt][i] + b * kT);
+    const int q = lane & 31;             // 16-byte chunk of the row's block
+    const int s = q & 7, cq = q >> 3;    // fragment and lane group c it belongs to
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            slot[(mt * 8 + s) * kSlotChunks + 17 * cq + 2 * i + (lane >> 5)] = raw[mt][i];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int S = 0; S < 8; ++S) xf.v[mt][S] = slot[(mt * 8 + S) * kSlotChunks + 17 * c + j];
+}
+
+// One task: eight fragments, the gathers of the next two in flight while one is
+// packed and multiplied against the MT activation tiles. A new block first
+// refreshes the activation fragments: a rare path, and the only one whose
+// memory wait covers the prefetched code words.
 template <int K, int MT>
-__device__ __forceinline__ void block_mma(const uint32_t (&w)[2 * K + 1],
-                                          const float* __restrict__ lut_s, float scale,
-                                          const uint16_t* __restrict__ xrow0,
-                                          const uint16_t* __restrict__ xrow1,
-                                          floatx4 (&acc)[MT]) {
+__device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, int& xb, u32x4* __restrict__ slot,
+                                         const uint16_t* const (&xrows)[MT][8],
+                                         floatx4 (&acc)[kGroups][MT],
+                                         const float* __restrict__ tab, int lane, int j, int c) {
+    constexpr bool P = false;
+    if (t.b != xb) {
+        xb = t.b;
+        load_x_block<MT>(xf, slot, xrows, t.b, lane, j, c);
+    }
+    if (!t.valid) {
+#pragma unroll
+        for (int i = 0; i < 2 * K; ++i) t.w[i] = 0u;
+    }
+    t.w[2 * K] = next_run_word(t.w[0]);
+    floatx4 cur[MT];
+    static_for<0, kGroups>([&](auto gc) {
+        constexpr int G = decltype(gc)::value;
+        if (t.g == G) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) cur[mt] = acc[G][mt];
+        }
+    });
+    Gathered<P> g0 = gather_run64<K, 0, P>(t.w, tab);
+    Gathered<P> g1 = gather_run64<K, 1, P>(t.w, tab);
     static_for<0, 8>([&](auto sc) {
         constexpr int S = decltype(sc)::value;
-        const bf16x8 bfrag = as_bf16x8(run64_fragment<K, S, false>(w, lut_s, scale));
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(xrow0 + 8 * S);
-        acc[0] = mfma16x16x32(as_bf16x8(a0), bfrag, acc[0]);
-        if constexpr (MT == 2) {
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(xrow1 + 8 * S);
-            acc[1] = mfma16x16x32(as_bf16x8(a1), bfrag, acc[1]);
+        Gathered<P> g2;
+        if constexpr (S + 2 < 8) g2 = gather_run64<K, S + 2, P>(t.w, tab);
+        const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g0, t.scale));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            cur[mt] = mfma16x16x32(as_bf16x8(xf.v[mt][S]), bfrag, cur[mt]);
+        g0 = g1;
+        if constexpr (S + 2 < 8) g1 = g2;
+    });
+    static_for<0, kGroups>([&](auto gc) {
+        constexpr int G = decltype(gc)::value;
+        if (t.g == G) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[G][mt] = cur[mt];
         }
     });
 }
 
 template <int K, int MT>
-__global__ __launch_bounds__(kThreads) void axis1_mma_kernel(
+__global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
     const float* __restrict__ scales, const float* __restrict__ lut,
     uint16_t* __restrict__ y, int N, int nb, int M) {
-    constexpr int wpb = Bits<K>::wpb;
-    __shared__ __attribute__((aligned(16))) float lut_s[kLutEntries];
-    __shared__ float red[4][MT * 16][16];
+    constexpr int kThreadsP = PrefillShape<MT>::threads, kWaves = PrefillShape<MT>::waves;
+    __shared__ __attribute__((aligned(16))) float lds[PrefillLds<MT>::floats];
+    float* const tab = lds;
 
+    const int G = gridDim.x, wg = blockIdx.x;
+    const int r0 = static_cast<int>(static_cast<long>(wg) * N / G);
+    const int r1 = static_cast<int>(static_cast<long>(wg + 1) * N / G);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, c = lane >> 4, cp = 3 - c;
-    const int n0 = blockIdx.x * 16;
-    const int n = n0 + j;
-    const int row = n < N ? n : N - 1;  // ragged tail: valid address, result dropped
+    const int gc = (r1 - r0 + 15) >> 4;  // groups in this workgroup, <= kGroups
+    const int tasks = gc * nb;
+    const int tau0 = static_cast<int>(static_cast<long>(wave) * tasks / kWaves);
+    const int tau1 = static_cast<int>(static_cast<long>(wave + 1) * tasks / kWaves);
     const long in = static_cast<long>(nb) * kT;
-    const uint32_t* __restrict__ rowp = codes + static_cast<size_t>(row) * nb * wpb;
-    const float scale = scales[row];
-    // A-fragment rows: m = j (and 16 + j); rows past M read row 0 (see block_mma).
-    const uint16_t* __restrict__ xr0 = x + (j < M ? j : 0) * in + 64 * c;
-    const uint16_t* __restrict__ xr1 = x + (16 + j < M ? 16 + j : 0) * in + 64 * c;
 
-    uint32_t wa[2 * K + 1], wb[2 * K + 1];
-    if (wave < nb) load_run64<K>(rowp + static_cast<size_t>(wave) * wpb, cp, wa);
-    stage_lut<kThreads>(lut_s, lut);
-    __syncthreads();
-
-    floatx4 acc[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    // Blocks wave, wave + 4, ...; two register sets ping-pong so the next
-    // block's words are in flight while the current one is decoded.
-    for (int b = wave; b < nb; b += 8) {
-        if (b + 4 < nb) load_run64<K>(rowp + static_cast<size_t>(b + 4) * wpb, cp, wb);
-        block_mma<K, MT>(wa, lut_s, scale, xr0 + static_cast<long>(b) * kT,
-                         xr1 + static_cast<long>(b) * kT, acc);
-        if (b + 4 >= nb) break;
-        if (b + 8 < nb) load_run64<K>(rowp + static_cast<size_t>(b + 8) * wpb, cp, wa);
-        block_mma<K, MT>(wb, lut_s, scale, xr0 + static_cast<long>(b + 4) * kT,
-                         xr1 + static_cast<long>(b + 4) * kT, acc);
-    }
-
-    // D layout: lane holds D[m = 4c + v][n = j] of each 16x16 tile.
+    // Coalesced activation rows: instruction i of tile mt reads row
+    // 16 mt + 2 i + lane / 32. A rows past M read row M - 1: row m of A only
+    // feeds row m of D, which is never stored for m >= M.
+    const uint16_t* xrows[MT][8];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave][mt * 16 + 4 * c + v][j] = acc[mt][v];
+        for (int i = 0; i < 8; ++i) {
+            const int m = 16 * mt + 2 * i + (lane >> 5);
+            xrows[mt][i] = x + (m < M ? m : M - 1) * in + 8 * (lane & 31);
+        }
+    u32x4* const slot = reinterpret_cast<u32x4*>(lds + kLutEntries) + wave * PrefillLds<MT>::slot_chunks;
+
+    TaskCtx cx{codes, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp};
+    floatx4 acc[kGroups][MT];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[g][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const bool busy = tau1 > tau0;
+    Task<K> ta, tb, tc;
+    if (busy) {
+        load_task<K>(ta, cx, tau0, tau1);
+        load_task<K>(tb, cx, tau0 + 1, tau1);
+    }
+    stage_lut<kThreadsP>(tab, lut);
     __syncthreads();
-    for (int idx = tid; idx < MT * 16 * 16; idx += kThreads) {
-        const int m = idx >> 4, jj = idx & 15;
-        const float sum = ((red[0][m][jj] + red[1][m][jj]) + red[2][m][jj]) + red[3][m][jj];
-        const int nn = n0 + jj;
-        if (m < M && nn < N) y[static_cast<size_t>(m) * N + nn] = round_bf16(sum);
+
+    if (busy) {
+        XFrags<MT> xf;
+        int xb = -1;
+        // Three register sets rotate: the words of the next two tasks are in
+        // flight while one is decoded.
+        for (int t0 = tau0; t0 < tau1; t0 += 3) {
+            load_task<K>(tc, cx, t0 + 2, tau1);
+            run_task<K, MT>(ta, xf, xb, slot, xrows, acc, tab, lane, j, c);
+            load_task<K>(ta, cx, t0 + 3, tau1);
+            if (t0 + 1 < tau1) run_task<K, MT>(tb, xf, xb, slot, xrows, acc, tab, lane, j, c);
+            load_task<K>(tb, cx, t0 + 4, tau1);
+            if (t0 + 2 < tau1) run_task<K, MT>(tc, xf, xb, slot, xrows, acc, tab, lane, j, c);
+        }
+    }
+    __syncthreads();  // the table is dead from here on; its space takes the partials
+
+    // part[wave][group][m][j]: D[m = 4c + v][j] of each tile; untouched groups add zeros.
+    float* const part = lds;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                part[((wave * kGroups + g) * 16 + 4 * c + v) * 16 + j] = acc[g][mt][v];
+        __syncthreads();
+        for (int idx = tid; idx < gc * 256; idx += kThreadsP) {
+            const int g = idx >> 8, m = (idx >> 4) & 15, jj = idx & 15;
+            float s = 0.f;
+            for (int w = 0; w < kWaves; ++w) s += part[((w * kGroups + g) * 16 + m) * 16 + jj];
+            const int row = r0 + 16 * g + jj, mm = 16 * mt + m;
+            if (mm < M && row < r1) y[static_cast<size_t>(mm) * N + row] = round_bf16(s);
+        }
+        __syncthreads();
     }
 }
 
@@ -139,9 +297,14 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(
 template <int K, int MT>
 hipError_t launch_axis1_k(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
                           const float* lut, uint16_t* y, int N, int nb, hipStream_t st) {
-    const dim3 grid((N + 15) / 16);
-    return launch_kernel(axis1_mma_kernel<K, MT>, grid, dim3(kThreads), st, x, codes, scales, lut, y,
-                         N, nb, M);
+    // One workgroup per compute unit while that leaves at most kGroups groups
+    // each; beyond that, as many workgroups as needed, run in rounds.
+    const int groups = (N + 15) / 16;
+    int G = groups < cu_count() ? groups : cu_count();
+    if ((N + G - 1) / G > 16 * kGroups) G = (N + 16 * kGroups - 1) / (16 * kGroups);
+    return launch_kernel(axis1_prefill_kernel<K, MT>, dim3(G), dim3(PrefillShape<MT>::threads), st,
+                         x, codes, scales,
+                         lut, y, N, nb, M);
 }
 
 template <int K>

@@ -130,6 +130,39 @@ __device__ __forceinline__ void load_run64(const uint32_t* __restrict__ block, i
     w[2 * K] = load_words<uint32_t, STREAM>(block + (nxt == wpb ? 0 : nxt));
 }
 
+// The 2k run words only; the word after the run comes from the neighbour lane
+// (next_run_word) instead of a second load.
+template <int K>
+__device__ __forceinline__ void load_run64_words(const uint32_t* __restrict__ block, int cp,
+                                                 uint32_t (&w)[2 * K + 1]) {
+    const uint32_t* p = block + 2 * K * cp;
+    if constexpr (K == 2) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if constexpr (K == 3) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+        const u32x2 b = *reinterpret_cast<const u32x2*>(p + 2);
+        const u32x2 c = *reinterpret_cast<const u32x2*>(p + 4);
+        w[0] = a.x; w[1] = a.y; w[2] = b.x; w[3] = b.y; w[4] = c.x; w[5] = c.y;
+    } else {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(p);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(p + 4);
+        w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+        w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+    }
+}
+
+// When the four runs of a block sit in lanes l, l + 16, l + 32, l + 48 with
+// run cp = 3 - l / 16, the word after run cp is the first word of run cp + 1,
+// held 16 lanes below; after the last run (cp = 3) it is word 0 of the block,
+// run 0, held 48 lanes above. Both are a rotation of the wave by 16 lanes.
+__device__ __forceinline__ uint32_t next_run_word(uint32_t first_word) {
+    const int lane = threadIdx.x & 63;
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_ds_bpermute(((lane - 16) & 63) << 2, static_cast<int>(first_word)));
+}
+
 // Entries of the k = 2 pair table: entry F (the 14-bit union of the windows
 // of an adjacent pair of weights, which overlap by 10 bits) holds
 // (LUT[F >> 2], LUT[F & 0xFFF]), the values of the earlier and the later weight.

@@ -18,6 +18,9 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_
     return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, st);
 }
 
+// Compute units of the current device (cached per device).
+int cu_count();
+
 // Axis-1 GEMV (M = 1): persistent kernel, one workgroup per compute unit,
 // activations staged in LDS. Needs nb <= gemv_max_blocks(k).
 hipError_t launch_gemv(const uint16_t* x, const uint32_t* codes, const float* scales,
@@ -25,6 +28,7 @@ hipError_t launch_gemv(const uint16_t* x, const uint32_t* codes, const float* sc
 int gemv_max_blocks(int k);
 
 // Axis 1, 1 <= M <= 32: y[M][N] from x[M][nb*256] and codes [N][nb][8k].
+// Persistent workgroups of at most 80 rows; any nb.
 hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
                         const float* lut, uint16_t* y, int N, int nb, int k, hipStream_t st);
 

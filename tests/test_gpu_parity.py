@@ -216,6 +216,20 @@ def test_prefill_small(gpu_lib, M, axis):
     assert gate(y, oracle_y(p)) <= TOL
 
 
+@pytest.mark.parametrize("M", [3, 20])
+def test_prefill_axis1_more_rows_than_persistent_grid(gpu_lib, M):
+    """25000 output rows exceed 80 rows per workgroup on every compute unit:
+    the axis-1 kernel then launches workgroups in rounds. Two blocks per row
+    leave most waves of a workgroup without tasks."""
+    T = gpu_lib
+    k = 2 + M % 3
+    shape = synth.Shape(1, 256, L, k, 512, 25000)
+    p = synth.make_problem(shape, M, CFG["test"], proj=600 + M)
+    say(f"prefill axis=1 in=512 out=25000 M={M} k={k}")
+    y = bf16_to_f64(run(T, Dev(p, T)))
+    assert gate(y, oracle_y(p)) <= TOL
+
+
 @pytest.mark.parametrize("k", [2, 3, 4])
 @pytest.mark.parametrize("M", [5, 8, 16, 32])
 def test_prefill_qwen_up_sampled(gpu_lib, M, k):
