@@ -50,17 +50,17 @@ struct PrefillShape {
     static constexpr int waves = threads / kWave;
 };
 
-// Per-wave activation slot: the eight A fragments of each M tile, in lane
-// order, 16-byte chunks; chunk (S, c, j) sits at S * kSlotChunks + 17 c + j, a
-// skew that keeps both the transposing writes and the lane-order reads off
-// shared banks.
-constexpr int kSlotChunks = 67;
-
-template <int MT>
+// Per-wave activation slot: `lines` 128-byte lines (8 chunks of 16 bytes) of
+// each of the 16 rows of each M tile. Beside the 128 KB pair table only one
+// line fits (2 KB per tile); beside the 16 KB codebook all four do.
+template <int K, int MT>
 struct PrefillLds {
+    static constexpr bool pair = K == 2;
+    static constexpr int tab_floats = pair ? 2 * kPairEntries : kLutEntries;
     static constexpr int waves = PrefillShape<MT>::waves;
-    static constexpr int slot_chunks = MT * 8 * kSlotChunks;
-    static constexpr int decode_floats = kLutEntries + waves * slot_chunks * 4;
+    static constexpr int lines = pair ? 1 : 4;
+    static constexpr int slot_chunks = MT * lines * 16 * 8;
+    static constexpr int decode_floats = tab_floats + waves * slot_chunks * 4;
     static constexpr int part_floats = waves * kGroups * 256;  // one M tile of wave partials
     static constexpr int floats = decode_floats > part_floats ? decode_floats : part_floats;
 };
@@ -103,33 +103,76 @@ struct XFrags {
 };
 
 // Activation fragments of block b for a wave: A fragment S of lane (j, c) is
-// x[m = 16 mt + j][256 b + 64 c + 8 S .. + 8] (weights 64 c + 8 S + e are the
-// ones that lane decodes). Fetched directly, each
-// instruction would touch 64 cache lines (16 rows x 4 runs), which measured
-// as the dominant cost; instead the wave reads the 16 rows x 512 bytes
-// coalesced (rows 2i and 2i + 1 per instruction, one 16-byte chunk per lane),
-// transposes through its LDS slot and reads back its fragments.
-template <int MT>
+// x[m = 16 mt + j][256 b + 64 c + 8 S .. + 8] (the weights 64 c + 8 S + e are
+// the ones that lane decodes), i.e. chunk S of 128-byte line c of the row's
+// block. Fetched directly, each instruction would touch 64 cache lines (16
+// rows x 4 lines), which measured as the dominant cost. Instead instruction
+// (c, h) reads line c of rows 8h .. 8h + 7 (8 lanes per line, coalesced) and
+// the lines pass through the wave's LDS slot to the lanes of group c: all
+// four at once when the slot holds them, else one at a time. Chunk S of row r
+// of a line sits at slot chunk 8 r + (S ^ (r & 7)), so the writes are
+// conflict-free and the reads at most 2-way.
+template <int MT, int LINES>
 __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__ slot,
-                                             const uint16_t* const (&xrows)[MT][8], int b,
+                                             const uint16_t* const (&xrows)[MT][2], int b,
                                              int lane, int j, int c) {
-    u32x4 raw[MT][8];
+    const int wr = lane >> 3, ws = lane & 7;  // row within the half and chunk this lane loaded
+    if constexpr (LINES == 4) {
+        u32x4 raw[MT][4][2];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            raw[mt][i] = *reinterpret_cast<const u32x4*>(xrows[mt][i] + b * kT);
-    const int q = lane & 31;             // 16-byte chunk of the row's block
-    const int s = q & 7, cq = q >> 3;    // fragment and lane group c it belongs to
+            for (int line = 0; line < 4; ++line)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+                for (int h = 0; h < 2; ++h)
+                    raw[mt][line][h] =
+                        *reinterpret_cast<const u32x4*>(xrows[mt][h] + b * kT + 64 * line);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            slot[(mt * 8 + s) * kSlotChunks + 17 * cq + 2 * i + (lane >> 5)] = raw[mt][i];
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+            for (int line = 0; line < 4; ++line)
 #pragma unroll
-        for (int S = 0; S < 8; ++S) xf.v[mt][S] = slot[(mt * 8 + S) * kSlotChunks + 17 * c + j];
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 8 * h + wr;
+                    slot[((mt * 4 + line) * 16 + r) * 8 + (ws ^ (r & 7))] = raw[mt][line][h];
+                }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int S = 0; S < 8; ++S)
+                xf.v[mt][S] = slot[((mt * 4 + c) * 16 + j) * 8 + (S ^ (j & 7))];
+        return;
+    }
+    // Two lines at a time: fetching all four at once spills registers at k = 4.
+#pragma unroll
+    for (int l0 = 0; l0 < 4; l0 += 2) {
+        u32x4 raw[MT][2][2];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int dl = 0; dl < 2; ++dl)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    raw[mt][dl][h] =
+                        *reinterpret_cast<const u32x4*>(xrows[mt][h] + b * kT + 64 * (l0 + dl));
+#pragma unroll
+        for (int dl = 0; dl < 2; ++dl) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 8 * h + wr;
+                    slot[(mt * 16 + r) * 8 + (ws ^ (r & 7))] = raw[mt][dl][h];
+                }
+            if (c == l0 + dl) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int S = 0; S < 8; ++S)
+                        xf.v[mt][S] = slot[(mt * 16 + j) * 8 + (S ^ (j & 7))];
+            }
+        }
+    }
 }
 
 // One task: eight fragments, the gathers of the next two in flight while one is
@@ -138,13 +181,13 @@ __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__
 // memory wait covers the prefetched code words.
 template <int K, int MT>
 __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, int& xb, u32x4* __restrict__ slot,
-                                         const uint16_t* const (&xrows)[MT][8],
+                                         const uint16_t* const (&xrows)[MT][2],
                                          floatx4 (&acc)[kGroups][MT],
                                          const float* __restrict__ tab, int lane, int j, int c) {
-    constexpr bool P = false;
+    constexpr bool P = PrefillLds<K, MT>::pair;
     if (t.b != xb) {
         xb = t.b;
-        load_x_block<MT>(xf, slot, xrows, t.b, lane, j, c);
+        load_x_block<MT, PrefillLds<K, MT>::lines>(xf, slot, xrows, t.b, lane, j, c);
     }
     if (!t.valid) {
 #pragma unroll
@@ -187,7 +230,7 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     const float* __restrict__ scales, const float* __restrict__ lut,
     uint16_t* __restrict__ y, int N, int nb, int M) {
     constexpr int kThreadsP = PrefillShape<MT>::threads, kWaves = PrefillShape<MT>::waves;
-    __shared__ __attribute__((aligned(16))) float lds[PrefillLds<MT>::floats];
+    __shared__ __attribute__((aligned(16))) float lds[PrefillLds<K, MT>::floats];
     float* const tab = lds;
 
     const int G = gridDim.x, wg = blockIdx.x;
@@ -202,18 +245,19 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     const int tau1 = static_cast<int>(static_cast<long>(wave + 1) * tasks / kWaves);
     const long in = static_cast<long>(nb) * kT;
 
-    // Coalesced activation rows: instruction i of tile mt reads row
-    // 16 mt + 2 i + lane / 32. A rows past M read row M - 1: row m of A only
-    // feeds row m of D, which is never stored for m >= M.
-    const uint16_t* xrows[MT][8];
+    // Coalesced activation rows: half h of tile mt is rows 16 mt + 8 h + lane / 8,
+    // lane % 8 the 16-byte chunk within a line. A rows past M read row M - 1:
+    // row m of A only feeds row m of D, which is never stored for m >= M.
+    const uint16_t* xrows[MT][2];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int m = 16 * mt + 2 * i + (lane >> 5);
-            xrows[mt][i] = x + (m < M ? m : M - 1) * in + 8 * (lane & 31);
+        for (int h = 0; h < 2; ++h) {
+            const int m = 16 * mt + 8 * h + (lane >> 3);
+            xrows[mt][h] = x + (m < M ? m : M - 1) * in + 8 * (lane & 7);
         }
-    u32x4* const slot = reinterpret_cast<u32x4*>(lds + kLutEntries) + wave * PrefillLds<MT>::slot_chunks;
+    u32x4* const slot = reinterpret_cast<u32x4*>(lds + PrefillLds<K, MT>::tab_floats) +
+                        wave * PrefillLds<K, MT>::slot_chunks;
 
     TaskCtx cx{codes, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp};
     floatx4 acc[kGroups][MT];
@@ -228,7 +272,10 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
         load_task<K>(ta, cx, tau0, tau1);
         load_task<K>(tb, cx, tau0 + 1, tau1);
     }
-    stage_lut<kThreadsP>(tab, lut);
+    if constexpr (PrefillLds<K, MT>::pair)
+        stage_pair_table<kThreadsP>(tab, lut);
+    else
+        stage_lut<kThreadsP>(tab, lut);
     __syncthreads();
 
     if (busy) {
