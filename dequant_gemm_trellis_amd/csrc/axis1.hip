@@ -202,18 +202,20 @@ __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, int& xb, u32
             for (int mt = 0; mt < MT; ++mt) cur[mt] = acc[G][mt];
         }
     });
-    Gathered<P> g0 = gather_run64<K, 0, P>(t.w, tab);
-    Gathered<P> g1 = gather_run64<K, 1, P>(t.w, tab);
-    static_for<0, 8>([&](auto sc) {
-        constexpr int S = decltype(sc)::value;
+    // Fragments 7 .. 0: only fragment 0 reads the word from the neighbouring
+    // lane, which thus has the whole task to arrive.
+    Gathered<P> g0 = gather_run64<K, 7, P>(t.w, tab);
+    Gathered<P> g1 = gather_run64<K, 6, P>(t.w, tab);
+    static_for<0, 8>([&](auto ic) {
+        constexpr int S = 7 - decltype(ic)::value;
         Gathered<P> g2;
-        if constexpr (S + 2 < 8) g2 = gather_run64<K, S + 2, P>(t.w, tab);
+        if constexpr (S >= 2) g2 = gather_run64<K, S - 2, P>(t.w, tab);
         const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g0, t.scale));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
             cur[mt] = mfma16x16x32(as_bf16x8(xf.v[mt][S]), bfrag, cur[mt]);
         g0 = g1;
-        if constexpr (S + 2 < 8) g1 = g2;
+        if constexpr (S >= 2) g1 = g2;
     });
     static_for<0, kGroups>([&](auto gc) {
         constexpr int G = decltype(gc)::value;

@@ -17,12 +17,12 @@
 //
 // Work mapping. The grid is persistent: one 1024-thread workgroup per compute
 // unit, workgroup g owning rows [g N / G, (g+1) N / G), so every CU gets the
-// same number of rows. A unit of work is one 256-weight block of one row, and
-// units are numbered block-major inside a row chunk: the 16 units a wave takes
-// together are 16 rows of one block, so the lanes that share a run index c
-// read the same activations (broadcast reads of the LDS copy; numbered
-// row-major, each lane reads its own 128 B of activations per unit and the
-// LDS, already the bottleneck, spends about a third more time).
+// same number of rows. A unit of work is one 256-weight block of one row;
+// units are numbered block-major inside a row chunk (all rows of block 0,
+// then block 1, ...) and wave w takes the contiguous range
+// [w U / 16, (w + 1) U / 16), 16 units per step. The 16 units of a step are
+// thus 16 rows of one block (two where the range crosses a block edge), and a
+// lane's block changes only once or twice over the wave's whole range.
 // Lane l = 16 c + j takes the 64-weight run c of the unit in its column j.
 // The run's 64 weights form eight 8-weight B fragments of
 // v_mfma_f32_16x16x32_bf16 and the A fragment of the same lane carries the 8
@@ -33,11 +33,11 @@
 // row is summed over its blocks in ascending order, so the result does not
 // depend on timing.
 //
-// The activations are staged in LDS once per workgroup (each lane needs 128 B
-// of them per unit; served from the cache hierarchy instead, they cost
-// several times the code traffic). Block b starts at byte 528 b, a stride of
-// 132 words (4 mod 64), which keeps the reads of a wave that straddles two
-// blocks on disjoint banks.
+// The activations are staged in LDS once per workgroup (served from the cache
+// hierarchy instead, they cost several times the code traffic) and a lane
+// keeps its unit's A fragments in registers until its block changes. Block b
+// starts at byte 528 b, a stride of 132 words (4 mod 64), which keeps the
+// reads of lanes on two different blocks on disjoint banks.
 //
 // Code words are prefetched two steps ahead into registers: measured under
 // load, a memory round trip takes longer than one step of decode.
@@ -49,7 +49,6 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kUnitsPerStep = kWaves * 16;
 constexpr int kPartialCap = 2048;    // unit partials held in LDS per row chunk
 constexpr int kXStride = 528;        // bytes per staged activation block (512 + 16)
 
@@ -60,6 +59,9 @@ struct GemvLds {
     // activation bytes that fit beside the table and the partials in 160 KB
     static constexpr int x_bytes = pair ? 24576 : 65536;
     static constexpr int max_blocks = x_bytes / kXStride;
+    // fragments whose gathers are in flight ahead of the one being packed
+    // (3 and 4 measured no faster)
+    static constexpr int depth = 2;
 };
 
 // Code words of one step for one lane, plus the unit's block and the
@@ -90,11 +92,12 @@ __device__ __forceinline__ uint32_t div_magic(int d) {
     return static_cast<uint32_t>(((1ull << 31) + d - 1) / d);
 }
 
-// Unit u of the chunk (block-major): block u / cr, chunk row u % cr.
+// Unit u of the chunk (block-major): block u / cr, chunk row u % cr. Units at
+// or past the wave's end re-read its last unit.
 template <int K>
-__device__ __forceinline__ void load_step(Step<K>& st, const Ctx& cx, int u, int U) {
+__device__ __forceinline__ void load_step(Step<K>& st, const Ctx& cx, int u, int u_end) {
     constexpr int wpb = Bits<K>::wpb;
-    const uint32_t uu = static_cast<uint32_t>(u < U ? u : U - 1);  // idle lanes re-read a valid unit
+    const uint32_t uu = static_cast<uint32_t>(u < u_end ? u : u_end - 1);
     const uint32_t b = __umulhi(uu << 1, cx.magic);
     const uint32_t rl = uu - b * static_cast<uint32_t>(cx.cr);
     st.b = b;
@@ -117,26 +120,37 @@ __device__ __forceinline__ XFrag load_x(const char* __restrict__ xs, uint32_t b,
 // The word after the run is not loaded but taken from the lane that holds the
 // next run (next_run_word): one vector-memory instruction less per step
 // measurably helps, since cache-missing loads slow the LDS-bound decode.
+// The A fragments stay in registers while the lane's unit stays in the same
+// block (xb), which with contiguous unit ranges per wave is all but one or two
+// steps; re-reading them every step would cost about a quarter of the LDS time.
 template <int K>
-__device__ __forceinline__ void run_step(Step<K> st, const char* __restrict__ xs,
+__device__ __forceinline__ void run_step(Step<K> st, XFrag& xf, uint32_t& xb,
+                                         const char* __restrict__ xs,
                                          const float* __restrict__ tab, float* __restrict__ part,
-                                         int u, int U, int j, int c) {
+                                         int u, int u_end, int j, int c) {
     constexpr bool P = GemvLds<K>::pair;
     st.w[2 * K] = next_run_word(st.w[0]);
-    const XFrag xf = load_x(xs, st.b, c);
+    if (st.b != xb) {
+        xb = st.b;
+        xf = load_x(xs, st.b, c);
+    }
+    // Fragments in the order 7 .. 0: only the run's first weights (fragment 0)
+    // have windows reaching into the next run's word, so its exchange has the
+    // whole step to arrive.
+    constexpr int D = GemvLds<K>::depth;
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    Gathered<P> g0 = gather_run64<K, 0, P>(st.w, tab);
-    Gathered<P> g1 = gather_run64<K, 1, P>(st.w, tab);
-    static_for<0, 8>([&](auto sc) {
-        constexpr int S = decltype(sc)::value;
-        Gathered<P> g2;
-        if constexpr (S + 2 < 8) g2 = gather_run64<K, S + 2, P>(st.w, tab);
-        const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g0, st.scale));
-        acc = mfma16x16x32(as_bf16x8(xf.v[S]), bfrag, acc);
-        g0 = g1;
-        if constexpr (S + 2 < 8) g1 = g2;
+    Gathered<P> g[8];
+    static_for<0, D>([&](auto ic) {
+        constexpr int S = 7 - decltype(ic)::value;
+        g[S] = gather_run64<K, S, P>(st.w, tab);
     });
-    if (c == (j >> 2) && u < U) {
+    static_for<0, 8>([&](auto ic) {
+        constexpr int S = 7 - decltype(ic)::value;
+        if constexpr (S >= D) g[S - D] = gather_run64<K, S - D, P>(st.w, tab);
+        const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g[S], st.scale));
+        acc = mfma16x16x32(as_bf16x8(xf.v[S]), bfrag, acc);
+    });
+    if (c == (j >> 2) && u < u_end) {
         const int v = j & 3;
         part[st.slot] = v == 0 ? acc[0] : v == 1 ? acc[1] : v == 2 ? acc[2] : acc[3];
     }
@@ -148,9 +162,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const float* __restrict__ scales, const float* __restrict__ lut,
     uint16_t* __restrict__ y, int N, int nb) {
     constexpr int wpb = Bits<K>::wpb;
-    __shared__ __attribute__((aligned(16))) float tab[GemvLds<K>::tab_floats];
-    __shared__ __attribute__((aligned(16))) char xs[GemvLds<K>::x_bytes];
-    __shared__ float part[kPartialCap];
+    // One LDS array with the table first: a gather address then needs no base
+    // added (the table at 64 KB, past the 16-bit instruction offset, costs a
+    // VALU op per weight).
+    __shared__ __attribute__((aligned(16)))
+    float lds[GemvLds<K>::tab_floats + GemvLds<K>::x_bytes / 4 + kPartialCap];
+    float* const tab = lds;
+    char* const xs = reinterpret_cast<char*>(lds + GemvLds<K>::tab_floats);
+    float* const part = lds + GemvLds<K>::tab_floats + GemvLds<K>::x_bytes / 4;
 
     const int G = gridDim.x, g = blockIdx.x;
     const int r0 = static_cast<int>(static_cast<long>(g) * N / G);
@@ -159,16 +178,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, c = lane >> 4;
     const int chunk_rows = kPartialCap / nb;
-    const int my = wave * 16 + j;  // this lane's column slot within a step
 
     Ctx cx{codes + static_cast<size_t>(r0) * nb * wpb, scales + r0, nb, 1, 0u, 3 - c};
     Step<K> sa, sb, sc;
+    XFrag xf;
+    uint32_t xb = ~0u;
+    // Wave w takes units [w U / W, (w + 1) U / W) of the chunk, 16 per step.
     int CR = min(r1 - r0, chunk_rows), U = CR * nb;
-    if (CR > 0) {
+    int ub = wave * U / kWaves, ue = (wave + 1) * U / kWaves;
+    if (CR > 0 && ue > ub) {
         cx.cr = CR;
         cx.magic = div_magic(CR);
-        load_step<K>(sa, cx, my, U);
-        load_step<K>(sb, cx, my + kUnitsPerStep, U);
+        load_step<K>(sa, cx, ub + j, ue);
+        load_step<K>(sb, cx, ub + 16 + j, ue);
     }
     if constexpr (GemvLds<K>::pair)
         stage_pair_table<kThreads>(tab, lut);
@@ -182,13 +204,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     for (int cr0 = r0; cr0 < r1; cr0 += chunk_rows) {
         CR = min(r1 - cr0, chunk_rows);
         U = CR * nb;
-        if (cr0 != r0) {
+        ub = wave * U / kWaves;
+        ue = (wave + 1) * U / kWaves;
+        if (cr0 != r0 && ue > ub) {
             cx.codes = codes + static_cast<size_t>(cr0) * nb * wpb;
             cx.scales = scales + cr0;
             cx.cr = CR;
             cx.magic = div_magic(CR);
-            load_step<K>(sa, cx, my, U);
-            load_step<K>(sb, cx, my + kUnitsPerStep, U);
+            load_step<K>(sa, cx, ub + j, ue);
+            load_step<K>(sb, cx, ub + 16 + j, ue);
         }
         // Three register sets rotate, so the code words of the next two steps
         // are in flight while one step is decoded. Every load is
@@ -196,15 +220,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         // decode steps are guarded: the memory-counter waits the compiler
         // places must hold on every path, so a conditional load, or a loop
         // exit between loads, makes it wait for the prefetch too.
-        for (int u0 = 0; u0 < U; u0 += 3 * kUnitsPerStep) {
-            const int ua = u0 + my;
-            load_step<K>(sc, cx, ua + 2 * kUnitsPerStep, U);
-            run_step<K>(sa, xs, tab, part, ua, U, j, c);
-            load_step<K>(sa, cx, ua + 3 * kUnitsPerStep, U);
-            if (u0 + kUnitsPerStep < U) run_step<K>(sb, xs, tab, part, ua + kUnitsPerStep, U, j, c);
-            load_step<K>(sb, cx, ua + 4 * kUnitsPerStep, U);
-            if (u0 + 2 * kUnitsPerStep < U)
-                run_step<K>(sc, xs, tab, part, ua + 2 * kUnitsPerStep, U, j, c);
+        for (int u0 = ub; u0 < ue; u0 += 48) {
+            const int ua = u0 + j;
+            load_step<K>(sc, cx, ua + 32, ue);
+            run_step<K>(sa, xf, xb, xs, tab, part, ua, ue, j, c);
+            load_step<K>(sa, cx, ua + 48, ue);
+            if (u0 + 16 < ue) run_step<K>(sb, xf, xb, xs, tab, part, ua + 16, ue, j, c);
+            load_step<K>(sb, cx, ua + 64, ue);
+            if (u0 + 32 < ue) run_step<K>(sc, xf, xb, xs, tab, part, ua + 32, ue, j, c);
         }
         __syncthreads();
         for (int r = tid; r < CR; r += kThreads) {
