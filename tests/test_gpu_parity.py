@@ -268,6 +268,26 @@ def test_prefill_axis0_qwen_down_sampled(gpu_lib, M):
         assert gate(y[:, a:b], oracle_y(p, a, b)[:, a:b]) <= TOL, (a, b)
 
 
+def test_axis0_workspace_reused_across_shapes(gpu_lib):
+    """One workspace, sized for the largest call, serves a sequence of axis-0
+    calls of different shapes and batch sizes; stale contents do not leak."""
+    T = gpu_lib
+    shape = synth.Shape(0, 256, L, 3, 1000, 768)
+    big = synth.Shape(0, 256, L, 2, 4000, 1280)
+    ws = torch.full((T.workspace_bytes(big, 32, T.OP_PREFILL) // 4,), float("nan"),
+                    dtype=torch.float32, device="cuda:0")
+    for sh, M in ((shape, 1), (big, 32), (shape, 8), (big, 1), (shape, 32), (shape, 1)):
+        p = synth.make_problem(sh, M, CFG["test"], proj=700 + M + sh.k)
+        say(f"axis0 reused workspace in={sh.in_features} out={sh.out_features} M={M} k={sh.k}")
+        d = Dev(p, T)
+        if M == 1:
+            y = T.gemv_scatter(d.x.reshape(-1), d.codes, d.scales, d.lut, sh, workspace=ws)
+        else:
+            y = T.prefill(d.x, d.codes, d.scales, d.lut, sh, workspace=ws)
+        torch.cuda.synchronize()
+        assert gate(bf16_to_f64(y.reshape(M, -1)), oracle_y(p)) <= TOL
+
+
 def test_prefill_deterministic(gpu_lib):
     T = gpu_lib
     shape = synth.Shape(1, 256, L, 2, QWEN_IN, QWEN_OUT)
