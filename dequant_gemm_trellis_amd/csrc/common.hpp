@@ -215,19 +215,60 @@ __device__ __forceinline__ u32x4 run64_fragment(const uint32_t (&w)[2 * K + 1],
     return pack_fragment<PAIR>(gather_run64<K, S, PAIR>(w, tab), scale);
 }
 
+// Decode table staging in two phases, so that a kernel can issue its other
+// loads in between and wait for all of them once: fetch_table loads this
+// thread's share of the codebook into registers, store_table writes the LDS
+// table from them. With PAIR the table is the k = 2 pair table: entry F holds
+// (LUT[F >> 2], LUT[F & 0xFFF]); the four entries 4 grp + i share F >> 2 = grp
+// and take F & 0xFFF = 4 (grp & 1023) + i.
+template <int NTHREADS, bool PAIR>
+struct TableSrc {
+    static constexpr int n = (PAIR ? kPairEntries : kLutEntries) / 4 / NTHREADS;
+    float a[n];
+    float4 b[n];
+};
+
+template <int NTHREADS, bool PAIR>
+__device__ __forceinline__ void fetch_table(TableSrc<NTHREADS, PAIR>& src,
+                                            const float* __restrict__ lut) {
+    const float4* lut4 = reinterpret_cast<const float4*>(lut);
+#pragma unroll
+    for (int i = 0; i < TableSrc<NTHREADS, PAIR>::n; ++i) {
+        const int grp = threadIdx.x + NTHREADS * i;
+        if constexpr (PAIR) {
+            src.a[i] = lut[grp];
+            src.b[i] = lut4[grp & 1023];
+        } else {
+            src.b[i] = lut4[grp];
+        }
+    }
+}
+
+template <int NTHREADS, bool PAIR>
+__device__ __forceinline__ void store_table(const TableSrc<NTHREADS, PAIR>& src,
+                                            float* __restrict__ tab) {
+    float4* dst = reinterpret_cast<float4*>(tab);
+#pragma unroll
+    for (int i = 0; i < TableSrc<NTHREADS, PAIR>::n; ++i) {
+        const int grp = threadIdx.x + NTHREADS * i;
+        if constexpr (PAIR) {
+            const float a = src.a[i];
+            const float4 b = src.b[i];
+            dst[2 * grp] = float4{a, b.x, a, b.y};
+            dst[2 * grp + 1] = float4{a, b.z, a, b.w};
+        } else {
+            dst[grp] = src.b[i];
+        }
+    }
+}
+
 // Build the k = 2 pair table in LDS from the codebook in global memory.
 template <int NTHREADS>
 __device__ __forceinline__ void stage_pair_table(float* __restrict__ tab,
                                                  const float* __restrict__ lut) {
-    const float4* lut4 = reinterpret_cast<const float4*>(lut);
-    float4* dst = reinterpret_cast<float4*>(tab);
-    for (int grp = threadIdx.x; grp < kPairEntries / 4; grp += NTHREADS) {
-        // F = 4 grp + i, i = 0..3: F >> 2 = grp and F & 0xFFF = 4 (grp & 1023) + i
-        const float a = lut[grp];
-        const float4 b = lut4[grp & 1023];
-        dst[2 * grp] = float4{a, b.x, a, b.y};
-        dst[2 * grp + 1] = float4{a, b.z, a, b.w};
-    }
+    TableSrc<NTHREADS, true> src;
+    fetch_table<NTHREADS, true>(src, lut);
+    store_table<NTHREADS, true>(src, tab);
 }
 
 __device__ __forceinline__ uint16_t round_bf16(float f) {

@@ -183,22 +183,42 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     Step<K> sa, sb, sc;
     XFrag xf;
     uint32_t xb = ~0u;
+    // Prologue: the codebook and the activations are fetched first, then the
+    // first two steps' code words; the table and activation stores then wait
+    // only for their own data (memory-counter waits retire in issue order),
+    // while the code words are still on their way from HBM.
+    constexpr bool kPair = GemvLds<K>::pair;
+    constexpr int kXChunks = (GemvLds<K>::max_blocks * 32 + kThreads - 1) / kThreads;
+    TableSrc<kThreads, kPair> tsrc;
+    fetch_table<kThreads, kPair>(tsrc, lut);
+    u32x4 xv[kXChunks];
+#pragma unroll
+    for (int q = 0; q < kXChunks; ++q) {  // 16-byte chunks of x, 32 per block
+        const int i = tid + q * kThreads;   // past the end: re-read the last chunk
+        xv[q] = reinterpret_cast<const u32x4*>(x)[i < nb * 32 ? i : nb * 32 - 1];
+    }
+    // Keep the table and activation loads ahead of the code words. (At k = 3
+    // and 4 the compiler still sinks the one codebook load to its use, and the
+    // store waits for the code words there; without restrict on the codebook
+    // pointer it stays put, but the kernel measured 40% slower.)
+    asm volatile("" ::: "memory");
     // Wave w takes units [w U / W, (w + 1) U / W) of the chunk, 16 per step.
+    // Every workgroup owns at least one row (G <= N), so CR >= 1, and the
+    // first two steps are loaded unconditionally (a wave without units
+    // re-reads a valid one): a load under a branch would make the table
+    // stores below wait for the code words too.
     int CR = min(r1 - r0, chunk_rows), U = CR * nb;
     int ub = wave * U / kWaves, ue = (wave + 1) * U / kWaves;
-    if (CR > 0 && ue > ub) {
-        cx.cr = CR;
-        cx.magic = div_magic(CR);
-        load_step<K>(sa, cx, ub + j, ue);
-        load_step<K>(sb, cx, ub + 16 + j, ue);
+    cx.cr = CR;
+    cx.magic = div_magic(CR);
+    load_step<K>(sa, cx, ub + j, ue > 1 ? ue : 1);
+    load_step<K>(sb, cx, ub + 16 + j, ue > 1 ? ue : 1);
+    store_table<kThreads, kPair>(tsrc, tab);
+#pragma unroll
+    for (int q = 0; q < kXChunks; ++q) {
+        const int i = tid + q * kThreads;
+        if (i < nb * 32) *reinterpret_cast<u32x4*>(xs + (i >> 5) * kXStride + (i & 31) * 16) = xv[q];
     }
-    if constexpr (GemvLds<K>::pair)
-        stage_pair_table<kThreads>(tab, lut);
-    else
-        stage_lut<kThreads>(tab, lut);
-    for (int i = tid; i < nb * 32; i += kThreads)  // 16-byte chunks of x, 32 per block
-        *reinterpret_cast<u32x4*>(xs + (i >> 5) * kXStride + (i & 31) * 16) =
-            reinterpret_cast<const u32x4*>(x)[i];
     __syncthreads();
 
     for (int cr0 = r0; cr0 < r1; cr0 += chunk_rows) {
