@@ -253,7 +253,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         for (int r = tid; r < CR; r += kThreads) {
             const float* pr = part + r * nb;
             float s = 0.f;
-            for (int q = 0; q < nb; ++q) s += pr[q];
+            int q = 0;
+            for (; q + 8 <= nb; q += 8) {  // reads issued together, added in order
+                float v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = pr[q + i];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s += v[i];
+            }
+            for (; q < nb; ++q) s += pr[q];
             y[cr0 + r] = round_bf16(s);
         }
         __syncthreads();
