@@ -166,8 +166,25 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
     const int per = (G + 3) / 4;
     const int g0 = q * per, g1 = min(G, g0 + per);
     float s = 0.f;
-    if (i < MC)
-        for (int g = g0; g < g1; ++g) s += partial[static_cast<size_t>(g) * MC + i];
+    if (i < MC) {
+        int g = g0;
+        for (; g + 8 <= g1; g += 8) {  // loads issued together, added in order
+            float v[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = partial[static_cast<size_t>(g + t) * MC + i];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) s += v[t];
+        }
+        if (g + 4 <= g1) {
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = partial[static_cast<size_t>(g + t) * MC + i];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) s += v[t];
+            g += 4;
+        }
+        for (; g < g1; ++g) s += partial[static_cast<size_t>(g) * MC + i];
+    }
     red[q][lane] = s;
     __syncthreads();
     if (q == 0 && i < MC) y[i] = round_bf16(((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
