@@ -97,6 +97,38 @@ __device__ __forceinline__ void load_task(Task<K>& t, const TaskCtx& cx, int tau
     t.scale = cx.scales[rc];
 }
 
+// load_task through opaque global-address-space pointers, for the prologue:
+// through the restrict kernel pointers the loads count as invariant and the
+// compiler sinks them past the table stores and the barrier to their first
+// use, so the table stores and the code words no longer overlap.
+template <int K>
+__device__ __forceinline__ void load_task_opaque(Task<K>& t, const TaskCtx& cx, int tau, int tau_end) {
+    using gu32 = const __attribute__((address_space(1))) uint32_t*;
+    using gu32x4 = const __attribute__((address_space(1))) u32x4*;
+    using gf32 = const __attribute__((address_space(1))) float*;
+    constexpr int wpb = Bits<K>::wpb;
+    gu32 codes = (gu32)cx.codes;  // generic to global: an address-space cast
+    gf32 scales = (gf32)cx.scales;
+    asm volatile("" : "+s"(codes), "+s"(scales));
+    const int tc = tau < tau_end ? tau : tau_end - 1;
+    const int b = tc / cx.gc;
+    const int g = tc - b * cx.gc;
+    const int row = cx.r0 + 16 * g + cx.j;
+    t.valid = row < cx.r1;
+    const int rc = t.valid ? row : cx.r1 - 1;
+    t.b = b;
+    t.g = g;
+    const gu32 p = codes + (static_cast<size_t>(rc) * cx.nb + b) * wpb + 2 * K * cx.cp;
+    if constexpr (K == 2) {
+        const u32x4 v = *reinterpret_cast<gu32x4>(p);
+        t.w[0] = v.x; t.w[1] = v.y; t.w[2] = v.z; t.w[3] = v.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2 * K; ++i) t.w[i] = p[i];
+    }
+    t.scale = scales[rc];
+}
+
 template <int MT>
 struct XFrags {
     u32x4 v[MT][8];
@@ -268,31 +300,32 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[g][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    const bool busy = tau1 > tau0;
+    // Prologue: the codebook first, then the first two tasks' code words
+    // (unconditionally: a wave without tasks re-reads a valid one, and a load
+    // under a branch would make the table stores wait for the code words too).
+    constexpr bool kPair = PrefillLds<K, MT>::pair;
+    TableSrc<kThreadsP, kPair> tsrc;
+    fetch_table<kThreadsP, kPair>(tsrc, lut);
+    asm volatile("" ::: "memory");
     Task<K> ta, tb, tc;
-    if (busy) {
-        load_task<K>(ta, cx, tau0, tau1);
-        load_task<K>(tb, cx, tau0 + 1, tau1);
-    }
-    if constexpr (PrefillLds<K, MT>::pair)
-        stage_pair_table<kThreadsP>(tab, lut);
-    else
-        stage_lut<kThreadsP>(tab, lut);
+    load_task_opaque<K>(ta, cx, tau0, tau1 > 1 ? tau1 : 1);
+    load_task_opaque<K>(tb, cx, tau0 + 1, tau1 > 1 ? tau1 : 1);
+    asm volatile("" ::: "memory");
+    store_table<kThreadsP, kPair>(tsrc, tab);
     __syncthreads();
 
-    if (busy) {
-        XFrags<MT> xf;
-        int xb = -1;
-        // Three register sets rotate: the words of the next two tasks are in
-        // flight while one is decoded.
-        for (int t0 = tau0; t0 < tau1; t0 += 3) {
-            load_task<K>(tc, cx, t0 + 2, tau1);
-            run_task<K, MT>(ta, xf, xb, slot, xrows, acc, tab, lane, j, c);
-            load_task<K>(ta, cx, t0 + 3, tau1);
-            if (t0 + 1 < tau1) run_task<K, MT>(tb, xf, xb, slot, xrows, acc, tab, lane, j, c);
-            load_task<K>(tb, cx, t0 + 4, tau1);
-            if (t0 + 2 < tau1) run_task<K, MT>(tc, xf, xb, slot, xrows, acc, tab, lane, j, c);
-        }
+    // Three register sets rotate: the words of the next two tasks are in
+    // flight while one is decoded. (No branch around the loop: the prologue's
+    // loads would be sunk into it, behind the barrier.)
+    XFrags<MT> xf;
+    int xb = -1;
+    for (int t0 = tau0; t0 < tau1; t0 += 3) {
+        load_task<K>(tc, cx, t0 + 2, tau1);
+        run_task<K, MT>(ta, xf, xb, slot, xrows, acc, tab, lane, j, c);
+        load_task<K>(ta, cx, t0 + 3, tau1);
+        if (t0 + 1 < tau1) run_task<K, MT>(tb, xf, xb, slot, xrows, acc, tab, lane, j, c);
+        load_task<K>(tb, cx, t0 + 4, tau1);
+        if (t0 + 2 < tau1) run_task<K, MT>(tc, xf, xb, slot, xrows, acc, tab, lane, j, c);
     }
     __syncthreads();  // the table is dead from here on; its space takes the partials
 

@@ -225,21 +225,28 @@ template <int NTHREADS, bool PAIR>
 struct TableSrc {
     static constexpr int n = (PAIR ? kPairEntries : kLutEntries) / 4 / NTHREADS;
     float a[n];
-    float4 b[n];
+    floatx4 b[n];
 };
 
+// The loads go through an opaque global-address-space copy of the pointer:
+// through a restrict kernel pointer they count as invariant, and the compiler
+// sinks them past any barrier to their use in store_table, after whatever the
+// kernel issued in between.
 template <int NTHREADS, bool PAIR>
-__device__ __forceinline__ void fetch_table(TableSrc<NTHREADS, PAIR>& src,
-                                            const float* __restrict__ lut) {
-    const float4* lut4 = reinterpret_cast<const float4*>(lut);
+__device__ __forceinline__ void fetch_table(TableSrc<NTHREADS, PAIR>& src, const float* lut) {
+    using gf32 = const __attribute__((address_space(1))) float*;
+    using gf32x4 = const __attribute__((address_space(1))) floatx4*;
+    gf32 l = (gf32)lut;  // generic to global: an address-space cast
+    asm volatile("" : "+s"(l));
+    const gf32x4 l4 = reinterpret_cast<gf32x4>(l);
 #pragma unroll
     for (int i = 0; i < TableSrc<NTHREADS, PAIR>::n; ++i) {
         const int grp = threadIdx.x + NTHREADS * i;
         if constexpr (PAIR) {
-            src.a[i] = lut[grp];
-            src.b[i] = lut4[grp & 1023];
+            src.a[i] = l[grp];
+            src.b[i] = l4[grp & 1023];
         } else {
-            src.b[i] = lut4[grp];
+            src.b[i] = l4[grp];
         }
     }
 }
@@ -253,11 +260,12 @@ __device__ __forceinline__ void store_table(const TableSrc<NTHREADS, PAIR>& src,
         const int grp = threadIdx.x + NTHREADS * i;
         if constexpr (PAIR) {
             const float a = src.a[i];
-            const float4 b = src.b[i];
-            dst[2 * grp] = float4{a, b.x, a, b.y};
-            dst[2 * grp + 1] = float4{a, b.z, a, b.w};
+            const floatx4 b = src.b[i];
+            dst[2 * grp] = float4{a, b[0], a, b[1]};
+            dst[2 * grp + 1] = float4{a, b[2], a, b[3]};
         } else {
-            dst[grp] = src.b[i];
+            const floatx4 b = src.b[i];
+            dst[grp] = float4{b[0], b[1], b[2], b[3]};
         }
     }
 }

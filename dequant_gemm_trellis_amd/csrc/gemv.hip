@@ -197,11 +197,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         const int i = tid + q * kThreads;   // past the end: re-read the last chunk
         xv[q] = reinterpret_cast<const u32x4*>(x)[i < nb * 32 ? i : nb * 32 - 1];
     }
-    // Keep the table and activation loads ahead of the code words. (At k = 3
-    // and 4 the compiler still sinks the one codebook load to its use, and the
-    // store waits for the code words there; without restrict on the codebook
-    // pointer it stays put, but the kernel measured 40% slower.)
-    asm volatile("" ::: "memory");
+    asm volatile("" ::: "memory");  // keep the table and activation loads ahead of the code words
     // Wave w takes units [w U / W, (w + 1) U / W) of the chunk, 16 per step.
     // Every workgroup owns at least one row (G <= N), so CR >= 1, and the
     // first two steps are loaded unconditionally (a wave without units
