@@ -87,6 +87,20 @@ def test_gemv_small(gpu_lib, i, o, k):
     assert gate(y, oracle_y(p)) <= TOL
 
 
+@pytest.mark.parametrize("k", [2, 4])
+def test_gemv_rows_in_several_chunks(gpu_lib, k):
+    """30000 rows of 5120: 118 rows per workgroup, more than the 102 unit
+    partials of 20 blocks the persistent kernel holds in LDS at once, so each
+    workgroup runs two row chunks. Checked on rows spread over the range."""
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, k, QWEN_IN, 30000)
+    p = synth.make_problem(shape, 1, CFG["test"], proj=800 + k)
+    say(f"gemv in=5120 out=30000 k={k} (two row chunks per workgroup)")
+    y = bf16_to_f64(run(T, Dev(p, T), op="gemv"))
+    rows = np.unique(np.concatenate([np.arange(0, 30000, 97), np.arange(100, 120), [29999]]))
+    assert gate(y[:, rows], oracle_y(row_subset(p, rows))) <= TOL
+
+
 @pytest.mark.parametrize("k", [2, 3, 4])
 def test_gemv_qwen_sampled(gpu_lib, k):
     T = gpu_lib
@@ -192,6 +206,20 @@ def test_scatter_integer_codebook_bit_exact(gpu_lib):
     y = bf16_bits(run(T, Dev(p, T), op="scatter"))
     exact = oracle_y(p)
     assert np.array_equal(y, synth.to_bf16_bits(exact.astype(np.float32)))
+
+
+@pytest.mark.parametrize("M", [1, 3, 20])
+def test_axis0_fewer_rows_than_splits(gpu_lib, M):
+    """37 input rows over 128 (or 64) splits: one row per split, most splits
+    empty, and an odd row count (the element-wise activation path)."""
+    T = gpu_lib
+    k = 2 + M % 3
+    shape = synth.Shape(0, 256, L, k, 37, 512)
+    p = synth.make_problem(shape, M, CFG["test"], proj=900 + M)
+    say(f"axis0 in=37 out=512 M={M} k={k}")
+    d = Dev(p, T)
+    y = run(T, d, op="scatter") if M == 1 else run(T, d)
+    assert gate(bf16_to_f64(y), oracle_y(p)) <= TOL
 
 
 def test_scatter_deterministic(gpu_lib):
