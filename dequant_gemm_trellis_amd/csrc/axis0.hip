@@ -29,8 +29,12 @@
 namespace trellis {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // split reduce
 constexpr int kTileCols = 128;
+// Splits per workgroup, one wave each; their partials are summed in LDS in
+// wave order. (8 or 16 per workgroup measured 15% and 3x slower.)
+constexpr int kA0Waves = 4;
+constexpr int kA0Threads = kA0Waves * kWave;
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     floatx2 p = {a, b};
@@ -38,7 +42,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 
 template <int K, int MT>
-__global__ __launch_bounds__(kThreads) void axis0_mma_kernel(
+__global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
     const float* __restrict__ scales, const float* __restrict__ lut,
     float* __restrict__ partial, int R, int C, int M, int S, int rows_per_split) {
@@ -48,10 +52,10 @@ __global__ __launch_bounds__(kThreads) void axis0_mma_kernel(
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, c = lane >> 4;
-    const int groups = (S + 3) / 4;
+    const int groups = (S + kA0Waves - 1) / kA0Waves;
     const int tile = blockIdx.x / groups;
     const int sgroup = blockIdx.x - tile * groups;
-    const int split = sgroup * 4 + wave;
+    const int split = sgroup * kA0Waves + wave;
     const int col0 = tile * kTileCols;
     const int blk = col0 / kT;
     const int t0 = (col0 % kT) + 8 * j;         // first weight of this lane's 8 columns
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void axis0_mma_kernel(
     if (r_end > R) r_end = R;
     if (r_begin > r_end) r_begin = r_end;
 
-    stage_lut<kThreads>(lut_s, lut);
+    stage_lut<kA0Threads>(lut_s, lut);
     __syncthreads();
 
     floatx4 acc[8][MT];
@@ -131,9 +135,9 @@ __global__ __launch_bounds__(kThreads) void axis0_mma_kernel(
         });
     }
 
-    // Sum the 4 waves' tiles in wave order through LDS; the last wave stores.
+    // Sum the waves' tiles in wave order through LDS; the last wave stores.
     // D layout: lane holds D[m = 4c + v][n = j] of each 16x16 tile.
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kA0Waves; ++w) {
         if (wave == w) {
 #pragma unroll
             for (int e = 0; e < 8; ++e)
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void axis0_mma_kernel(
                         const int m = mt * 16 + 4 * c + v;
                         const float prev = w == 0 ? 0.f : red[e][m][j];
                         const float sum = w == 0 ? acc[e][mt][v] : prev + acc[e][mt][v];
-                        if (w < 3) {
+                        if (w < kA0Waves - 1) {
                             red[e][m][j] = sum;
                         } else if (m < M) {
                             partial[(static_cast<size_t>(sgroup) * M + m) * C + col0 + 8 * j + e] = sum;
@@ -195,15 +199,15 @@ hipError_t launch_axis0_k(const uint16_t* x, int M, const uint32_t* codes, const
                           const float* lut, float* partial, int R, int C, int S,
                           hipStream_t st) {
     const int rows_per_split = (R + S - 1) / S;
-    const int groups = (S + 3) / 4;
+    const int groups = axis0_split_groups(S);
     const dim3 grid(static_cast<unsigned>((C / kTileCols) * groups));
-    return launch_kernel(axis0_mma_kernel<K, MT>, grid, dim3(kThreads), st, x, codes, scales, lut,
+    return launch_kernel(axis0_mma_kernel<K, MT>, grid, dim3(kA0Threads), st, x, codes, scales, lut,
                          partial, R, C, M, S, rows_per_split);
 }
 
 }  // namespace
 
-int axis0_split_groups(int S) { return (S + 3) / 4; }
+int axis0_split_groups(int S) { return (S + kA0Waves - 1) / kA0Waves; }
 
 hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
                         const float* lut, float* partial, uint16_t* y, int R, int C, int S, int k,
