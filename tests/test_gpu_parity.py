@@ -341,3 +341,48 @@ def test_mlp_projections_sampled(gpu_lib, M):
             assert gate(y[:, SAMPLE_ROWS], oracle_y(row_subset(p, SAMPLE_ROWS))) <= TOL
         else:
             assert gate(y[:, :40], oracle_y(p, 0, 40)[:, :40]) <= TOL
+
+
+# ------------------------------------------------------------- HIP graphs
+def test_graph_capture_replays_match_eager(gpu_lib):
+    """The entry points enqueue only kernels (no allocation, memset or host
+    sync on the compute path), so a sequence of them can be captured into a
+    HIP graph. Each replay, with eager work and synchronisation in between,
+    must reproduce the eager results bit for bit."""
+    T = gpu_lib
+    up = synth.Shape(1, 256, L, 2, 1024, 600)
+    down = synth.Shape(0, 256, L, 3, 600, 768)
+    pu = synth.make_problem(up, 1, CFG["test"], proj=950)
+    pp = synth.make_problem(up, 5, CFG["test"], proj=951)
+    pd = synth.make_problem(down, 1, CFG["test"], proj=952)
+    du, dp, dd = Dev(pu, T), Dev(pp, T), Dev(pd, T)
+    ws = torch.zeros(T.workspace_bytes(down, 1, T.OP_GEMV_SCATTER) // 4, dtype=torch.float32,
+                     device="cuda:0")
+    y1 = torch.empty(600, dtype=torch.bfloat16, device="cuda:0")
+    y2 = torch.empty((5, 600), dtype=torch.bfloat16, device="cuda:0")
+    y3 = torch.empty(768, dtype=torch.bfloat16, device="cuda:0")
+
+    def step(stream):
+        T.gemv(du.x.reshape(-1), du.codes, du.scales, du.lut, up, y=y1, stream=stream)
+        T.prefill(dp.x, dp.codes, dp.scales, dp.lut, up, y=y2, stream=stream)
+        T.gemv_scatter(dd.x.reshape(-1), dd.codes, dd.scales, dd.lut, down, workspace=ws,
+                       y=y3, stream=stream)
+
+    say("graph capture: gemv + prefill + scatter")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step(s)
+    torch.cuda.synchronize()
+    ref = [bf16_bits(y.clone()) for y in (y1, y2, y3)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step(s)
+    for rep in range(4):
+        for y in (y1, y2, y3):
+            y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for r, y in zip(ref, (y1, y2, y3)):
+            assert np.array_equal(bf16_bits(y), r), rep
+    assert gate(bf16_to_f64(y1.reshape(1, -1)), oracle_y(pu)) <= TOL
