@@ -386,3 +386,43 @@ def test_graph_capture_replays_match_eager(gpu_lib):
         for r, y in zip(ref, (y1, y2, y3)):
             assert np.array_equal(bf16_bits(y), r), rep
     assert gate(bf16_to_f64(y1.reshape(1, -1)), oracle_y(pu)) <= TOL
+
+
+# ------------------------------------------------------------ maximum sizes
+MAXF = 1 << 19  # largest in/out feature count the library accepts
+
+
+@pytest.mark.parametrize("k", [2, 4])
+def test_gemv_longest_rows(gpu_lib, k):
+    """2^19 inputs (2048 blocks per row): the long-row path of the GEMV."""
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, k, MAXF, 20)
+    p = synth.make_problem(shape, 1, CFG["test"], proj=960 + k)
+    say(f"gemv in=2^19 out=20 k={k}")
+    y = bf16_to_f64(run(T, Dev(p, T), op="gemv"))
+    assert gate(y, oracle_y(p)) <= TOL
+
+
+def test_gemv_most_rows(gpu_lib):
+    """2^19 output rows of 256 inputs, checked on rows spread over the range
+    (the last ones included)."""
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, 2, 256, MAXF)
+    p = synth.make_problem(shape, 1, CFG["test"], proj=970)
+    say("gemv in=256 out=2^19 k=2")
+    y = bf16_to_f64(run(T, Dev(p, T), op="gemv"))
+    rows = np.unique(np.concatenate([np.arange(0, MAXF, 4099), np.arange(MAXF - 40, MAXF)]))
+    assert gate(y[:, rows], oracle_y(row_subset(p, rows))) <= TOL
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_axis0_most_input_rows(gpu_lib, M):
+    """Axis 0 with 2^19 stored (input) rows over 256 output columns: 4096 rows
+    per split."""
+    T = gpu_lib
+    shape = synth.Shape(0, 256, L, 3, MAXF, 256)
+    p = synth.make_problem(shape, M, CFG["test"], proj=980 + M)
+    say(f"axis0 in=2^19 out=256 M={M} k=3")
+    d = Dev(p, T)
+    y = run(T, d, op="scatter") if M == 1 else run(T, d)
+    assert gate(bf16_to_f64(y), oracle_y(p)) <= TOL
