@@ -34,6 +34,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
+CUS, CLOCK_HZ = 256, 2.4e9      # MI355X compute units and peak engine clock
+# Codebook-gather ceiling, decoded weights per clock per CU, measured on MI355X
+# with a random-index LDS gather microbenchmark (uniform 12-bit indices):
+# ds_read_b64 from the 128 KB k = 2 pair table (two weights per lane) and
+# ds_read_b32 from the 16 KB codebook (k = 3, 4).
+GATHER_PEAK_W_PER_CLK = {2: 17.07, 3: 8.36, 4: 8.36}
 MALL_BYTES = 256 << 20
 QWEN_IN, QWEN_OUT = 5120, 17408
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_qwen_up_k2.json")
@@ -114,6 +120,9 @@ def gemv_bench(T, torch, dev, k, steps, warmup):
     warm = time_calls(torch, lambda i: launch(0), 1, max(steps // 4, 10), 5)
     res = {"us_per_call": ms * 1e3, "gbps": code_bytes / (ms * 1e-3) / 1e9,
            "frac_hbm": code_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "decode_w_per_clk_cu": shape.rows * shape.cols / (ms * 1e-3) / CUS / CLOCK_HZ,
+           "frac_decode_ceiling": shape.rows * shape.cols / (ms * 1e-3) / CUS / CLOCK_HZ
+                                  / GATHER_PEAK_W_PER_CLK[k],
            "code_bytes": code_bytes, "rotation_sets": len(sets.items),
            "us_per_call_mall_resident": warm * 1e3}
     first = sets.first
@@ -313,6 +322,10 @@ def main() -> int:
                      "traffic": traffic_entry(),
                      "kernel": "gemv_kernel<2>",
                      "bytes_per_launch": head["code_bytes"]},
+        "decode": {"bound": "lds_gather", "unit": "weights/clk/CU",
+                   "achieved": round(head["decode_w_per_clk_cu"], 3),
+                   "peak": GATHER_PEAK_W_PER_CLK[2],
+                   "frac": round(head["frac_decode_ceiling"], 4)},
         "cpu_baseline": cpu,
     }
     if extra is not None:
