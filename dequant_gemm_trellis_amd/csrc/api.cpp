@@ -5,7 +5,7 @@
 // Pages cited: diff views of "@mlx-bun/inference" 0.0.0-stage -> 1.0.0;
 // page 60 tiled-prefill.ts and wide-prefill.ts reject unsupported geometry
 // (T 256, L 12, k 2/3/4, cols a multiple of 256, row-contiguous layout)
-// before any launch; page 59 scatter.ts fixes 128 row splits.
+// before any launch.
 #include <math.h>
 #include <stdint.h>
 
@@ -52,17 +52,11 @@ int check_io(const void* x, const void* y) {
     return TRELLIS_OK;
 }
 
-// Row splits of the axis-0 kernel: 128 for the scatter GEMV (page 59
-// scatter.ts); for the prefill, 128 up to M = 16 and 64 above, which keeps the
-// float32 partial traffic near 10 MB at the 17408 x 5120 shape.
-int axis0_splits(int M, int op) {
-    if (op == TRELLIS_OP_GEMV_SCATTER) return TRELLIS_SCATTER_SPLITS;
-    return M > 16 ? 64 : 128;
-}
-
-size_t axis0_workspace(const Dims& d, int M, int op) {
-    return static_cast<size_t>(trellis::axis0_split_groups(axis0_splits(M, op))) *
-           static_cast<size_t>(M) * static_cast<size_t>(d.cols) * sizeof(float);
+// Axis-0 workspace: the float32 partials of the row ranges ("parts") the
+// kernel splits the contraction into, P * M * cols floats.
+size_t axis0_workspace(const Dims& d, int M) {
+    return static_cast<size_t>(trellis::axis0_parts(d.rows, d.cols)) * static_cast<size_t>(M) *
+           static_cast<size_t>(d.cols) * sizeof(float);
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? TRELLIS_OK : TRELLIS_ERR_HIP; }
@@ -113,9 +107,9 @@ int trellis_gemv_scatter(const uint16_t* x, const uint32_t* codes, const float* 
     if ((st = check_operands(codes, scales, lut)) || (st = check_io(x, y))) return st;
     if (!workspace) return TRELLIS_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return TRELLIS_ERR_ALIGN;
-    if (workspace_bytes < axis0_workspace(d, 1, TRELLIS_OP_GEMV_SCATTER)) return TRELLIS_ERR_WORKSPACE;
+    if (workspace_bytes < axis0_workspace(d, 1)) return TRELLIS_ERR_WORKSPACE;
     return status_of(trellis::launch_axis0(x, 1, codes, scales, lut, workspace, y, d.rows, d.cols,
-                                           axis0_splits(1, TRELLIS_OP_GEMV_SCATTER), g->k, stream));
+                                           g->k, stream));
 }
 
 int trellis_prefill(const uint16_t* x, int32_t M, const uint32_t* codes, const float* scales,
@@ -133,9 +127,9 @@ int trellis_prefill(const uint16_t* x, int32_t M, const uint32_t* codes, const f
         return status_of(trellis::launch_axis1(x, M, codes, scales, lut, y, d.rows, d.nb, g->k, stream));
     if (!workspace) return TRELLIS_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return TRELLIS_ERR_ALIGN;
-    if (workspace_bytes < axis0_workspace(d, M, TRELLIS_OP_PREFILL)) return TRELLIS_ERR_WORKSPACE;
+    if (workspace_bytes < axis0_workspace(d, M)) return TRELLIS_ERR_WORKSPACE;
     return status_of(trellis::launch_axis0(x, M, codes, scales, lut, workspace, y, d.rows, d.cols,
-                                           axis0_splits(M, TRELLIS_OP_PREFILL), g->k, stream));
+                                           g->k, stream));
 }
 
 size_t trellis_workspace_bytes(const trellis_geometry* g, int32_t M, int32_t op) {
@@ -145,10 +139,10 @@ size_t trellis_workspace_bytes(const trellis_geometry* g, int32_t M, int32_t op)
     case TRELLIS_OP_GEMV:
         return (g->axis == 1 && M == 1) ? 0 : static_cast<size_t>(-1);
     case TRELLIS_OP_GEMV_SCATTER:
-        return (g->axis == 0 && M == 1) ? axis0_workspace(d, 1, op) : static_cast<size_t>(-1);
+        return (g->axis == 0 && M == 1) ? axis0_workspace(d, 1) : static_cast<size_t>(-1);
     case TRELLIS_OP_PREFILL:
         if (M < 0 || M > TRELLIS_MAX_M) return static_cast<size_t>(-1);
-        return (g->axis == 1 || M == 0) ? 0 : axis0_workspace(d, M, op);
+        return (g->axis == 1 || M == 0) ? 0 : axis0_workspace(d, M);
     default:
         return static_cast<size_t>(-1);
     }

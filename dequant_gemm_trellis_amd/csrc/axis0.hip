@@ -1,78 +1,217 @@
 // Axis-0 trellis kernels for gfx950: split-K decode + bf16 MFMA partials and
-// the ordered split reduction. They serve the M = 1 "scatter" GEMV and the
-// axis-0 prefill.
+// the ordered reduction over the splits. They serve the M = 1 "scatter" GEMV
+// and the axis-0 prefill.
 //
 // Pages cited: diff views of "@mlx-bun/inference" 0.0.0-stage -> 1.0.0,
-// page 59: scatter.ts (axis-0 GEMV: 128 row splits of ceil(rows/128) rows,
-// float32 partials [M][128][cols], then a sum over the split axis and a cast)
-// and splitk-prefill.ts (axis-0 prefill: split-K float32 partials and an
-// ordered accumulate kernel).
+// page 59: scatter.ts (axis-0 GEMV: the stored rows split into ranges, one
+// float32 partial per range and output column, then a sum over the ranges and
+// a cast) and splitk-prefill.ts (axis-0 prefill: split-K float32 partials and
+// an ordered accumulate kernel).
 //
 // On axis 0 the contraction runs over stored rows r, and the MFMA B fragment
 // of a lane holds 8 consecutive contraction indices of one output column. So
 // a lane decodes an 8 x 8 patch: 8 stored rows x 8 adjacent columns. For each
 // row it loads the two words that hold the 8 windows (always enough: at most
 // 7k + 12 bits starting anywhere inside a word), funnels them to a 64-bit
-// value, and reads the windows at compile-time offsets. Column e of the patch
-// over the 8 rows is the B fragment of MFMA number e, whose accumulator
-// collects output column 8j + e. The A fragment is x[m][the same 8 rows].
+// value, and reads the windows at compile-time offsets (for k = 2 as four
+// adjacent-column pairs from the pair table). Column e of the patch over the 8
+// rows is the B fragment of MFMA number e, whose accumulator collects output
+// column 8j + e. The A fragment is x[m][the same 8 rows].
 //
-// Mapping: a wave owns 128 output columns (lane j = l % 16 -> columns
-// 8j..8j+7, row chunk c = l / 16 -> rows 8c..8c+7 of each 32-row step) and one
-// split of rows. A workgroup holds the 4 consecutive splits of one column
-// tile; their partials are summed in LDS in wave order, then written as one
-// partial per split group. The reduce kernel sums split groups in ascending
-// order. Every order is fixed, so repeated calls give identical bits.
+// Mapping: a workgroup of 8 waves owns one 128-column tile and one of P
+// contiguous row ranges of it ("parts"; P = 256 / tiles, at least 1, a fixed
+// count so that results do not depend on the device). Each wave takes a
+// contiguous share of the part's 32-row steps (lane j = l % 16 -> columns
+// 8j..8j+7, c = l / 16 -> rows 8c..8c+7 of a step) and accumulates in
+// registers; the waves' tiles are summed in LDS in wave order, one partial per
+// part, and the reduce kernel sums the parts in a fixed order. Every order is
+// fixed, so repeated calls give identical bits.
+//
+// The codebook (or pair table) is staged once per workgroup, and the next
+// step's words, scales and activations are in flight in registers while one
+// step is decoded (the first-generation kernel, one wave per split, four per
+// workgroup, restaged the codebook in 1280 workgroups and waited on every
+// step's loads).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace trellis {
 namespace {
 
-constexpr int kThreads = 256;  // split reduce
+constexpr int kThreads = 256;       // split reduce
 constexpr int kTileCols = 128;
-// Splits per workgroup, one wave each; their partials are summed in LDS in
-// wave order. (8 or 16 per workgroup measured 15% and 3x slower.)
-constexpr int kA0Waves = 4;
-constexpr int kA0Threads = kA0Waves * kWave;
+constexpr int kA0Threads = 512;     // 8 waves, two per SIMD
+constexpr int kA0Waves = kA0Threads / kWave;
+constexpr int kA0TargetGroups = 256;  // tiles x parts is about this
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     floatx2 p = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
 }
 
-template <int K, int MT>
+template <int K>
+struct A0Lds {
+    static constexpr bool pair = K == 2;
+    static constexpr int tab_floats = pair ? 2 * kPairEntries : kLutEntries;
+    static constexpr int red_floats = kA0Waves * 16 * kTileCols;  // one M tile of wave partials
+    static constexpr int floats = tab_floats > red_floats ? tab_floats : red_floats;
+};
+
+// One 32-row step of a lane: the raw words w0, w1 of its 8 rows (the funnel
+// shift waits until decode, so the loads can be in flight meanwhile), the
+// rows' scales, and its A fragment per M tile.
+template <int MT>
+struct A0Step {
+    uint32_t a[8], b[8];
+    float sc[8];
+    u32x4 x[MT];
+    int rc;  // first row of the lane's 8-row chunk
+};
+
+struct A0Ctx {
+    const uint32_t* cbase;  // word 0 of the tile's block in stored row 0
+    const float* scales;
+    const uint16_t* xr[2];  // A rows m = j and 16 + j (rows past M read row 0)
+    size_t row_words;
+    int w0, w1, R, c;
+};
+
+// Issue step s's loads; every address is valid whatever s is (rows clamp to
+// the last stored row), so the loads are unconditional. With VEC (R % 8 == 0)
+// a lane's 8 rows are all stored rows or all past the end and its A fragment
+// is one aligned 16-byte load; otherwise x is read element by element with
+// the row count applied.
+template <int MT, bool VEC>
+__device__ __forceinline__ void a0_load(A0Step<MT>& st, const A0Ctx& cx, int s) {
+    const int rc = 32 * s + 8 * cx.c;
+    st.rc = rc;
+    static_for<0, 8>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const int r = rc + i < cx.R ? rc + i : cx.R - 1;
+        const uint32_t* p = cx.cbase + static_cast<size_t>(r) * cx.row_words;
+        st.a[i] = p[cx.w0];
+        st.b[i] = p[cx.w1];
+        st.sc[i] = cx.scales[r];
+    });
+    static_for<0, MT>([&](auto mc) {
+        constexpr int mt = decltype(mc)::value;
+        if constexpr (VEC) {
+            const int rx = rc < cx.R ? rc : cx.R - 8;
+            st.x[mt] = *reinterpret_cast<const u32x4*>(cx.xr[mt] + rx);
+        } else {
+            const uint16_t* xp = cx.xr[mt] + rc;
+            static_for<0, 4>([&](auto dc) {
+                constexpr int d = decltype(dc)::value;
+                const uint32_t lo16 = rc + 2 * d < cx.R ? xp[2 * d] : 0u;
+                const uint32_t hi16 = rc + 2 * d + 1 < cx.R ? xp[2 * d + 1] : 0u;
+                st.x[mt][d] = lo16 | (hi16 << 16);
+            });
+        }
+    });
+}
+
+// Decode a step's 8 x 8 patch and multiply, column by column (k = 3, 4) or
+// column pair by column pair (k = 2), the next column's gathers in flight
+// while one is packed and multiplied.
+template <int K, int MT, bool VEC>
+__device__ __forceinline__ void a0_decode(const A0Step<MT>& st, const A0Ctx& cx, int sh,
+                                          const float* __restrict__ tab, floatx4 (&acc)[8][MT]) {
+    uint32_t g[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        g[i][0] = __builtin_amdgcn_alignbit(st.b[i], st.a[i], sh);
+        g[i][1] = st.b[i] >> sh;
+    }
+    bf16x8 afrag[MT];
+    const bool live = !VEC || st.rc < cx.R;  // VEC: a chunk past the end contributes nothing
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+        afrag[mt] = as_bf16x8(live ? st.x[mt] : u32x4{0u, 0u, 0u, 0u});
+    if constexpr (A0Lds<K>::pair) {
+        // columns 2p (earlier weight) and 2p + 1: the pair field starts at the
+        // later weight, (6 - 2p) k bits above the lane's lowest window
+        auto gather = [&](auto pc, floatx2 (&v)[8]) {
+            constexpr int O = (6 - 2 * decltype(pc)::value) * K;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = lds_pair(tab, field_offset<O, 14, 3>(g[i]));
+        };
+        floatx2 va[8], vb[8];
+        gather(std::integral_constant<int, 0>{}, va);
+        static_for<0, 4>([&](auto pc) {
+            constexpr int p = decltype(pc)::value;
+            floatx2 (&cur)[8] = (p & 1) ? vb : va;
+            floatx2 (&nxt)[8] = (p & 1) ? va : vb;
+            if constexpr (p + 1 < 4) gather(std::integral_constant<int, p + 1>{}, nxt);
+            u32x4 b0, b1;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                b0[d] = pack2(cur[2 * d].x * st.sc[2 * d], cur[2 * d + 1].x * st.sc[2 * d + 1]);
+                b1[d] = pack2(cur[2 * d].y * st.sc[2 * d], cur[2 * d + 1].y * st.sc[2 * d + 1]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                acc[2 * p][mt] = mfma16x16x32(afrag[mt], as_bf16x8(b0), acc[2 * p][mt]);
+                acc[2 * p + 1][mt] = mfma16x16x32(afrag[mt], as_bf16x8(b1), acc[2 * p + 1][mt]);
+            }
+        });
+    } else {
+        // weight t0 + e starts (7 - e) k bits above the lane's lowest window
+        auto gather = [&](auto ec, float (&v)[8]) {
+            constexpr int o = (7 - decltype(ec)::value) * K;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = lds_lut(tab, lut_byte_offset<o>(g[i]));
+        };
+        float va[8], vb[8];
+        gather(std::integral_constant<int, 0>{}, va);
+        static_for<0, 8>([&](auto ec) {
+            constexpr int e = decltype(ec)::value;
+            float (&cur)[8] = (e & 1) ? vb : va;
+            float (&nxt)[8] = (e & 1) ? va : vb;
+            if constexpr (e + 1 < 8) gather(std::integral_constant<int, e + 1>{}, nxt);
+            u32x4 bq;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                bq[d] = pack2(cur[2 * d] * st.sc[2 * d], cur[2 * d + 1] * st.sc[2 * d + 1]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[e][mt] = mfma16x16x32(afrag[mt], as_bf16x8(bq), acc[e][mt]);
+        });
+    }
+}
+
+template <int K, int MT, bool VEC>
 __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
     const float* __restrict__ scales, const float* __restrict__ lut,
-    float* __restrict__ partial, int R, int C, int M, int S, int rows_per_split) {
+    float* __restrict__ partial, int R, int C, int M, int P) {
     constexpr int wpb = Bits<K>::wpb;
-    __shared__ __attribute__((aligned(16))) float lut_s[kLutEntries];
-    __shared__ float red[8][MT * 16][16];
+    constexpr bool kPair = A0Lds<K>::pair;
+    __shared__ __attribute__((aligned(16))) float lds[A0Lds<K>::floats];
+    float* const tab = lds;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, c = lane >> 4;
-    const int groups = (S + kA0Waves - 1) / kA0Waves;
-    const int tile = blockIdx.x / groups;
-    const int sgroup = blockIdx.x - tile * groups;
-    const int split = sgroup * kA0Waves + wave;
+    const int tile = blockIdx.x / P;
+    const int part = blockIdx.x - tile * P;
     const int col0 = tile * kTileCols;
     const int blk = col0 / kT;
     const int t0 = (col0 % kT) + 8 * j;         // first weight of this lane's 8 columns
     const int lo = (kT - 8 - t0) * K;           // bit of weight t0 + 7
     const int w0 = lo >> 5, sh = lo & 31;
     const int w1 = (w0 + 1 == wpb) ? 0 : w0 + 1;  // tail-biting wrap to word 0
-    const size_t row_words = static_cast<size_t>(C) / kT * wpb;
-    const uint32_t* __restrict__ cbase = codes + static_cast<size_t>(blk) * wpb;
 
-    int r_begin = split * rows_per_split;
-    int r_end = r_begin + rows_per_split;
-    if (split >= S) r_begin = r_end = 0;
-    if (r_end > R) r_end = R;
-    if (r_begin > r_end) r_begin = r_end;
+    // This part's 32-row steps, and this wave's contiguous share of them.
+    const int RS = (R + 31) / 32;
+    const int p0 = static_cast<int>(static_cast<long>(part) * RS / P);
+    const int p1 = static_cast<int>(static_cast<long>(part + 1) * RS / P);
+    const int s0 = p0 + wave * (p1 - p0) / kA0Waves;
+    const int s1 = p0 + (wave + 1) * (p1 - p0) / kA0Waves;
 
-    stage_lut<kA0Threads>(lut_s, lut);
-    __syncthreads();
+    A0Ctx cx{codes + static_cast<size_t>(blk) * wpb, scales,
+             {x + static_cast<size_t>(j < M ? j : 0) * R, x + static_cast<size_t>(16 + j < M ? 16 + j : 0) * R},
+             static_cast<size_t>(C) / kT * wpb, w0, w1, R, c};
 
     floatx4 acc[8][MT];
 #pragma unroll
@@ -80,87 +219,56 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[e][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // A-fragment rows m = 16 mt + j; rows at or past M read row 0 (their D
-    // rows are never stored). Contraction rows past the split end are real
-    // terms and are zeroed in x.
-    const uint16_t* __restrict__ xr0 = x + static_cast<size_t>(j < M ? j : 0) * R;
-    const uint16_t* __restrict__ xr1 = x + static_cast<size_t>(16 + j < M ? 16 + j : 0) * R;
+    // The table sources first, then the first step's loads (unconditional; a
+    // wave without steps reads a valid clamped step), so the table stores do
+    // not wait for them.
+    TableSrc<kA0Threads, kPair> tsrc;
+    fetch_table<kA0Threads, kPair>(tsrc, lut);
+    asm volatile("" ::: "memory");
+    A0Step<MT> sa, sb;
+    a0_load<MT, VEC>(sa, cx, s0);
+    store_table<kA0Threads, kPair>(tsrc, tab);
+    __syncthreads();
 
-    for (int rs = r_begin; rs < r_end; rs += 32) {
-        const int rc = rs + 8 * c;  // first row of this lane's chunk
-        uint32_t g[8][2];
-        float sc[8];
-        static_for<0, 8>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            const int r = rc + i < r_end ? rc + i : r_end - 1;  // masked rows: valid address
-            const uint32_t* p = cbase + static_cast<size_t>(r) * row_words;
-            const uint32_t a = p[w0], bw = p[w1];
-            g[i][0] = __builtin_amdgcn_alignbit(bw, a, sh);
-            g[i][1] = bw >> sh;
-            sc[i] = scales[r];
-        });
-        bf16x8 afrag[MT];
-        static_for<0, MT>([&](auto mc) {
-            constexpr int mt = decltype(mc)::value;
-            const uint16_t* xp = (mt == 0 ? xr0 : xr1) + rc;
-            u32x4 a;
-            if (rc + 8 <= r_end && ((reinterpret_cast<uintptr_t>(xp) & 15) == 0)) {
-                a = *reinterpret_cast<const u32x4*>(xp);
-            } else {
-                static_for<0, 4>([&](auto dc) {
-                    constexpr int d = decltype(dc)::value;
-                    const uint32_t lo16 = rc + 2 * d < r_end ? xp[2 * d] : 0u;
-                    const uint32_t hi16 = rc + 2 * d + 1 < r_end ? xp[2 * d + 1] : 0u;
-                    a[d] = lo16 | (hi16 << 16);
-                });
-            }
-            afrag[mt] = as_bf16x8(a);
-        });
-        static_for<0, 8>([&](auto ec) {
-            // weight t0 + e starts (7 - e) * k bits above `lo`
-            constexpr int e = decltype(ec)::value;
-            constexpr int o = (7 - e) * K;
-            u32x4 bq;
-            static_for<0, 4>([&](auto dc) {
-                constexpr int d = decltype(dc)::value;
-                const float v0 = lds_lut(lut_s, lut_byte_offset<o>(g[2 * d]));
-                const float v1 = lds_lut(lut_s, lut_byte_offset<o>(g[2 * d + 1]));
-                bq[d] = pack2(v0 * sc[2 * d], v1 * sc[2 * d + 1]);
-            });
-            const bf16x8 bfrag = as_bf16x8(bq);
-            static_for<0, MT>([&](auto mc) {
-                constexpr int mt = decltype(mc)::value;
-                acc[e][mt] = mfma16x16x32(afrag[mt], bfrag, acc[e][mt]);
-            });
-        });
+    // Two register sets alternate: the next step's loads are in flight while
+    // one is decoded. Inside the loop every load feeds an unconditional decode
+    // (a load used only under a branch gets sunk into it, behind the waits);
+    // an odd last step is decoded after the loop.
+    int s = s0;
+    for (; s + 1 < s1; s += 2) {
+        a0_load<MT, VEC>(sb, cx, s + 1);
+        a0_decode<K, MT, VEC>(sa, cx, sh, tab, acc);
+        a0_load<MT, VEC>(sa, cx, s + 2);
+        a0_decode<K, MT, VEC>(sb, cx, sh, tab, acc);
     }
+    if (s < s1) a0_decode<K, MT, VEC>(sa, cx, sh, tab, acc);
+    __syncthreads();  // the table is dead from here on; its space takes the wave partials
 
-    // Sum the waves' tiles in wave order through LDS; the last wave stores.
-    // D layout: lane holds D[m = 4c + v][n = j] of each 16x16 tile.
-    for (int w = 0; w < kA0Waves; ++w) {
-        if (wave == w) {
+    // Sum the waves' tiles in wave order, one M tile at a time.
+    // D layout: lane holds D[m = 4c + v][n = j] of the tile of column 8j + e.
+    float* const red = lds;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+        for (int e = 0; e < 8; ++e)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int m = mt * 16 + 4 * c + v;
-                        const float prev = w == 0 ? 0.f : red[e][m][j];
-                        const float sum = w == 0 ? acc[e][mt][v] : prev + acc[e][mt][v];
-                        if (w < kA0Waves - 1) {
-                            red[e][m][j] = sum;
-                        } else if (m < M) {
-                            partial[(static_cast<size_t>(sgroup) * M + m) * C + col0 + 8 * j + e] = sum;
-                        }
-                    }
+            for (int v = 0; v < 4; ++v)
+                red[(wave * 16 + 4 * c + v) * kTileCols + 8 * j + e] = acc[e][mt][v];
+        __syncthreads();
+        for (int idx = tid; idx < 16 * kTileCols; idx += kA0Threads) {
+            const int m = idx / kTileCols, col = idx % kTileCols;
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < kA0Waves; ++w) sum += red[(w * 16 + m) * kTileCols + col];
+            const int mm = 16 * mt + m;
+            if (mm < M) partial[(static_cast<size_t>(part) * M + mm) * C + col0 + col] = sum;
         }
         __syncthreads();
     }
 }
 
-// y[i] = bf16( sum over split groups g ascending of partial[g][i] ), i < M*C.
-// Four waves each sum a contiguous quarter of the groups; the quarters are
+// y[i] = bf16( sum over parts g ascending of partial[g][i] ), i < M*C.
+// Four waves each sum a contiguous quarter of the parts; the quarters are
 // then added in order.
 __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
     const float* __restrict__ partial, uint16_t* __restrict__ y, int MC, int G) {
@@ -194,39 +302,50 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
     if (q == 0 && i < MC) y[i] = round_bf16(((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
 }
 
-template <int K, int MT>
+template <int K, int MT, bool VEC>
 hipError_t launch_axis0_k(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
-                          const float* lut, float* partial, int R, int C, int S,
-                          hipStream_t st) {
-    const int rows_per_split = (R + S - 1) / S;
-    const int groups = axis0_split_groups(S);
-    const dim3 grid(static_cast<unsigned>((C / kTileCols) * groups));
-    return launch_kernel(axis0_mma_kernel<K, MT>, grid, dim3(kA0Threads), st, x, codes, scales, lut,
-                         partial, R, C, M, S, rows_per_split);
+                          const float* lut, float* partial, int R, int C, int P, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>((C / kTileCols) * P));
+    return launch_kernel(axis0_mma_kernel<K, MT, VEC>, grid, dim3(kA0Threads), st, x, codes, scales,
+                         lut, partial, R, C, M, P);
+}
+
+template <int K, int MT>
+hipError_t launch_axis0_v(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
+                          const float* lut, float* partial, int R, int C, int P, hipStream_t st) {
+    if (R % 8 == 0)
+        return launch_axis0_k<K, MT, true>(x, M, codes, scales, lut, partial, R, C, P, st);
+    return launch_axis0_k<K, MT, false>(x, M, codes, scales, lut, partial, R, C, P, st);
 }
 
 }  // namespace
 
-int axis0_split_groups(int S) { return (S + kA0Waves - 1) / kA0Waves; }
+int axis0_parts(int R, int C) {
+    const int tiles = C / kTileCols, steps = (R + 31) / 32;
+    int P = kA0TargetGroups / tiles;
+    if (P > steps) P = steps;
+    return P > 1 ? P : 1;
+}
 
 hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
-                        const float* lut, float* partial, uint16_t* y, int R, int C, int S, int k,
+                        const float* lut, float* partial, uint16_t* y, int R, int C, int k,
                         hipStream_t st) {
     const bool two = M > 16;
+    const int P = axis0_parts(R, C);
     hipError_t e;
     switch (k) {
-    case 2: e = two ? launch_axis0_k<2, 2>(x, M, codes, scales, lut, partial, R, C, S, st)
-                    : launch_axis0_k<2, 1>(x, M, codes, scales, lut, partial, R, C, S, st); break;
-    case 3: e = two ? launch_axis0_k<3, 2>(x, M, codes, scales, lut, partial, R, C, S, st)
-                    : launch_axis0_k<3, 1>(x, M, codes, scales, lut, partial, R, C, S, st); break;
-    case 4: e = two ? launch_axis0_k<4, 2>(x, M, codes, scales, lut, partial, R, C, S, st)
-                    : launch_axis0_k<4, 1>(x, M, codes, scales, lut, partial, R, C, S, st); break;
+    case 2: e = two ? launch_axis0_v<2, 2>(x, M, codes, scales, lut, partial, R, C, P, st)
+                    : launch_axis0_v<2, 1>(x, M, codes, scales, lut, partial, R, C, P, st); break;
+    case 3: e = two ? launch_axis0_v<3, 2>(x, M, codes, scales, lut, partial, R, C, P, st)
+                    : launch_axis0_v<3, 1>(x, M, codes, scales, lut, partial, R, C, P, st); break;
+    case 4: e = two ? launch_axis0_v<4, 2>(x, M, codes, scales, lut, partial, R, C, P, st)
+                    : launch_axis0_v<4, 1>(x, M, codes, scales, lut, partial, R, C, P, st); break;
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
     const int MC = M * C;
     return launch_kernel(split_reduce_kernel, dim3((MC + 63) / 64), dim3(kThreads), st, partial, y,
-                         MC, axis0_split_groups(S));
+                         MC, P);
 }
 
 }  // namespace trellis

@@ -32,12 +32,12 @@ int gemv_max_blocks(int k);
 hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
                         const float* lut, uint16_t* y, int N, int nb, int k, hipStream_t st);
 
-// Axis 0, 1 <= M <= 32, S row splits: partials then the ordered reduce into
-// y[M][C]. `partial` holds axis0_split_groups(S) * M * C floats.
+// Axis 0, 1 <= M <= 32: per-part partials, then the ordered reduce over the
+// parts into y[M][C]. `partial` holds axis0_parts(R, C) * M * C floats.
 hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
-                        const float* lut, float* partial, uint16_t* y, int R, int C, int S, int k,
+                        const float* lut, float* partial, uint16_t* y, int R, int C, int k,
                         hipStream_t st);
-int axis0_split_groups(int S);
+int axis0_parts(int R, int C);
 
 // Decoded weights w[rows][nb*256].
 hipError_t launch_expand(const uint32_t* codes, const float* scales, const float* lut,

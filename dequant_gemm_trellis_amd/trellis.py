@@ -32,7 +32,6 @@ ERR_HIP = -6
 OP_GEMV = 0
 OP_GEMV_SCATTER = 1
 OP_PREFILL = 2
-SCATTER_SPLITS = 128
 MAX_M = 32
 
 # Every function trellis.h declares, for the export check.

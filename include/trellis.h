@@ -78,10 +78,6 @@ enum {
     TRELLIS_OP_PREFILL = 2
 };
 
-/* Number of row splits of the axis-0 scatter GEMV (page 59 scatter.ts uses
- * 128 split-K row ranges of ceil(rows/128) rows each). */
-#define TRELLIS_SCATTER_SPLITS 128
-
 /* Largest activation batch accepted by trellis_prefill (page 60
  * tiled-prefill.ts serves M = 5..32). */
 #define TRELLIS_MAX_M 32
@@ -110,15 +106,19 @@ int trellis_gemv(const uint16_t *x, const uint32_t *codes, const float *scales,
                  hipStream_t stream);
 
 /*
- * Axis-0 "scatter" GEMV, one activation row (page 59 scatter.ts):
- *   partial[s][n] = sum over stored rows r in split s of x[r] * W[r][n]
- *   y[n]          = bf16( sum_{s=0..127} partial[s][n] ),  s ascending.
- * Split s covers rows [s*R', min(in, (s+1)*R')) with R' = ceil(in/128).
+ * Axis-0 "scatter" GEMV, one activation row (page 59 scatter.ts: split-K over
+ * the stored rows, float32 partials per row range, then their sum and a cast):
+ *   partial[s][n] = sum over stored rows r in range s of x[r] * W[r][n]
+ *   y[n]          = bf16( sum over s of partial[s][n] ).
+ * The stored rows of each 128-column tile are split into P contiguous ranges,
+ * P = max(1, min(ceil(in / 32), 256 / (out / 128))); every sum runs in a fixed
+ * order, so a geometry always gives the same bits. (The pages use 128 ranges;
+ * the count only changes the float32 summation order, which is free.)
  * x: bf16 [in]; codes: uint32 [in][out*k/32]; scales: float32 [in];
  * lut: float32 [4096]; y: bf16 [out]. g->axis must be 0.
  * workspace: float32 scratch of at least
- * trellis_workspace_bytes(g, 1, TRELLIS_OP_GEMV_SCATTER) bytes; its contents
- * on entry do not matter and are overwritten.
+ * trellis_workspace_bytes(g, 1, TRELLIS_OP_GEMV_SCATTER) bytes (P * out
+ * floats); its contents on entry do not matter and are overwritten.
  */
 int trellis_gemv_scatter(const uint16_t *x, const uint32_t *codes, const float *scales,
                          const float *lut, const trellis_geometry *g, float *workspace,

@@ -135,8 +135,13 @@ def test_prefill_validation(T):
 
 def test_workspace_bytes(T):
     g0 = geom(T, axis=0, i=17408, o=5120, k=3)
-    # 128 splits summed four at a time inside the kernel: 32 float32 partial rows
-    assert T.workspace_bytes(g0, 1, T.OP_GEMV_SCATTER) == 32 * 5120 * 4
+    # 40 tiles of 128 output columns, 256 / 40 = 6 row ranges each: 6 float32
+    # partial rows of 5120
+    assert T.workspace_bytes(g0, 1, T.OP_GEMV_SCATTER) == 6 * 5120 * 4
+    assert T.workspace_bytes(g0, 32, T.OP_PREFILL) == 6 * 32 * 5120 * 4
+    # 2 tiles: ranges capped by the 32-row steps (37 rows: 2 steps)
+    small = geom(T, axis=0, i=37, o=256, k=3)
+    assert T.workspace_bytes(small, 1, T.OP_GEMV_SCATTER) == 2 * 256 * 4
     assert T.workspace_bytes(geom(T), 1, T.OP_GEMV) == 0
     with pytest.raises(T.TrellisError):
         T.workspace_bytes(geom(T), 2, T.OP_GEMV)

@@ -210,8 +210,9 @@ def test_scatter_integer_codebook_bit_exact(gpu_lib):
 
 @pytest.mark.parametrize("M", [1, 3, 20])
 def test_axis0_fewer_rows_than_splits(gpu_lib, M):
-    """37 input rows over 128 (or 64) splits: one row per split, most splits
-    empty, and an odd row count (the element-wise activation path)."""
+    """37 input rows: two 32-row steps in two row ranges, so most waves of a
+    workgroup have no step, and an odd row count (the element-wise activation
+    path)."""
     T = gpu_lib
     k = 2 + M % 3
     shape = synth.Shape(0, 256, L, k, 37, 512)
