@@ -24,22 +24,31 @@
 // workgroup g owning rows [g N / G, (g+1) N / G), at most kGroups
 // 16-row groups. A task is one group x one 256-weight block; the workgroup's
 // tasks are numbered block-major (all groups of block 0, then block 1, ...)
-// and each wave takes a contiguous range of them. A wave thus meets only one
-// or two blocks and loads their activation fragments once, reusing them for
-// every group: fetched per task instead, those loads touch 16 rows x 4 runs =
-// 64 cache lines per instruction and, measured, dominate the kernel from
-// M = 16 up. Each wave keeps one accumulator tile per group; at the end the
-// per-wave tiles are summed in LDS in wave order (deterministic), reusing the
-// table's space. Lanes of rows past the workgroup's range decode all-zero
-// words, so their gathers all hit one LDS address.
+// and each wave takes a contiguous range of them. A wave thus meets only a
+// few blocks and loads their activation fragments once per block, reusing
+// them for every group. Each wave keeps one accumulator tile per group; at the
+// end the per-wave tiles are summed in LDS in wave order (deterministic),
+// reusing the table's space. Lanes of rows past the workgroup's range decode
+// all-zero words, so their gathers all hit one LDS address.
+//
+// Activation fragments reach the lanes one of two ways, chosen by M:
+//   - direct (M <= kDirectMaxM): each lane loads its own fragments from
+//     global memory in A layout, one block ahead of use. Lanes of rows
+//     m >= M read row M - 1, so an instruction touches only M x 4 distinct
+//     cache lines, and nothing goes through the LDS, which the codebook
+//     gathers keep busy;
+//   - staged (larger M): coalesced loads of 16 rows, transposed through a
+//     per-wave LDS slot when the block changes. Direct loads would touch 64
+//     lines per instruction there, which measured slower.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace trellis {
 namespace {
 
-constexpr int kThreads = 256;  // expand kernel
-constexpr int kGroups = 5;     // 16-row groups per prefill workgroup (80 rows)
+constexpr int kThreads = 256;    // expand kernel
+constexpr int kGroups = 5;       // 16-row groups per prefill workgroup (80 rows)
+constexpr int kDirectMaxM = 8;   // largest M whose activation fragments are loaded directly
 
 // Prefill workgroup size: 8 waves, two per SIMD. For one M tile this
 // measured 2-7% faster than 16 waves (less contention in the LDS queue); two
@@ -51,16 +60,17 @@ struct PrefillShape {
     static constexpr int waves = threads / kWave;
 };
 
-// Per-wave activation slot: `lines` 128-byte lines (8 chunks of 16 bytes) of
-// each of the 16 rows of each M tile. Beside the 128 KB pair table only one
-// line fits (2 KB per tile); beside the 16 KB codebook all four do.
-template <int K, int MT>
+// Per-wave activation slot (staged path only): `lines` 128-byte lines (8
+// chunks of 16 bytes) of each of the 16 rows of each M tile. Beside the 128 KB
+// pair table only one line fits (2 KB per tile); beside the 16 KB codebook all
+// four do.
+template <int K, int MT, bool DIRECT>
 struct PrefillLds {
     static constexpr bool pair = K == 2;
     static constexpr int tab_floats = pair ? 2 * kPairEntries : kLutEntries;
     static constexpr int waves = PrefillShape<MT>::waves;
     static constexpr int lines = pair ? 1 : 4;
-    static constexpr int slot_chunks = MT * lines * 16 * 8;
+    static constexpr int slot_chunks = DIRECT ? 0 : MT * lines * 16 * 8;
     static constexpr int decode_floats = tab_floats + waves * slot_chunks * 4;
     static constexpr int part_floats = waves * kGroups * 256;  // one M tile of wave partials
     static constexpr int floats = decode_floats > part_floats ? decode_floats : part_floats;
@@ -135,11 +145,39 @@ struct XFrags {
     u32x4 v[MT][8];
 };
 
-// Activation fragments of block b for a wave: A fragment S of lane (j, c) is
-// x[m = 16 mt + j][256 b + 64 c + 8 S .. + 8] (the weights 64 c + 8 S + e are
-// the ones that lane decodes), i.e. chunk S of 128-byte line c of the row's
-// block. Fetched directly, each instruction would touch 64 cache lines (16
-// rows x 4 lines), which measured as the dominant cost. Instead instruction
+// Direct path: activation fragments of block b in A layout. A fragment S of
+// lane (j, c) is x[m = 16 mt + j][256 b + 64 c + 8 S .. + 8] (the weights
+// 64 c + 8 S + e are the ones that lane decodes); xa[mt] points at row m (row
+// M - 1 for m >= M: row m of A only feeds row m of D, which is never stored
+// for m >= M), column 64 c.
+template <int MT>
+__device__ __forceinline__ void load_x_frags(XFrags<MT>& xn, const uint16_t* const (&xa)[MT], int b) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int S = 0; S < 8; ++S)
+            xn.v[mt][S] = *reinterpret_cast<const u32x4*>(xa[mt] + b * kT + 8 * S);
+}
+
+// The same through an opaque global-address-space pointer, for the prologue
+// (see load_task_opaque).
+template <int MT>
+__device__ __forceinline__ void load_x_frags_opaque(XFrags<MT>& xn, const uint16_t* const (&xa)[MT],
+                                                    int b) {
+    using gu32x4 = const __attribute__((address_space(1))) u32x4*;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        gu32x4 p = (gu32x4)(xa[mt] + b * kT);
+        asm volatile("" : "+v"(p));
+#pragma unroll
+        for (int S = 0; S < 8; ++S) xn.v[mt][S] = p[S];
+    }
+}
+
+// Staged path: activation fragments of block b for a wave, the same A layout
+// as load_x_frags, i.e. chunk S of 128-byte line c of the row's block. Fetched
+// directly, each instruction would touch 64 cache lines (16 rows x 4 lines),
+// which measured slower than staging from M = 16 up. Instead instruction
 // (c, h) reads line c of rows 8h .. 8h + 7 (8 lanes per line, coalesced) and
 // the lines pass through the wave's LDS slot to the lanes of group c: all
 // four at once when the slot holds them, else one at a time. Chunk S of row r
@@ -208,29 +246,47 @@ __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__
     }
 }
 
+// Where a wave's activation fragments come from (see the two paths above).
+template <int MT>
+struct XSource {
+    const uint16_t* xrows[MT][2];  // staged: coalesced row pointers
+    const uint16_t* xa[MT];        // direct: A-layout row pointers
+    u32x4* slot;                   // staged: this wave's LDS slot
+    int nb;
+};
+
 // One task: eight fragments, the gathers of the next two in flight while one is
 // packed and multiplied against the MT activation tiles. A new block first
-// refreshes the activation fragments: a rare path, and the only one whose
-// memory wait covers the prefetched code words.
-template <int K, int MT>
-__device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, int& xb, u32x4* __restrict__ slot,
-                                         const uint16_t* const (&xrows)[MT][2],
-                                         floatx4 (&acc)[kGroups][MT],
+// refreshes the activation fragments: on the direct path from xn, loaded one
+// block change earlier (or in the prologue), which then fetches the next
+// block's; on the staged path through the LDS slot, the one memory wait that
+// covers the prefetched code words.
+template <int K, int MT, bool DIRECT>
+__device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& xn, int& xb,
+                                         const XSource<MT>& xs, floatx4 (&acc)[kGroups][MT],
                                          const float* __restrict__ tab, int lane, int j, int c) {
-    constexpr bool P = PrefillLds<K, MT>::pair;
+    constexpr bool P = PrefillLds<K, MT, DIRECT>::pair;
     if (t.b != xb) {
         xb = t.b;
-        load_x_block<MT, PrefillLds<K, MT>::lines>(xf, slot, xrows, t.b, lane, j, c);
+        if constexpr (DIRECT) {
+            xf = xn;
+            load_x_frags<MT>(xn, xs.xa, t.b + 1 < xs.nb ? t.b + 1 : xs.nb - 1);
+        } else {
+            load_x_block<MT, PrefillLds<K, MT, DIRECT>::lines>(xf, xs.slot, xs.xrows, t.b, lane, j, c);
+        }
     }
     if (!t.valid) {
 #pragma unroll
         for (int i = 0; i < 2 * K; ++i) t.w[i] = 0u;
     }
     t.w[2 * K] = next_run_word(t.w[0]);
+    // The group's accumulators move in and out under uniform branches (the
+    // empty asm keeps each a branch: as selects they cost 36 VALU per task).
     floatx4 cur[MT];
     static_for<0, kGroups>([&](auto gc) {
         constexpr int G = decltype(gc)::value;
         if (t.g == G) {
+            asm volatile("");
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) cur[mt] = acc[G][mt];
         }
@@ -253,19 +309,21 @@ __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, int& xb, u32
     static_for<0, kGroups>([&](auto gc) {
         constexpr int G = decltype(gc)::value;
         if (t.g == G) {
+            asm volatile("");
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[G][mt] = cur[mt];
         }
     });
 }
 
-template <int K, int MT>
+template <int K, int MT, bool DIRECT>
 __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
     const float* __restrict__ scales, const float* __restrict__ lut,
     uint16_t* __restrict__ y, int N, int nb, int M) {
     constexpr int kThreadsP = PrefillShape<MT>::threads, kWaves = PrefillShape<MT>::waves;
-    __shared__ __attribute__((aligned(16))) float lds[PrefillLds<K, MT>::floats];
+    using Lds = PrefillLds<K, MT, DIRECT>;
+    __shared__ __attribute__((aligned(16))) float lds[Lds::floats];
     float* const tab = lds;
 
     const int G = gridDim.x, wg = blockIdx.x;
@@ -280,19 +338,24 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     const int tau1 = static_cast<int>(static_cast<long>(wave + 1) * tasks / kWaves);
     const long in = static_cast<long>(nb) * kT;
 
-    // Coalesced activation rows: half h of tile mt is rows 16 mt + 8 h + lane / 8,
-    // lane % 8 the 16-byte chunk within a line. A rows past M read row M - 1:
-    // row m of A only feeds row m of D, which is never stored for m >= M.
-    const uint16_t* xrows[MT][2];
+    // Staged path, coalesced activation rows: half h of tile mt is rows
+    // 16 mt + 8 h + lane / 8, lane % 8 the 16-byte chunk within a line. Direct
+    // path: lane (j, c) reads row 16 mt + j from column 64 c of each block.
+    // A rows past M read row M - 1: row m of A only feeds row m of D, which is
+    // never stored for m >= M.
+    XSource<MT> xs;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int m = 16 * mt + 8 * h + (lane >> 3);
-            xrows[mt][h] = x + (m < M ? m : M - 1) * in + 8 * (lane & 7);
+            xs.xrows[mt][h] = x + (m < M ? m : M - 1) * in + 8 * (lane & 7);
         }
-    u32x4* const slot = reinterpret_cast<u32x4*>(lds + PrefillLds<K, MT>::tab_floats) +
-                        wave * PrefillLds<K, MT>::slot_chunks;
+        const int m = 16 * mt + j;
+        xs.xa[mt] = x + (m < M ? m : M - 1) * in + 64 * c;
+    }
+    xs.slot = reinterpret_cast<u32x4*>(lds + Lds::tab_floats) + wave * Lds::slot_chunks;
+    xs.nb = nb;
 
     TaskCtx cx{codes, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp};
     floatx4 acc[kGroups][MT];
@@ -301,16 +364,19 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[g][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // Prologue: the codebook first, then the first two tasks' code words
+    // Prologue: the codebook first, then the first two tasks' code words and,
+    // on the direct path, the first block's activation fragments
     // (unconditionally: a wave without tasks re-reads a valid one, and a load
     // under a branch would make the table stores wait for the code words too).
-    constexpr bool kPair = PrefillLds<K, MT>::pair;
+    constexpr bool kPair = Lds::pair;
     TableSrc<kThreadsP, kPair> tsrc;
     fetch_table<kThreadsP, kPair>(tsrc, lut);
     asm volatile("" ::: "memory");
     Task<K> ta, tb, tc;
     load_task_opaque<K>(ta, cx, tau0, tau1 > 1 ? tau1 : 1);
     load_task_opaque<K>(tb, cx, tau0 + 1, tau1 > 1 ? tau1 : 1);
+    XFrags<MT> xn;
+    if constexpr (DIRECT) load_x_frags_opaque<MT>(xn, xs.xa, ta.b);
     asm volatile("" ::: "memory");
     store_table<kThreadsP, kPair>(tsrc, tab);
     __syncthreads();
@@ -319,14 +385,14 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     // flight while one is decoded. (No branch around the loop: the prologue's
     // loads would be sunk into it, behind the barrier.)
     XFrags<MT> xf;
-    int xb = -1;
+    int xb = -1;  // block whose fragments xf holds
     for (int t0 = tau0; t0 < tau1; t0 += 3) {
         load_task<K>(tc, cx, t0 + 2, tau1);
-        run_task<K, MT>(ta, xf, xb, slot, xrows, acc, tab, lane, j, c);
+        run_task<K, MT, DIRECT>(ta, xf, xn, xb, xs, acc, tab, lane, j, c);
         load_task<K>(ta, cx, t0 + 3, tau1);
-        if (t0 + 1 < tau1) run_task<K, MT>(tb, xf, xb, slot, xrows, acc, tab, lane, j, c);
+        if (t0 + 1 < tau1) run_task<K, MT, DIRECT>(tb, xf, xn, xb, xs, acc, tab, lane, j, c);
         load_task<K>(tb, cx, t0 + 4, tau1);
-        if (t0 + 2 < tau1) run_task<K, MT>(tc, xf, xb, slot, xrows, acc, tab, lane, j, c);
+        if (t0 + 2 < tau1) run_task<K, MT, DIRECT>(tc, xf, xn, xb, xs, acc, tab, lane, j, c);
     }
     __syncthreads();  // the table is dead from here on; its space takes the partials
 
@@ -377,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(
     });
 }
 
-template <int K, int MT>
+template <int K, int MT, bool DIRECT>
 hipError_t launch_axis1_k(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
                           const float* lut, uint16_t* y, int N, int nb, hipStream_t st) {
     // One workgroup per compute unit while that leaves at most kGroups groups
@@ -385,7 +451,7 @@ hipError_t launch_axis1_k(const uint16_t* x, int M, const uint32_t* codes, const
     const int groups = (N + 15) / 16;
     int G = groups < cu_count() ? groups : cu_count();
     if ((N + G - 1) / G > 16 * kGroups) G = (N + 16 * kGroups - 1) / (16 * kGroups);
-    return launch_kernel(axis1_prefill_kernel<K, MT>, dim3(G), dim3(PrefillShape<MT>::threads), st,
+    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT>, dim3(G), dim3(PrefillShape<MT>::threads), st,
                          x, codes, scales,
                          lut, y, N, nb, M);
 }
@@ -402,14 +468,19 @@ hipError_t launch_expand_k(const uint32_t* codes, const float* scales, const flo
 
 hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
                         const float* lut, uint16_t* y, int N, int nb, int k, hipStream_t st) {
-    const bool two = M > 16;
-    switch (k) {
-    case 2: return two ? launch_axis1_k<2, 2>(x, M, codes, scales, lut, y, N, nb, st)
-                       : launch_axis1_k<2, 1>(x, M, codes, scales, lut, y, N, nb, st);
-    case 3: return two ? launch_axis1_k<3, 2>(x, M, codes, scales, lut, y, N, nb, st)
-                       : launch_axis1_k<3, 1>(x, M, codes, scales, lut, y, N, nb, st);
-    case 4: return two ? launch_axis1_k<4, 2>(x, M, codes, scales, lut, y, N, nb, st)
-                       : launch_axis1_k<4, 1>(x, M, codes, scales, lut, y, N, nb, st);
+    // One M tile up to M = 16, two above; direct activation fragments up to
+    // kDirectMaxM.
+    const int shape = M > 16 ? 2 : M > kDirectMaxM ? 1 : 0;
+    switch (k * 4 + shape) {
+    case 8: return launch_axis1_k<2, 1, true>(x, M, codes, scales, lut, y, N, nb, st);
+    case 9: return launch_axis1_k<2, 1, false>(x, M, codes, scales, lut, y, N, nb, st);
+    case 10: return launch_axis1_k<2, 2, false>(x, M, codes, scales, lut, y, N, nb, st);
+    case 12: return launch_axis1_k<3, 1, true>(x, M, codes, scales, lut, y, N, nb, st);
+    case 13: return launch_axis1_k<3, 1, false>(x, M, codes, scales, lut, y, N, nb, st);
+    case 14: return launch_axis1_k<3, 2, false>(x, M, codes, scales, lut, y, N, nb, st);
+    case 16: return launch_axis1_k<4, 1, true>(x, M, codes, scales, lut, y, N, nb, st);
+    case 17: return launch_axis1_k<4, 1, false>(x, M, codes, scales, lut, y, N, nb, st);
+    case 18: return launch_axis1_k<4, 2, false>(x, M, codes, scales, lut, y, N, nb, st);
     default: return hipErrorInvalidValue;
     }
 }
