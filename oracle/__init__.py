@@ -40,12 +40,13 @@ _lib.oracle_weight.restype = C.c_uint16
 _lib.oracle_weight.argtypes = [C.c_float, C.c_float]
 _lib.oracle_expand.restype = C.c_int
 _lib.oracle_expand.argtypes = [_u32p, _f32p, _f32p, C.c_int, C.c_int, C.c_int, C.c_int,
-                               C.c_int, C.c_int, _u16p]
+                               C.c_int, C.c_int, C.c_int, _u16p]
 _lib.oracle_matmul_f64.restype = C.c_int
 _lib.oracle_matmul_f64.argtypes = [_u16p, C.c_int, _u16p, C.c_int, C.c_int, C.c_int, _f64p]
 _lib.oracle_fused_f64.restype = C.c_int
 _lib.oracle_fused_f64.argtypes = [_u16p, C.c_int, _u32p, _f32p, _f32p, C.c_int, C.c_int,
-                                  C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, _f64p]
+                                  C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+                                  C.c_int, _f64p]
 
 
 def _p(a: np.ndarray, t):
@@ -94,8 +95,9 @@ def windows_from_bits(block: np.ndarray, T: int, k: int, L: int) -> np.ndarray:
 
 
 def expand(codes: np.ndarray, scales: np.ndarray, lut: np.ndarray, axis: int, T: int, L: int,
-           k: int, in_features: int, out_features: int) -> np.ndarray:
-    """Decoded bf16 weights (uint16 bits), shape [rows, cols]."""
+           k: int, in_features: int, out_features: int, block_interleave: int = 0) -> np.ndarray:
+    """Decoded bf16 weights (uint16 bits), shape [rows, cols]; `codes` in the
+    layout `block_interleave` names (0 row-major, 2 block pairs)."""
     rows, cols = _dims(axis, in_features, out_features)
     codes = np.ascontiguousarray(codes, dtype=np.uint32)
     scales = np.ascontiguousarray(scales, dtype=np.float32)
@@ -103,7 +105,7 @@ def expand(codes: np.ndarray, scales: np.ndarray, lut: np.ndarray, axis: int, T:
     assert codes.size == rows * cols * k // 32 and scales.size == rows and lut.size == 1 << L
     W = np.empty((rows, cols), dtype=np.uint16)
     ok = _lib.oracle_expand(_p(codes, _u32p), _p(scales, _f32p), _p(lut, _f32p), axis, T, L, k,
-                            in_features, out_features, _p(W, _u16p))
+                            in_features, out_features, block_interleave, _p(W, _u16p))
     if not ok:
         raise ValueError("oracle_expand: unsupported geometry")
     return W
@@ -123,9 +125,10 @@ def matmul_f64(x: np.ndarray, W: np.ndarray, axis: int, in_features: int,
 
 def fused_f64(x: np.ndarray, codes: np.ndarray, scales: np.ndarray, lut: np.ndarray, axis: int,
               T: int, L: int, k: int, in_features: int, out_features: int,
-              n_begin: int = 0, n_end: int | None = None) -> np.ndarray:
+              n_begin: int = 0, n_end: int | None = None, block_interleave: int = 0) -> np.ndarray:
     """y (float64, [M, out_features]); only output columns [n_begin, n_end) are
-    computed, the others are left at zero."""
+    computed, the others are left at zero. `codes` in the layout
+    `block_interleave` names (0 row-major, 2 block pairs)."""
     if n_end is None:
         n_end = out_features
     x = np.ascontiguousarray(x, dtype=np.uint16)
@@ -136,7 +139,7 @@ def fused_f64(x: np.ndarray, codes: np.ndarray, scales: np.ndarray, lut: np.ndar
     y = np.zeros((M, out_features), dtype=np.float64)
     ok = _lib.oracle_fused_f64(_p(x, _u16p), M, _p(codes, _u32p), _p(scales, _f32p),
                                _p(lut, _f32p), axis, T, L, k, in_features, out_features,
-                               n_begin, n_end, _p(y, _f64p))
+                               block_interleave, n_begin, n_end, _p(y, _f64p))
     if not ok:
         raise ValueError("oracle_fused_f64: unsupported geometry")
     return y
@@ -145,3 +148,22 @@ def fused_f64(x: np.ndarray, codes: np.ndarray, scales: np.ndarray, lut: np.ndar
 def bf16_bits_to_f64(h: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns exactly (a bit shift, no rounding)."""
     return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def interleave_blocks(codes: np.ndarray, rows: int, nb: int, wpb: int) -> np.ndarray:
+    """Row-major codes [rows][nb][wpb] rewritten in the block-interleave-2
+    order: block pairs outermost, then rows, then the pair's two blocks
+    ([P60] vector-expand.ts and [P59] scatter.ts address a block so when
+    INTERLEAVE is set). A reshape and a transpose; nb must be even."""
+    if nb % 2:
+        raise ValueError("block interleave 2 needs an even number of blocks per row")
+    a = np.asarray(codes, dtype=np.uint32).reshape(rows, nb // 2, 2, wpb)
+    return np.ascontiguousarray(a.transpose(1, 0, 2, 3)).reshape(-1)
+
+
+def deinterleave_blocks(codes: np.ndarray, rows: int, nb: int, wpb: int) -> np.ndarray:
+    """Inverse of interleave_blocks."""
+    if nb % 2:
+        raise ValueError("block interleave 2 needs an even number of blocks per row")
+    a = np.asarray(codes, dtype=np.uint32).reshape(nb // 2, rows, 2, wpb)
+    return np.ascontiguousarray(a.transpose(1, 0, 2, 3)).reshape(-1)

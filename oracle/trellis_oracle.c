@@ -33,7 +33,14 @@
  *     the activation type; [P59] scatter.ts rounds value*scale before the
  *     multiply-add);
  *   - on axis 0 the scale belongs to the stored row, i.e. the input index
- *     ([P59] scatter.ts reads scales[r] inside its row loop).
+ *     ([P59] scatter.ts reads scales[r] inside its row loop);
+ *   - the code array is row-major [rows][cols/T][T*k/32] (block interleave
+ *     0), or, with block interleave 2, pairs of blocks outermost: the words
+ *     of block b of row r start at (b/2)*rows*2*wpb + r*2*wpb + (b%2)*wpb
+ *     ([P60] vector-expand.ts and [P59] scatter.ts, splitk-prefill.ts
+ *     address a block this way when their INTERLEAVE constant is set). The
+ *     pages give no layout for an odd block count under interleave 2, so it
+ *     is rejected.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -70,6 +77,16 @@ static int oracle_dims(int axis, int in_features, int out_features, int *rows, i
     if (axis == 1) { *rows = out_features; *cols = in_features; return 1; }
     if (axis == 0) { *rows = in_features; *cols = out_features; return 1; }
     return 0;
+}
+
+/* Word offset of block b of stored row r in the code array, for block
+ * interleave 0 or 2 (see the header). Returns -1 for any other layout, or for
+ * interleave 2 with an odd block count. */
+static long oracle_block_word(long r, long b, long rows, long nb, long wpb, int interleave)
+{
+    if (interleave == 0) return (r * nb + b) * wpb;
+    if (interleave == 2 && nb % 2 == 0) return (b / 2) * rows * 2 * wpb + r * 2 * wpb + (b % 2) * wpb;
+    return -1;
 }
 
 /* Bit i of a block's bitstring, i in [0, T*k): bit (i mod 32) of word i/32. */
@@ -118,21 +135,23 @@ uint16_t oracle_weight(float value, float scale)
 }
 
 /* Expand the whole stored matrix to bf16 W[rows][cols] ([P60]
- * vector-expand.ts computes the same matrix). Returns 0 on bad geometry. */
+ * vector-expand.ts computes the same matrix). `interleave` is the code
+ * array's block interleave (0 or 2). Returns 0 on bad geometry. */
 int oracle_expand(const uint32_t *codes, const float *scales, const float *lut,
                   int axis, int T, int L, int k, int in_features, int out_features,
-                  uint16_t *W)
+                  int interleave, uint16_t *W)
 {
     int rows, cols;
     if (!oracle_dims(axis, in_features, out_features, &rows, &cols)) return 0;
     if (T <= 0 || k <= 0 || cols % T != 0 || ((long)T * k) % 32 != 0) return 0;
     const int nb = cols / T;
     const int wpb = T * k / 32;
+    if (oracle_block_word(0, 0, rows, nb, wpb, interleave) < 0) return 0;
     uint8_t *bits = (uint8_t *)malloc((size_t)T * k);
     if (!bits) return 0;
     for (long r = 0; r < rows; ++r) {
         for (int b = 0; b < nb; ++b) {
-            oracle_block_bits(codes + ((size_t)r * nb + b) * wpb, T, k, bits);
+            oracle_block_bits(codes + oracle_block_word(r, b, rows, nb, wpb, interleave), T, k, bits);
             for (int t = 0; t < T; ++t) {
                 uint32_t win = oracle_window_from_bits(bits, T, k, L, t);
                 W[(size_t)r * cols + (size_t)b * T + t] = oracle_weight(lut[win], scales[r]);
@@ -166,10 +185,12 @@ int oracle_matmul_f64(const uint16_t *x, int M, const uint16_t *W,
 /* Fused form: each weight is decoded from the words inside the contraction
  * loop (no materialised W). Same products and the same summation order as
  * oracle_expand followed by oracle_matmul_f64. Rows [n_begin, n_end) of the
- * output (all M of them) are computed; pass 0, out_features for all. */
+ * output (all M of them) are computed; pass 0, out_features for all.
+ * `interleave` is the code array's block interleave (0 or 2). */
 int oracle_fused_f64(const uint16_t *x, int M, const uint32_t *codes, const float *scales,
                      const float *lut, int axis, int T, int L, int k,
-                     int in_features, int out_features, int n_begin, int n_end, double *y)
+                     int in_features, int out_features, int interleave,
+                     int n_begin, int n_end, double *y)
 {
     int rows, cols;
     if (!oracle_dims(axis, in_features, out_features, &rows, &cols)) return 0;
@@ -177,13 +198,14 @@ int oracle_fused_f64(const uint16_t *x, int M, const uint32_t *codes, const floa
     if (M < 1 || M > 64) return 0;
     const int nb = cols / T;
     const int wpb = T * k / 32;
+    if (oracle_block_word(0, 0, rows, nb, wpb, interleave) < 0) return 0;
     double acc[64];
     for (long n = n_begin; n < n_end; ++n) {
         for (int m = 0; m < M; ++m) acc[m] = 0.0;
         for (long kk = 0; kk < in_features; ++kk) {
             long r = axis == 1 ? n : kk;   /* stored row */
             long c = axis == 1 ? kk : n;   /* stored column */
-            const uint32_t *block = codes + ((size_t)r * nb + c / T) * wpb;
+            const uint32_t *block = codes + oracle_block_word(r, c / T, rows, nb, wpb, interleave);
             uint32_t win = oracle_window(block, T, k, L, (int)(c % T));
             double w = oracle_bf16_to_f64(oracle_weight(lut[win], scales[r]));
             for (int m = 0; m < M; ++m)

@@ -359,3 +359,82 @@ def test_fused_equals_expand_then_matmul_bitwise(axis, M):
                           shape.out_features, 7, 40)
     assert np.array_equal(y3[:, 7:40], y1[:, 7:40])
     assert not np.any(y3[:, :7]) and not np.any(y3[:, 40:])
+
+
+# ------------------------------------------------------ block interleave 2
+def test_interleave_layout_brute_force():
+    """Block interleave 2 ([P60] vector-expand.ts, [P59] scatter.ts when
+    INTERLEAVE is set): block pairs outermost, then stored rows, then the
+    pair's two blocks, then the words of a block. Words are labelled with
+    their (row, block, word) and the rewritten array is compared with that
+    order written out as nested loops."""
+    rows, nb, wpb = 3, 4, 2
+    label = lambda r, b, w: 1000 * r + 10 * b + w
+    codes = np.array([label(r, b, w) for r in range(rows) for b in range(nb) for w in range(wpb)],
+                     dtype=np.uint32)
+    expect = []
+    for pair in range(nb // 2):
+        for r in range(rows):
+            for half in range(2):
+                for w in range(wpb):
+                    expect.append(label(r, 2 * pair + half, w))
+    il = oracle.interleave_blocks(codes, rows, nb, wpb)
+    assert il.tolist() == expect
+    assert np.array_equal(oracle.deinterleave_blocks(il, rows, nb, wpb), codes)
+    with pytest.raises(ValueError):
+        oracle.interleave_blocks(codes[: rows * 3 * wpb], rows, 3, wpb)
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_expand_reads_the_interleaved_layout(axis, k):
+    """The oracle's block addressing under interleave 2 (its offset formula)
+    against the layout produced by a reshape and transpose: the decoded
+    matrix must not depend on the layout."""
+    T = 256
+    rows, cols = 5, 4 * T
+    shape = synth.Shape(axis, T, L, k, cols if axis == 1 else rows, rows if axis == 1 else cols)
+    p = synth.make_problem(shape, 1, synth.CONFIG_IDS["test"], proj=23)
+    W0 = oracle.expand(p.codes, p.scales, p.lut, axis, T, L, k, shape.in_features,
+                       shape.out_features)
+    c2 = oracle.interleave_blocks(p.codes, rows, cols // T, T * k // 32)
+    assert not np.array_equal(c2, p.codes.ravel())
+    W2 = oracle.expand(c2, p.scales, p.lut, axis, T, L, k, shape.in_features,
+                       shape.out_features, block_interleave=2)
+    assert np.array_equal(W0, W2)
+    # brute force on the rewritten array: each block decoded through the
+    # closed-form windows at the position the nested-loop order puts it
+    wpb = T * k // 32
+    for r in range(rows):
+        for b in range(cols // T):
+            off = ((b // 2) * rows * 2 + r * 2 + b % 2) * wpb
+            win = rot_windows(c2[off:off + wpb], T, k)
+            vals = np.array([oracle.weight(float(p.lut[w]), float(p.scales[r])) for w in win],
+                            dtype=np.uint16)
+            assert np.array_equal(W2[r, b * T:(b + 1) * T], vals)
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_fused_reads_the_interleaved_layout(axis):
+    T, k, M = 256, 3, 2
+    rows, cols = 6, 2 * T
+    shape = synth.Shape(axis, T, L, k, cols if axis == 1 else rows, rows if axis == 1 else cols)
+    p = synth.make_problem(shape, M, synth.CONFIG_IDS["test"], proj=29)
+    y0 = oracle.fused_f64(p.x, p.codes, p.scales, p.lut, axis, T, L, k, shape.in_features,
+                          shape.out_features)
+    c2 = oracle.interleave_blocks(p.codes, rows, cols // T, T * k // 32)
+    y2 = oracle.fused_f64(p.x, c2, p.scales, p.lut, axis, T, L, k, shape.in_features,
+                          shape.out_features, block_interleave=2)
+    assert np.array_equal(y0.view(np.uint64), y2.view(np.uint64))
+
+
+def test_interleave_needs_an_even_block_count():
+    T, k = 256, 2
+    codes = np.zeros(2 * 3 * T * k // 32, dtype=np.uint32)
+    scales = np.ones(2, dtype=np.float32)
+    lut = np.zeros(4096, dtype=np.float32)
+    with pytest.raises(ValueError):
+        oracle.expand(codes, scales, lut, 1, T, L, k, 3 * T, 2, block_interleave=2)
+    with pytest.raises(ValueError):
+        oracle.expand(codes, scales, lut, 1, T, L, k, 3 * T, 2, block_interleave=1)
+    oracle.expand(codes, scales, lut, 1, T, L, k, 3 * T, 2, block_interleave=0)
