@@ -132,7 +132,9 @@ def gemv_bench(T, torch, dev, k, steps, warmup):
 
 
 def extra_bench(T, torch, dev, steps, warmup):
-    """Other workloads: axis-0 scatter k=3, prefill M=5/8/16/32, MLP k=4 M=1/32."""
+    """Other workloads: axis-0 scatter k=3, prefill M=5/8/16/32, MLP k=4 M=1/32,
+    and the scatter and the k=2 GEMV on block-interleave-2 codes (the same
+    uniform random words, read in the pair layout)."""
     from dequant_gemm_trellis_amd import synth
 
     out = {}
@@ -147,6 +149,20 @@ def extra_bench(T, torch, dev, steps, warmup):
     ms = time_calls(torch, lambda i: T.gemv_scatter(*sets.items[i], g, workspace=ws, y=y),
                     len(sets.items), steps, warmup)
     out["scatter_qwen_down_k3"] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
+    g2 = T.Geometry.of(synth.Shape(0, 256, 12, 3, QWEN_OUT, QWEN_IN, 2))
+    ms = time_calls(torch, lambda i: T.gemv_scatter(*sets.items[i], g2, workspace=ws, y=y),
+                    len(sets.items), steps, warmup)
+    out["scatter_qwen_down_k3_interleave2"] = {"us_per_call": ms * 1e3,
+                                               "gbps": cb / (ms * 1e-3) / 1e9}
+    del sets
+    sh = synth.Shape(1, 256, 12, 2, QWEN_IN, QWEN_OUT, 2)
+    cb = sh.rows * sh.words_per_row * 4
+    sets = Sets(sh, 1, C["qwen_up_gemv"], n_sets_for(cb), T, torch, dev)
+    y = torch.empty(QWEN_OUT, dtype=torch.bfloat16, device=dev)
+    g2 = T.Geometry.of(sh)
+    ms = time_calls(torch, lambda i: T.gemv(*sets.items[i], g2, y=y), len(sets.items), steps,
+                    warmup)
+    out["gemv_qwen_up_k2_interleave2"] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
     del sets
     for k in (2, 3, 4):
         sh = synth.Shape(1, 256, 12, k, QWEN_IN, QWEN_OUT)
@@ -320,7 +336,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_entry(),
-                     "kernel": "gemv_kernel<2>",
+                     "kernel": "gemv_kernel<2, false>",
                      "bytes_per_launch": head["code_bytes"]},
         "decode": {"bound": "lds_gather", "unit": "weights/clk/CU",
                    "achieved": round(head["decode_w_per_clk_cu"], 3),

@@ -4,8 +4,9 @@
 //
 // Pages cited: diff views of "@mlx-bun/inference" 0.0.0-stage -> 1.0.0;
 // page 60 tiled-prefill.ts and wide-prefill.ts reject unsupported geometry
-// (T 256, L 12, k 2/3/4, cols a multiple of 256, row-contiguous layout)
-// before any launch.
+// (T 256, L 12, k 2/3/4, cols a multiple of 256) before any launch; page 60
+// vector-expand.ts and page 59 scatter.ts define the block-interleave-2 code
+// layout.
 #include <math.h>
 #include <stdint.h>
 
@@ -19,6 +20,7 @@ constexpr uint64_t kMaxWeights = 1ull << 40;
 
 struct Dims {
     int rows, cols, nb;
+    trellis::CodeLayout lay;
 };
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -36,6 +38,9 @@ int check_geometry(const trellis_geometry* g, Dims* d) {
     if (static_cast<uint64_t>(d->rows) * static_cast<uint64_t>(d->cols) > kMaxWeights)
         return TRELLIS_ERR_GEOMETRY;
     d->nb = d->cols / g->T;
+    if (g->block_interleave != 0 && g->block_interleave != 2) return TRELLIS_ERR_GEOMETRY;
+    if (g->block_interleave == 2 && d->nb % 2 != 0) return TRELLIS_ERR_GEOMETRY;
+    d->lay = trellis::code_layout(g->block_interleave, d->rows, d->nb, g->k);
     return TRELLIS_OK;
 }
 
@@ -67,8 +72,8 @@ int status_of(hipError_t e) { return e == hipSuccess ? TRELLIS_OK : TRELLIS_ERR_
 hipError_t launch_axis1_m1(const uint16_t* x, const uint32_t* codes, const float* scales,
                            const float* lut, uint16_t* y, const Dims& d, int k, hipStream_t st) {
     if (d.nb <= trellis::gemv_max_blocks(k))
-        return trellis::launch_gemv(x, codes, scales, lut, y, d.rows, d.nb, k, st);
-    return trellis::launch_axis1(x, 1, codes, scales, lut, y, d.rows, d.nb, k, st);
+        return trellis::launch_gemv(x, codes, d.lay, scales, lut, y, d.rows, d.nb, k, st);
+    return trellis::launch_axis1(x, 1, codes, d.lay, scales, lut, y, d.rows, d.nb, k, st);
 }
 
 }  // namespace
@@ -108,8 +113,8 @@ int trellis_gemv_scatter(const uint16_t* x, const uint32_t* codes, const float* 
     if (!workspace) return TRELLIS_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return TRELLIS_ERR_ALIGN;
     if (workspace_bytes < axis0_workspace(d, 1)) return TRELLIS_ERR_WORKSPACE;
-    return status_of(trellis::launch_axis0(x, 1, codes, scales, lut, workspace, y, d.rows, d.cols,
-                                           g->k, stream));
+    return status_of(trellis::launch_axis0(x, 1, codes, d.lay, scales, lut, workspace, y, d.rows,
+                                           d.cols, g->k, stream));
 }
 
 int trellis_prefill(const uint16_t* x, int32_t M, const uint32_t* codes, const float* scales,
@@ -124,12 +129,13 @@ int trellis_prefill(const uint16_t* x, int32_t M, const uint32_t* codes, const f
     if (g->axis == 1 && M == 1)
         return status_of(launch_axis1_m1(x, codes, scales, lut, y, d, g->k, stream));
     if (g->axis == 1)
-        return status_of(trellis::launch_axis1(x, M, codes, scales, lut, y, d.rows, d.nb, g->k, stream));
+        return status_of(trellis::launch_axis1(x, M, codes, d.lay, scales, lut, y, d.rows, d.nb, g->k,
+                                               stream));
     if (!workspace) return TRELLIS_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return TRELLIS_ERR_ALIGN;
     if (workspace_bytes < axis0_workspace(d, M)) return TRELLIS_ERR_WORKSPACE;
-    return status_of(trellis::launch_axis0(x, M, codes, scales, lut, workspace, y, d.rows, d.cols,
-                                           g->k, stream));
+    return status_of(trellis::launch_axis0(x, M, codes, d.lay, scales, lut, workspace, y, d.rows,
+                                           d.cols, g->k, stream));
 }
 
 size_t trellis_workspace_bytes(const trellis_geometry* g, int32_t M, int32_t op) {
@@ -156,7 +162,27 @@ int trellis_expand(const uint32_t* codes, const float* scales, const float* lut,
     if ((st = check_operands(codes, scales, lut))) return st;
     if (!w) return TRELLIS_ERR_NULL;
     if (!aligned(w, 16)) return TRELLIS_ERR_ALIGN;
-    return status_of(trellis::launch_expand(codes, scales, lut, w, d.rows, d.nb, g->k, stream));
+    return status_of(
+        trellis::launch_expand(codes, d.lay, scales, lut, w, d.rows, d.nb, g->k, stream));
+}
+
+int trellis_repack(const uint32_t* src, uint32_t* dst, const trellis_geometry* g,
+                   int32_t to_block_interleave, hipStream_t stream) {
+    Dims d;
+    int st = check_geometry(g, &d);
+    if (st) return st;
+    trellis_geometry to = *g;
+    to.block_interleave = to_block_interleave;
+    Dims dt;
+    if ((st = check_geometry(&to, &dt))) return st;
+    if (!src || !dst) return TRELLIS_ERR_NULL;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return TRELLIS_ERR_ALIGN;
+    const uint64_t bytes = static_cast<uint64_t>(d.rows) * static_cast<uint64_t>(d.cols) *
+                           static_cast<uint64_t>(g->k) / 8;
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), t0 = reinterpret_cast<uintptr_t>(dst);
+    if (s0 < t0 + bytes && t0 < s0 + bytes) return TRELLIS_ERR_OVERLAP;
+    return status_of(trellis::launch_repack(src, d.lay, dst, to_block_interleave == 2, d.rows, d.nb,
+                                            g->k, stream));
 }
 
 const char* trellis_strerror(int status) {
@@ -168,6 +194,7 @@ const char* trellis_strerror(int status) {
     case TRELLIS_ERR_LUT: return "codebook must hold 4096 finite float32 entries";
     case TRELLIS_ERR_WORKSPACE: return "workspace missing or too small";
     case TRELLIS_ERR_HIP: return "HIP runtime error while enqueuing work";
+    case TRELLIS_ERR_OVERLAP: return "source and destination arrays overlap";
     default: return "unknown trellis status";
     }
 }

@@ -184,7 +184,7 @@ template <int K, int MT, bool VEC>
 __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
     const float* __restrict__ scales, const float* __restrict__ lut,
-    float* __restrict__ partial, int R, int C, int M, int P) {
+    float* __restrict__ partial, CodeLayout lay, int R, int C, int M, int P) {
     constexpr int wpb = Bits<K>::wpb;
     constexpr bool kPair = A0Lds<K>::pair;
     __shared__ __attribute__((aligned(16))) float lds[A0Lds<K>::floats];
@@ -209,9 +209,9 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const int s0 = p0 + wave * (p1 - p0) / kA0Waves;
     const int s1 = p0 + (wave + 1) * (p1 - p0) / kA0Waves;
 
-    A0Ctx cx{codes + static_cast<size_t>(blk) * wpb, scales,
+    A0Ctx cx{codes + block_word<K>(lay, 0, blk), scales,
              {x + static_cast<size_t>(j < M ? j : 0) * R, x + static_cast<size_t>(16 + j < M ? 16 + j : 0) * R},
-             static_cast<size_t>(C) / kT * wpb, w0, w1, R, c};
+             lay.row_words, w0, w1, R, c};
 
     floatx4 acc[8][MT];
 #pragma unroll
@@ -303,19 +303,21 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
 }
 
 template <int K, int MT, bool VEC>
-hipError_t launch_axis0_k(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
-                          const float* lut, float* partial, int R, int C, int P, hipStream_t st) {
+hipError_t launch_axis0_k(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
+                          const float* scales, const float* lut, float* partial, int R, int C, int P,
+                          hipStream_t st) {
     const dim3 grid(static_cast<unsigned>((C / kTileCols) * P));
     return launch_kernel(axis0_mma_kernel<K, MT, VEC>, grid, dim3(kA0Threads), st, x, codes, scales,
-                         lut, partial, R, C, M, P);
+                         lut, partial, lay, R, C, M, P);
 }
 
 template <int K, int MT>
-hipError_t launch_axis0_v(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
-                          const float* lut, float* partial, int R, int C, int P, hipStream_t st) {
+hipError_t launch_axis0_v(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
+                          const float* scales, const float* lut, float* partial, int R, int C, int P,
+                          hipStream_t st) {
     if (R % 8 == 0)
-        return launch_axis0_k<K, MT, true>(x, M, codes, scales, lut, partial, R, C, P, st);
-    return launch_axis0_k<K, MT, false>(x, M, codes, scales, lut, partial, R, C, P, st);
+        return launch_axis0_k<K, MT, true>(x, M, codes, lay, scales, lut, partial, R, C, P, st);
+    return launch_axis0_k<K, MT, false>(x, M, codes, lay, scales, lut, partial, R, C, P, st);
 }
 
 }  // namespace
@@ -327,19 +329,19 @@ int axis0_parts(int R, int C) {
     return P > 1 ? P : 1;
 }
 
-hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
-                        const float* lut, float* partial, uint16_t* y, int R, int C, int k,
-                        hipStream_t st) {
+hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
+                        const float* scales, const float* lut, float* partial, uint16_t* y, int R,
+                        int C, int k, hipStream_t st) {
     const bool two = M > 16;
     const int P = axis0_parts(R, C);
     hipError_t e;
     switch (k) {
-    case 2: e = two ? launch_axis0_v<2, 2>(x, M, codes, scales, lut, partial, R, C, P, st)
-                    : launch_axis0_v<2, 1>(x, M, codes, scales, lut, partial, R, C, P, st); break;
-    case 3: e = two ? launch_axis0_v<3, 2>(x, M, codes, scales, lut, partial, R, C, P, st)
-                    : launch_axis0_v<3, 1>(x, M, codes, scales, lut, partial, R, C, P, st); break;
-    case 4: e = two ? launch_axis0_v<4, 2>(x, M, codes, scales, lut, partial, R, C, P, st)
-                    : launch_axis0_v<4, 1>(x, M, codes, scales, lut, partial, R, C, P, st); break;
+    case 2: e = two ? launch_axis0_v<2, 2>(x, M, codes, lay, scales, lut, partial, R, C, P, st)
+                    : launch_axis0_v<2, 1>(x, M, codes, lay, scales, lut, partial, R, C, P, st); break;
+    case 3: e = two ? launch_axis0_v<3, 2>(x, M, codes, lay, scales, lut, partial, R, C, P, st)
+                    : launch_axis0_v<3, 1>(x, M, codes, lay, scales, lut, partial, R, C, P, st); break;
+    case 4: e = two ? launch_axis0_v<4, 2>(x, M, codes, lay, scales, lut, partial, R, C, P, st)
+                    : launch_axis0_v<4, 1>(x, M, codes, lay, scales, lut, partial, R, C, P, st); break;
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;

@@ -78,6 +78,7 @@ struct PrefillLds {
 
 struct TaskCtx {
     const uint32_t* codes;
+    CodeLayout lay;
     const float* scales;
     int nb, gc, r0, r1, j, cp;
 };
@@ -90,12 +91,20 @@ struct Task {
     bool valid;  // this lane's row lies in the workgroup's range
 };
 
+// Word offset of block b of row rc. Row-major codes (PAIRS false) keep the
+// plain row-major product; the general layout form measured 1% slower there
+// (more scalar work per task).
+template <int K, bool PAIRS>
+__device__ __forceinline__ uint64_t task_word(const TaskCtx& cx, int rc, int b) {
+    if constexpr (PAIRS) return block_word<K>(cx.lay, rc, b);
+    else return (static_cast<size_t>(rc) * cx.nb + b) * Bits<K>::wpb;
+}
+
 // Load task tau's code words (2k per lane) and scale. Past the wave's last
 // task it re-reads that task: every load is unconditional, so the compiler's
 // memory-counter waits never have to cover a skipped load.
-template <int K>
+template <int K, bool PAIRS>
 __device__ __forceinline__ void load_task(Task<K>& t, const TaskCtx& cx, int tau, int tau_end) {
-    constexpr int wpb = Bits<K>::wpb;
     const int tc = tau < tau_end ? tau : tau_end - 1;
     const int b = tc / cx.gc;
     const int g = tc - b * cx.gc;
@@ -104,7 +113,7 @@ __device__ __forceinline__ void load_task(Task<K>& t, const TaskCtx& cx, int tau
     const int rc = t.valid ? row : cx.r1 - 1;
     t.b = b;
     t.g = g;
-    load_run64_words<K>(cx.codes + (static_cast<size_t>(rc) * cx.nb + b) * wpb, cx.cp, t.w);
+    load_run64_words<K>(cx.codes + task_word<K, PAIRS>(cx, rc, b), cx.cp, t.w);
     t.scale = cx.scales[rc];
 }
 
@@ -112,12 +121,11 @@ __device__ __forceinline__ void load_task(Task<K>& t, const TaskCtx& cx, int tau
 // through the restrict kernel pointers the loads count as invariant and the
 // compiler sinks them past the table stores and the barrier to their first
 // use, so the table stores and the code words no longer overlap.
-template <int K>
+template <int K, bool PAIRS>
 __device__ __forceinline__ void load_task_opaque(Task<K>& t, const TaskCtx& cx, int tau, int tau_end) {
     using gu32 = const __attribute__((address_space(1))) uint32_t*;
     using gu32x4 = const __attribute__((address_space(1))) u32x4*;
     using gf32 = const __attribute__((address_space(1))) float*;
-    constexpr int wpb = Bits<K>::wpb;
     gu32 codes = (gu32)cx.codes;  // generic to global: an address-space cast
     gf32 scales = (gf32)cx.scales;
     asm volatile("" : "+s"(codes), "+s"(scales));
@@ -129,7 +137,7 @@ __device__ __forceinline__ void load_task_opaque(Task<K>& t, const TaskCtx& cx, 
     const int rc = t.valid ? row : cx.r1 - 1;
     t.b = b;
     t.g = g;
-    const gu32 p = codes + (static_cast<size_t>(rc) * cx.nb + b) * wpb + 2 * K * cx.cp;
+    const gu32 p = codes + task_word<K, PAIRS>(cx, rc, b) + 2 * K * cx.cp;
     if constexpr (K == 2) {
         const u32x4 v = *reinterpret_cast<gu32x4>(p);
         t.w[0] = v.x; t.w[1] = v.y; t.w[2] = v.z; t.w[3] = v.w;
@@ -316,11 +324,11 @@ __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& 
     });
 }
 
-template <int K, int MT, bool DIRECT>
+template <int K, int MT, bool DIRECT, bool PAIRS>
 __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
     const float* __restrict__ scales, const float* __restrict__ lut,
-    uint16_t* __restrict__ y, int N, int nb, int M) {
+    uint16_t* __restrict__ y, CodeLayout lay, int N, int nb, int M) {
     constexpr int kThreadsP = PrefillShape<MT>::threads, kWaves = PrefillShape<MT>::waves;
     using Lds = PrefillLds<K, MT, DIRECT>;
     __shared__ __attribute__((aligned(16))) float lds[Lds::floats];
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     xs.slot = reinterpret_cast<u32x4*>(lds + Lds::tab_floats) + wave * Lds::slot_chunks;
     xs.nb = nb;
 
-    TaskCtx cx{codes, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp};
+    TaskCtx cx{codes, lay, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp};
     floatx4 acc[kGroups][MT];
 #pragma unroll
     for (int g = 0; g < kGroups; ++g)
@@ -373,8 +381,8 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     fetch_table<kThreadsP, kPair>(tsrc, lut);
     asm volatile("" ::: "memory");
     Task<K> ta, tb, tc;
-    load_task_opaque<K>(ta, cx, tau0, tau1 > 1 ? tau1 : 1);
-    load_task_opaque<K>(tb, cx, tau0 + 1, tau1 > 1 ? tau1 : 1);
+    load_task_opaque<K, PAIRS>(ta, cx, tau0, tau1 > 1 ? tau1 : 1);
+    load_task_opaque<K, PAIRS>(tb, cx, tau0 + 1, tau1 > 1 ? tau1 : 1);
     XFrags<MT> xn;
     if constexpr (DIRECT) load_x_frags_opaque<MT>(xn, xs.xa, ta.b);
     asm volatile("" ::: "memory");
@@ -387,11 +395,11 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     XFrags<MT> xf;
     int xb = -1;  // block whose fragments xf holds
     for (int t0 = tau0; t0 < tau1; t0 += 3) {
-        load_task<K>(tc, cx, t0 + 2, tau1);
+        load_task<K, PAIRS>(tc, cx, t0 + 2, tau1);
         run_task<K, MT, DIRECT>(ta, xf, xn, xb, xs, acc, tab, lane, j, c);
-        load_task<K>(ta, cx, t0 + 3, tau1);
+        load_task<K, PAIRS>(ta, cx, t0 + 3, tau1);
         if (t0 + 1 < tau1) run_task<K, MT, DIRECT>(tb, xf, xn, xb, xs, acc, tab, lane, j, c);
-        load_task<K>(tb, cx, t0 + 4, tau1);
+        load_task<K, PAIRS>(tb, cx, t0 + 4, tau1);
         if (t0 + 2 < tau1) run_task<K, MT, DIRECT>(tc, xf, xn, xb, xs, acc, tab, lane, j, c);
     }
     __syncthreads();  // the table is dead from here on; its space takes the partials
@@ -422,8 +430,7 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
 template <int K>
 __global__ __launch_bounds__(kThreads) void expand_kernel(
     const uint32_t* __restrict__ codes, const float* __restrict__ scales,
-    const float* __restrict__ lut, uint16_t* __restrict__ w, long rows, int nb) {
-    constexpr int wpb = Bits<K>::wpb;
+    const float* __restrict__ lut, uint16_t* __restrict__ w, CodeLayout lay, long rows, int nb) {
     __shared__ __attribute__((aligned(16))) float lut_s[kLutEntries];
     stage_lut<kThreads>(lut_s, lut);
     __syncthreads();
@@ -434,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(
     const int rem = static_cast<int>(run - row * nb * 4);
     const int b = rem >> 2, cp = rem & 3, c = 3 - cp;
     uint32_t wr[2 * K + 1];
-    load_run64<K>(codes + (static_cast<size_t>(row) * nb + b) * wpb, cp, wr);
+    load_run64<K>(codes + block_word<K>(lay, static_cast<uint32_t>(row), b), cp, wr);
     const float scale = scales[row];
     uint16_t* dst = w + static_cast<size_t>(row) * nb * kT + b * kT + 64 * c;
     static_for<0, 8>([&](auto sc) {
@@ -444,53 +451,62 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(
 }
 
 template <int K, int MT, bool DIRECT>
-hipError_t launch_axis1_k(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
-                          const float* lut, uint16_t* y, int N, int nb, hipStream_t st) {
+hipError_t launch_axis1_k(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
+                          const float* scales, const float* lut, uint16_t* y, int N, int nb,
+                          hipStream_t st) {
     // One workgroup per compute unit while that leaves at most kGroups groups
     // each; beyond that, as many workgroups as needed, run in rounds.
     const int groups = (N + 15) / 16;
     int G = groups < cu_count() ? groups : cu_count();
     if ((N + G - 1) / G > 16 * kGroups) G = (N + 16 * kGroups - 1) / (16 * kGroups);
-    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT>, dim3(G), dim3(PrefillShape<MT>::threads), st,
-                         x, codes, scales,
-                         lut, y, N, nb, M);
+    // Row-major iff a row's blocks are contiguous (with two blocks per row the
+    // two layouts coincide).
+    if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
+        return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, false>, dim3(G),
+                             dim3(PrefillShape<MT>::threads), st, x, codes, scales, lut, y, lay, N,
+                             nb, M);
+    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, true>, dim3(G),
+                         dim3(PrefillShape<MT>::threads), st, x, codes, scales, lut, y, lay, N, nb,
+                         M);
 }
 
 template <int K>
-hipError_t launch_expand_k(const uint32_t* codes, const float* scales, const float* lut,
-                           uint16_t* w, long rows, int nb, hipStream_t st) {
+hipError_t launch_expand_k(const uint32_t* codes, CodeLayout lay, const float* scales,
+                           const float* lut, uint16_t* w, long rows, int nb, hipStream_t st) {
     const long runs = rows * nb * 4;
     const dim3 grid(static_cast<unsigned>((runs + kThreads - 1) / kThreads));
-    return launch_kernel(expand_kernel<K>, grid, dim3(kThreads), st, codes, scales, lut, w, rows, nb);
+    return launch_kernel(expand_kernel<K>, grid, dim3(kThreads), st, codes, scales, lut, w, lay, rows,
+                         nb);
 }
 
 }  // namespace
 
-hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
-                        const float* lut, uint16_t* y, int N, int nb, int k, hipStream_t st) {
+hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
+                        const float* scales, const float* lut, uint16_t* y, int N, int nb, int k,
+                        hipStream_t st) {
     // One M tile up to M = 16, two above; direct activation fragments up to
     // kDirectMaxM.
     const int shape = M > 16 ? 2 : M > kDirectMaxM ? 1 : 0;
     switch (k * 4 + shape) {
-    case 8: return launch_axis1_k<2, 1, true>(x, M, codes, scales, lut, y, N, nb, st);
-    case 9: return launch_axis1_k<2, 1, false>(x, M, codes, scales, lut, y, N, nb, st);
-    case 10: return launch_axis1_k<2, 2, false>(x, M, codes, scales, lut, y, N, nb, st);
-    case 12: return launch_axis1_k<3, 1, true>(x, M, codes, scales, lut, y, N, nb, st);
-    case 13: return launch_axis1_k<3, 1, false>(x, M, codes, scales, lut, y, N, nb, st);
-    case 14: return launch_axis1_k<3, 2, false>(x, M, codes, scales, lut, y, N, nb, st);
-    case 16: return launch_axis1_k<4, 1, true>(x, M, codes, scales, lut, y, N, nb, st);
-    case 17: return launch_axis1_k<4, 1, false>(x, M, codes, scales, lut, y, N, nb, st);
-    case 18: return launch_axis1_k<4, 2, false>(x, M, codes, scales, lut, y, N, nb, st);
+    case 8: return launch_axis1_k<2, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    case 9: return launch_axis1_k<2, 1, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    case 10: return launch_axis1_k<2, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    case 12: return launch_axis1_k<3, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    case 13: return launch_axis1_k<3, 1, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    case 14: return launch_axis1_k<3, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    case 16: return launch_axis1_k<4, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    case 17: return launch_axis1_k<4, 1, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    case 18: return launch_axis1_k<4, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_expand(const uint32_t* codes, const float* scales, const float* lut,
-                         uint16_t* w, long rows, int nb, int k, hipStream_t st) {
+hipError_t launch_expand(const uint32_t* codes, CodeLayout lay, const float* scales,
+                         const float* lut, uint16_t* w, long rows, int nb, int k, hipStream_t st) {
     switch (k) {
-    case 2: return launch_expand_k<2>(codes, scales, lut, w, rows, nb, st);
-    case 3: return launch_expand_k<3>(codes, scales, lut, w, rows, nb, st);
-    case 4: return launch_expand_k<4>(codes, scales, lut, w, rows, nb, st);
+    case 2: return launch_expand_k<2>(codes, lay, scales, lut, w, rows, nb, st);
+    case 3: return launch_expand_k<3>(codes, lay, scales, lut, w, rows, nb, st);
+    case 4: return launch_expand_k<4>(codes, lay, scales, lut, w, rows, nb, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -10,6 +10,8 @@
 
 #include <type_traits>
 
+#include "launch.hpp"
+
 namespace trellis {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -27,6 +29,13 @@ constexpr int kWave = 64;
 template <int K> struct Bits {
     static constexpr int wpb = kT * K / 32;   // 16 / 24 / 32
 };
+
+// Word offset of block b of stored row r (CodeLayout).
+template <int K>
+__device__ __forceinline__ uint64_t block_word(const CodeLayout& lay, uint32_t r, uint32_t b) {
+    return static_cast<uint64_t>(r) * lay.row_words + static_cast<uint64_t>(b >> 1) * lay.pair_words +
+           (b & 1u) * static_cast<uint32_t>(Bits<K>::wpb);
+}
 
 // Copy the 16 KB float32 codebook into LDS with 16-byte loads
 // (page 59 scatter.ts stages the LUT into threadgroup memory once per group).

@@ -81,7 +81,8 @@ struct XFrag {
 };
 
 struct Ctx {
-    const uint32_t* codes;   // first word of the row chunk
+    const uint32_t* codes;   // word 0 of block 0 of the row chunk's first row
+    CodeLayout lay;          // where a (row, block)'s words sit
     const float* scales;     // scale of the chunk's first row
     int nb;                  // blocks per row
     int cr;                  // rows in the chunk
@@ -95,16 +96,20 @@ __device__ __forceinline__ uint32_t div_magic(int d) {
 }
 
 // Unit u of the chunk (block-major): block u / cr, chunk row u % cr. Units at
-// or past the wave's end re-read its last unit.
-template <int K>
+// or past the wave's end re-read its last unit. Row-major codes (PAIRS false)
+// sit at the unit's row-major index times wpb, a 32-bit product within the
+// chunk; block-interleaved codes take the general 64-bit offset.
+template <int K, bool PAIRS>
 __device__ __forceinline__ void load_step(Step<K>& st, const Ctx& cx, int u, int u_end) {
-    constexpr int wpb = Bits<K>::wpb;
     const uint32_t uu = static_cast<uint32_t>(u < u_end ? u : u_end - 1);
     const uint32_t b = __umulhi(uu << 1, cx.magic);
     const uint32_t rl = uu - b * static_cast<uint32_t>(cx.cr);
     st.b = b;
     st.slot = rl * static_cast<uint32_t>(cx.nb) + b;
-    load_run64_words<K>(cx.codes + st.slot * wpb, cx.cp, st.w);
+    if constexpr (PAIRS)
+        load_run64_words<K>(cx.codes + block_word<K>(cx.lay, rl, b), cx.cp, st.w);
+    else
+        load_run64_words<K>(cx.codes + st.slot * Bits<K>::wpb, cx.cp, st.w);
     st.scale = cx.scales[rl];
 }
 
@@ -158,12 +163,11 @@ __device__ __forceinline__ void run_step(Step<K> st, XFrag& xf, uint32_t& xb,
     }
 }
 
-template <int K>
+template <int K, bool PAIRS>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
     const float* __restrict__ scales, const float* __restrict__ lut,
-    uint16_t* __restrict__ y, int N, int nb) {
-    constexpr int wpb = Bits<K>::wpb;
+    uint16_t* __restrict__ y, CodeLayout lay, int N, int nb) {
     // One LDS array with the table first: a gather address then needs no base
     // added (the table at 64 KB, past the 16-bit instruction offset, costs a
     // VALU op per weight).
@@ -181,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const int j = lane & 15, c = lane >> 4;
     const int chunk_rows = kPartialCap / nb;
 
-    Ctx cx{codes + static_cast<size_t>(r0) * nb * wpb, scales + r0, nb, 1, 0u, 3 - c};
+    Ctx cx{codes + static_cast<size_t>(r0) * lay.row_words, lay, scales + r0, nb, 1, 0u, 3 - c};
     Step<K> sa, sb, sc;
     XFrag xf;
     uint32_t xb = ~0u;
@@ -209,8 +213,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     int ub = wave * U / kWaves, ue = (wave + 1) * U / kWaves;
     cx.cr = CR;
     cx.magic = div_magic(CR);
-    load_step<K>(sa, cx, ub + j, ue > 1 ? ue : 1);
-    load_step<K>(sb, cx, ub + 16 + j, ue > 1 ? ue : 1);
+    load_step<K, PAIRS>(sa, cx, ub + j, ue > 1 ? ue : 1);
+    load_step<K, PAIRS>(sb, cx, ub + 16 + j, ue > 1 ? ue : 1);
     store_table<kThreads, kPair>(tsrc, tab);
 #pragma unroll
     for (int q = 0; q < kXChunks; ++q) {
@@ -225,12 +229,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         ub = wave * U / kWaves;
         ue = (wave + 1) * U / kWaves;
         if (cr0 != r0 && ue > ub) {
-            cx.codes = codes + static_cast<size_t>(cr0) * nb * wpb;
+            cx.codes = codes + static_cast<size_t>(cr0) * lay.row_words;
             cx.scales = scales + cr0;
             cx.cr = CR;
             cx.magic = div_magic(CR);
-            load_step<K>(sa, cx, ub + j, ue);
-            load_step<K>(sb, cx, ub + 16 + j, ue);
+            load_step<K, PAIRS>(sa, cx, ub + j, ue);
+            load_step<K, PAIRS>(sb, cx, ub + 16 + j, ue);
         }
         // Three register sets rotate, so the code words of the next two steps
         // are in flight while one step is decoded. Every load is
@@ -240,11 +244,11 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         // exit between loads, makes it wait for the prefetch too.
         for (int u0 = ub; u0 < ue; u0 += 48) {
             const int ua = u0 + j;
-            load_step<K>(sc, cx, ua + 32, ue);
+            load_step<K, PAIRS>(sc, cx, ua + 32, ue);
             run_step<K>(sa, xf, xb, xs, tab, part, ua, ue, j, c);
-            load_step<K>(sa, cx, ua + 48, ue);
+            load_step<K, PAIRS>(sa, cx, ua + 48, ue);
             if (u0 + 16 < ue) run_step<K>(sb, xf, xb, xs, tab, part, ua + 16, ue, j, c);
-            load_step<K>(sb, cx, ua + 64, ue);
+            load_step<K, PAIRS>(sb, cx, ua + 64, ue);
             if (u0 + 32 < ue) run_step<K>(sc, xf, xb, xs, tab, part, ua + 32, ue, j, c);
         }
         __syncthreads();
@@ -267,11 +271,17 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 }
 
 template <int K>
-hipError_t launch_gemv_k(const uint16_t* x, const uint32_t* codes, const float* scales,
-                         const float* lut, uint16_t* y, int N, int nb, hipStream_t st) {
+hipError_t launch_gemv_k(const uint16_t* x, const uint32_t* codes, CodeLayout lay,
+                         const float* scales, const float* lut, uint16_t* y, int N, int nb,
+                         hipStream_t st) {
     const int G = N < cu_count() ? N : cu_count();
-    return launch_kernel(gemv_kernel<K>, dim3(G), dim3(kThreads), st, x, codes, scales, lut, y,
-                         N, nb);
+    // Row-major iff a row's blocks are contiguous (with two blocks per row the
+    // two layouts coincide).
+    if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
+        return launch_kernel(gemv_kernel<K, false>, dim3(G), dim3(kThreads), st, x, codes, scales,
+                             lut, y, lay, N, nb);
+    return launch_kernel(gemv_kernel<K, true>, dim3(G), dim3(kThreads), st, x, codes, scales, lut,
+                         y, lay, N, nb);
 }
 
 }  // namespace
@@ -294,12 +304,12 @@ int gemv_max_blocks(int k) {
     return k == 2 ? GemvLds<2>::max_blocks : GemvLds<4>::max_blocks;
 }
 
-hipError_t launch_gemv(const uint16_t* x, const uint32_t* codes, const float* scales,
+hipError_t launch_gemv(const uint16_t* x, const uint32_t* codes, CodeLayout lay, const float* scales,
                        const float* lut, uint16_t* y, int N, int nb, int k, hipStream_t st) {
     switch (k) {
-    case 2: return launch_gemv_k<2>(x, codes, scales, lut, y, N, nb, st);
-    case 3: return launch_gemv_k<3>(x, codes, scales, lut, y, N, nb, st);
-    case 4: return launch_gemv_k<4>(x, codes, scales, lut, y, N, nb, st);
+    case 2: return launch_gemv_k<2>(x, codes, lay, scales, lut, y, N, nb, st);
+    case 3: return launch_gemv_k<3>(x, codes, lay, scales, lut, y, N, nb, st);
+    case 4: return launch_gemv_k<4>(x, codes, lay, scales, lut, y, N, nb, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -21,26 +21,51 @@ hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_
 // Compute units of the current device (cached per device).
 int cu_count();
 
+// Where the words of block b of stored row r start in the code array:
+//   r * row_words + (b / 2) * pair_words + (b % 2) * wpb      (wpb = 8k).
+// Row-major layout, [rows][nb][wpb] (block interleave 0):
+//   row_words = nb * wpb, pair_words = 2 * wpb.
+// Block interleave 2, [nb / 2][rows][2][wpb] (pages: vector-expand.ts and
+// scatter.ts with INTERLEAVE set):
+//   row_words = 2 * wpb, pair_words = rows * 2 * wpb.
+struct CodeLayout {
+    uint64_t row_words;
+    uint64_t pair_words;
+};
+
+inline CodeLayout code_layout(int interleave, int rows, int nb, int k) {
+    const uint64_t wpb = 8u * static_cast<uint64_t>(k);
+    if (interleave == 2) return {2 * wpb, static_cast<uint64_t>(rows) * 2 * wpb};
+    return {static_cast<uint64_t>(nb) * wpb, 2 * wpb};
+}
+
 // Axis-1 GEMV (M = 1): persistent kernel, one workgroup per compute unit,
 // activations staged in LDS. Needs nb <= gemv_max_blocks(k).
-hipError_t launch_gemv(const uint16_t* x, const uint32_t* codes, const float* scales,
+hipError_t launch_gemv(const uint16_t* x, const uint32_t* codes, CodeLayout lay, const float* scales,
                        const float* lut, uint16_t* y, int N, int nb, int k, hipStream_t st);
 int gemv_max_blocks(int k);
 
 // Axis 1, 1 <= M <= 32: y[M][N] from x[M][nb*256] and codes [N][nb][8k].
 // Persistent workgroups of at most 80 rows; any nb.
-hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
-                        const float* lut, uint16_t* y, int N, int nb, int k, hipStream_t st);
+hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
+                        const float* scales, const float* lut, uint16_t* y, int N, int nb, int k,
+                        hipStream_t st);
 
 // Axis 0, 1 <= M <= 32: per-part partials, then the ordered reduce over the
 // parts into y[M][C]. `partial` holds axis0_parts(R, C) * M * C floats.
-hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
-                        const float* lut, float* partial, uint16_t* y, int R, int C, int k,
-                        hipStream_t st);
+hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
+                        const float* scales, const float* lut, float* partial, uint16_t* y, int R,
+                        int C, int k, hipStream_t st);
 int axis0_parts(int R, int C);
 
 // Decoded weights w[rows][nb*256].
-hipError_t launch_expand(const uint32_t* codes, const float* scales, const float* lut,
-                         uint16_t* w, long rows, int nb, int k, hipStream_t st);
+hipError_t launch_expand(const uint32_t* codes, CodeLayout lay, const float* scales,
+                         const float* lut, uint16_t* w, long rows, int nb, int k, hipStream_t st);
+
+// Copy every block of a code array from layout `from` into dst, written
+// densely in block-interleave-2 order when dst_pairs, else row-major (src and
+// dst must not overlap).
+hipError_t launch_repack(const uint32_t* src, CodeLayout from, uint32_t* dst, bool dst_pairs,
+                         int rows, int nb, int k, hipStream_t st);
 
 }  // namespace trellis

@@ -48,6 +48,7 @@ class Shape:
     k: int
     in_features: int
     out_features: int
+    block_interleave: int = 0  # code layout: 0 row-major, 2 block pairs
 
     @property
     def rows(self) -> int:

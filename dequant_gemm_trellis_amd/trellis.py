@@ -29,6 +29,7 @@ ERR_ALIGN = -3
 ERR_LUT = -4
 ERR_WORKSPACE = -5
 ERR_HIP = -6
+ERR_OVERLAP = -7
 OP_GEMV = 0
 OP_GEMV_SCATTER = 1
 OP_PREFILL = 2
@@ -36,16 +37,18 @@ MAX_M = 32
 
 # Every function trellis.h declares, for the export check.
 EXPORTED = ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_scatter", "trellis_prefill",
-            "trellis_workspace_bytes", "trellis_expand", "trellis_strerror")
+            "trellis_workspace_bytes", "trellis_expand", "trellis_repack", "trellis_strerror")
 
 
 class Geometry(C.Structure):
     _fields_ = [("axis", C.c_int32), ("T", C.c_int32), ("L", C.c_int32), ("k", C.c_int32),
-                ("in_features", C.c_int32), ("out_features", C.c_int32)]
+                ("in_features", C.c_int32), ("out_features", C.c_int32),
+                ("block_interleave", C.c_int32)]
 
     @classmethod
     def of(cls, shape: Shape) -> "Geometry":
-        return cls(shape.axis, shape.T, shape.L, shape.k, shape.in_features, shape.out_features)
+        return cls(shape.axis, shape.T, shape.L, shape.k, shape.in_features, shape.out_features,
+                   shape.block_interleave)
 
 
 _vp = C.c_void_p
@@ -57,10 +60,11 @@ _lib.trellis_prefill.argtypes = [_vp, C.c_int32, _vp, _vp, _vp, _GP, _vp, C.c_si
 _lib.trellis_workspace_bytes.argtypes = [_GP, C.c_int32, C.c_int32]
 _lib.trellis_workspace_bytes.restype = C.c_size_t
 _lib.trellis_expand.argtypes = [_vp, _vp, _vp, _GP, _vp, _vp]
+_lib.trellis_repack.argtypes = [_vp, _vp, _GP, C.c_int32, _vp]
 _lib.trellis_strerror.argtypes = [C.c_int]
 _lib.trellis_strerror.restype = C.c_char_p
 for _f in ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_scatter", "trellis_prefill",
-           "trellis_expand"):
+           "trellis_expand", "trellis_repack"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -166,3 +170,14 @@ def expand(codes, scales, lut, g, w=None, stream=None) -> torch.Tensor:
     _check("trellis_expand", _lib.trellis_expand(_dev(codes), _dev(scales), _dev(lut),
                                                  C.byref(geom), _dev(w), _stream(stream)))
     return w
+
+
+def repack(codes, g, to_block_interleave: int, out=None, stream=None) -> torch.Tensor:
+    """Rewrite `codes` (in the layout g's block_interleave names) into layout
+    `to_block_interleave` (0 row-major, 2 block pairs); returns `out`."""
+    geom = _geom(g)
+    if out is None:
+        out = torch.empty_like(codes)
+    _check("trellis_repack", _lib.trellis_repack(_dev(codes), _dev(out), C.byref(geom),
+                                                 to_block_interleave, _stream(stream)))
+    return out

@@ -11,8 +11,14 @@
  *   (y = x W^T); axis 0 stores [in][out] (y = x W), the storage convention of
  *   tiled-prefill.ts's weight-tile decode.
  *
- *   Codes: uint32 words, row-major [rows][cols/T][T*k/32]. The block is a
- *   T*k-bit string, LSB-first within a word, words ascending. Weight t of a
+ *   Codes: uint32 words, T*k/32 per block, in one of two block layouts
+ *   (geometry field block_interleave):
+ *     0: row-major [rows][cols/T][T*k/32];
+ *     2: block pairs outermost, [cols/(2T)][rows][2][T*k/32]: block b of
+ *        row r starts at word (b/2)*rows*2*wpb + r*2*wpb + (b%2)*wpb
+ *        (page 60 vector-expand.ts and page 59 scatter.ts address a block
+ *        so when their INTERLEAVE constant is set); cols/T must be even.
+ *   The block is a T*k-bit string, LSB-first within a word, words ascending. Weight t of a
  *   block reads the L = 12 bits starting at bit (T-1-t)*k, wrapping to bit 0
  *   of the same block (tail-biting). That window indexes a 4096-entry float32
  *   codebook; the entry times the row's float32 scale is rounded to float32
@@ -35,8 +41,10 @@
  *     enqueued: on a negative status nothing was enqueued. A kernel fault
  *     shows up at the caller's next synchronisation.
  *   - Geometry accepted: axis in {0, 1}, T = 256, L = 12, k in {2, 3, 4},
- *     1 <= in_features, out_features <= 2^19, and cols % 256 == 0 (cols is
- *     in_features on axis 1, out_features on axis 0).
+ *     1 <= in_features, out_features <= 2^19, cols % 256 == 0 (cols is
+ *     in_features on axis 1, out_features on axis 0), block_interleave in
+ *     {0, 2}, and with 2 an even number of blocks per row (cols % 512 == 0).
+ *     Every operation gives bit-identical results for either layout.
  */
 #ifndef TRELLIS_H
 #define TRELLIS_H
@@ -58,6 +66,7 @@ typedef struct trellis_geometry {
     int32_t k;             /* bits per weight: 2, 3 or 4 */
     int32_t in_features;
     int32_t out_features;
+    int32_t block_interleave;  /* code layout: 0 row-major, 2 block pairs (see above) */
 } trellis_geometry;
 
 /* Status codes (0 = success, negative = nothing enqueued). */
@@ -68,7 +77,8 @@ enum {
     TRELLIS_ERR_ALIGN = -3,      /* a pointer is not aligned as required */
     TRELLIS_ERR_LUT = -4,        /* codebook size is not 2^L, or an entry is not finite */
     TRELLIS_ERR_WORKSPACE = -5,  /* workspace missing or smaller than trellis_workspace_bytes() */
-    TRELLIS_ERR_HIP = -6         /* the HIP runtime reported an error while enqueuing */
+    TRELLIS_ERR_HIP = -6,        /* the HIP runtime reported an error while enqueuing */
+    TRELLIS_ERR_OVERLAP = -7     /* source and destination arrays overlap */
 };
 
 /* Operation selector for trellis_workspace_bytes(). */
@@ -151,6 +161,19 @@ size_t trellis_workspace_bytes(const trellis_geometry *g, int32_t M, int32_t op)
  */
 int trellis_expand(const uint32_t *codes, const float *scales, const float *lut,
                    const trellis_geometry *g, uint16_t *w, hipStream_t stream);
+
+/*
+ * Rewrite a code array from one block layout into the other (page 60
+ * vector-expand.ts / page 59 scatter.ts INTERLEAVE addressing; a one-time
+ * conversion, not on the hot path). g describes the projection and
+ * g->block_interleave the layout of `src`; `to_block_interleave` (0 or 2)
+ * is the layout written to `dst`, which must then also satisfy the geometry
+ * rules (2 needs cols % 512 == 0). src and dst: device uint32 arrays of
+ * rows*cols*k/32 words, 16-byte aligned, not overlapping
+ * (TRELLIS_ERR_OVERLAP). Equal layouts make a plain copy.
+ */
+int trellis_repack(const uint32_t *src, uint32_t *dst, const trellis_geometry *g,
+                   int32_t to_block_interleave, hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char *trellis_strerror(int status);

@@ -58,8 +58,8 @@ def test_library_does_not_link_torch(T):
 FAKE = 0x10000  # 16-byte aligned, never dereferenced (every call below fails validation)
 
 
-def geom(T, axis=1, Tb=256, L=12, k=2, i=512, o=256):
-    return T.Geometry(axis, Tb, L, k, i, o)
+def geom(T, axis=1, Tb=256, L=12, k=2, i=512, o=256, il=0):
+    return T.Geometry(axis, Tb, L, k, i, o, il)
 
 
 def call_gemv(T, g, x=FAKE, codes=FAKE, scales=FAKE, lut=FAKE, y=FAKE):
@@ -180,5 +180,43 @@ def test_expand_validation(T):
 
 def test_strerror(T):
     for s in (T.OK, T.ERR_NULL, T.ERR_GEOMETRY, T.ERR_ALIGN, T.ERR_LUT, T.ERR_WORKSPACE,
-              T.ERR_HIP):
+              T.ERR_HIP, T.ERR_OVERLAP):
         assert T.strerror(s) and T.strerror(s) != T.strerror(-99)
+
+
+@pytest.mark.parametrize("il", [1, 3, -2, 4])
+def test_geometry_rejects_unknown_block_interleave(T, il):
+    assert call_gemv(T, geom(T, il=il)) == T.ERR_GEOMETRY
+
+
+def test_block_interleave_needs_even_block_count(T):
+    # 768 inputs = 3 blocks per row: no pair layout
+    assert call_gemv(T, geom(T, i=768, il=2)) == T.ERR_GEOMETRY
+    with pytest.raises(T.TrellisError):
+        T.workspace_bytes(geom(T, axis=0, i=300, o=768, il=2), 1, T.OP_GEMV_SCATTER)
+    # an even count is accepted, and the layout does not change the workspace
+    g0, g2 = geom(T, axis=0, i=300, o=1024), geom(T, axis=0, i=300, o=1024, il=2)
+    assert T.workspace_bytes(g2, 1, T.OP_GEMV_SCATTER) == T.workspace_bytes(g0, 1, T.OP_GEMV_SCATTER)
+
+
+def test_repack_validation(T):
+    lib = T.raw()
+
+    def rp(src, dst, g, to):
+        return lib.trellis_repack(C.c_void_p(src) if src else None, C.c_void_p(dst) if dst else None,
+                                  C.byref(g) if g is not None else None, to, C.c_void_p(0))
+
+    g = geom(T, i=1024, o=256)          # 4 blocks per row, 2048 words at k = 2
+    far = FAKE + (1 << 20)
+    assert rp(FAKE, far, None, 2) == T.ERR_NULL
+    assert rp(None, far, g, 2) == T.ERR_NULL
+    assert rp(FAKE, None, g, 2) == T.ERR_NULL
+    assert rp(FAKE + 4, far, g, 2) == T.ERR_ALIGN
+    assert rp(FAKE, far + 8, g, 2) == T.ERR_ALIGN
+    assert rp(FAKE, far, g, 1) == T.ERR_GEOMETRY
+    assert rp(FAKE, far, geom(T, i=768, o=256), 2) == T.ERR_GEOMETRY   # odd block count
+    assert rp(FAKE, far, geom(T, i=1024, o=256, il=5), 0) == T.ERR_GEOMETRY
+    # 256 rows x 1024 columns x 2 bits = 65536 bytes: any closer start overlaps
+    assert rp(FAKE, FAKE, g, 2) == T.ERR_OVERLAP
+    assert rp(FAKE, FAKE + 65536 - 16, g, 2) == T.ERR_OVERLAP
+    assert rp(FAKE + 65536 - 16, FAKE, g, 0) == T.ERR_OVERLAP
