@@ -79,11 +79,13 @@ struct A0Ctx {
 };
 
 // Issue step s's loads; every address is valid whatever s is (rows clamp to
-// the last stored row), so the loads are unconditional. With VEC (R % 8 == 0)
-// a lane's 8 rows are all stored rows or all past the end and its A fragment
-// is one aligned 16-byte load; otherwise x is read element by element with
-// the row count applied.
-template <int MT, bool VEC>
+// the last stored row), so the loads are unconditional. With VEC (R % 8 == 0,
+// scales 16-byte aligned) a lane's 8 rows are all stored rows or all past the
+// end: its A fragment is one aligned 16-byte load and, with VSC, its 8 scales
+// two (VSC is off where it measured slower: two M tiles at k = 2 then spill
+// registers); otherwise x is read element by element with the row count
+// applied.
+template <int MT, bool VEC, bool VSC>
 __device__ __forceinline__ void a0_load(A0Step<MT>& st, const A0Ctx& cx, int s) {
     const int rc = 32 * s + 8 * cx.c;
     st.rc = rc;
@@ -93,8 +95,16 @@ __device__ __forceinline__ void a0_load(A0Step<MT>& st, const A0Ctx& cx, int s) 
         const uint32_t* p = cx.cbase + static_cast<size_t>(r) * cx.row_words;
         st.a[i] = p[cx.w0];
         st.b[i] = p[cx.w1];
-        st.sc[i] = cx.scales[r];
+        if constexpr (!VSC) st.sc[i] = cx.scales[r];
     });
+    if constexpr (VSC) {
+        static_assert(VEC, "vector scales need whole 8-row chunks");
+        const int rs = rc < cx.R ? rc : cx.R - 8;
+        const floatx4 lo = *reinterpret_cast<const floatx4*>(cx.scales + rs);
+        const floatx4 hi = *reinterpret_cast<const floatx4*>(cx.scales + rs + 4);
+        st.sc[0] = lo.x; st.sc[1] = lo.y; st.sc[2] = lo.z; st.sc[3] = lo.w;
+        st.sc[4] = hi.x; st.sc[5] = hi.y; st.sc[6] = hi.z; st.sc[7] = hi.w;
+    }
     static_for<0, MT>([&](auto mc) {
         constexpr int mt = decltype(mc)::value;
         if constexpr (VEC) {
@@ -226,7 +236,8 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     fetch_table<kA0Threads, kPair>(tsrc, lut);
     asm volatile("" ::: "memory");
     A0Step<MT> sa, sb;
-    a0_load<MT, VEC>(sa, cx, s0);
+    constexpr bool kVsc = VEC && !(K == 2 && MT == 2);
+    a0_load<MT, VEC, kVsc>(sa, cx, s0);
     store_table<kA0Threads, kPair>(tsrc, tab);
     __syncthreads();
 
@@ -236,9 +247,9 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     // an odd last step is decoded after the loop.
     int s = s0;
     for (; s + 1 < s1; s += 2) {
-        a0_load<MT, VEC>(sb, cx, s + 1);
+        a0_load<MT, VEC, kVsc>(sb, cx, s + 1);
         a0_decode<K, MT, VEC>(sa, cx, sh, tab, acc);
-        a0_load<MT, VEC>(sa, cx, s + 2);
+        a0_load<MT, VEC, kVsc>(sa, cx, s + 2);
         a0_decode<K, MT, VEC>(sb, cx, sh, tab, acc);
     }
     if (s < s1) a0_decode<K, MT, VEC>(sa, cx, sh, tab, acc);
@@ -315,7 +326,7 @@ template <int K, int MT>
 hipError_t launch_axis0_v(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                           const float* scales, const float* lut, float* partial, int R, int C, int P,
                           hipStream_t st) {
-    if (R % 8 == 0)
+    if (R % 8 == 0 && reinterpret_cast<uintptr_t>(scales) % 16 == 0)
         return launch_axis0_k<K, MT, true>(x, M, codes, lay, scales, lut, partial, R, C, P, st);
     return launch_axis0_k<K, MT, false>(x, M, codes, lay, scales, lut, partial, R, C, P, st);
 }
