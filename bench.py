@@ -132,7 +132,7 @@ def gemv_bench(T, torch, dev, k, steps, warmup):
 
 
 def extra_bench(T, torch, dev, steps, warmup):
-    """Other workloads: axis-0 scatter k=3, prefill M=5/8/16/32, MLP k=4 M=1/32,
+    """Other workloads: axis-0 scatter k=3, prefill M=2/4/5/8/16/32, MLP k=4 M=1/32,
     and the scatter and the k=2 GEMV on block-interleave-2 codes (the same
     uniform random words, read in the pair layout)."""
     from dequant_gemm_trellis_amd import synth
@@ -167,7 +167,7 @@ def extra_bench(T, torch, dev, steps, warmup):
     for k in (2, 3, 4):
         sh = synth.Shape(1, 256, 12, k, QWEN_IN, QWEN_OUT)
         cb = sh.rows * sh.words_per_row * 4
-        for M in (5, 8, 16, 32):
+        for M in (2, 4, 5, 8, 16, 32):
             sets = Sets(sh, M, C["qwen_up_prefill"], n_sets_for(cb), T, torch, dev)
             y = torch.empty((M, QWEN_OUT), dtype=torch.bfloat16, device=dev)
             g = T.Geometry.of(sh)

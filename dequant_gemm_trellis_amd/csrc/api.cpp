@@ -66,14 +66,18 @@ size_t axis0_workspace(const Dims& d, int M) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? TRELLIS_OK : TRELLIS_ERR_HIP; }
 
-// Axis-1, one activation row: the persistent GEMV kernel stages the whole
-// activation vector in LDS; rows too long for that take the general axis-1
-// kernel with M = 1.
-hipError_t launch_axis1_m1(const uint16_t* x, const uint32_t* codes, const float* scales,
-                           const float* lut, uint16_t* y, const Dims& d, int k, hipStream_t st) {
-    if (d.nb <= trellis::gemv_max_blocks(k))
+// Axis 1, M activation rows. M = 1: the persistent GEMV kernel, which stages
+// the whole activation vector in LDS. Up to 8 rows (and single rows too long
+// for that staging): the GEMV's unit mapping with M outputs per unit, when
+// the workgroups own at least 16 rows whose partials fit in LDS. Otherwise
+// the tiled kernel of 16-row groups.
+hipError_t launch_axis1_any(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
+                            const float* lut, uint16_t* y, const Dims& d, int k, hipStream_t st) {
+    if (M == 1 && d.nb <= trellis::gemv_max_blocks(k))
         return trellis::launch_gemv(x, codes, d.lay, scales, lut, y, d.rows, d.nb, k, st);
-    return trellis::launch_axis1(x, 1, codes, d.lay, scales, lut, y, d.rows, d.nb, k, st);
+    if (trellis::gemv_rows_supported(M, d.rows, d.nb, k))
+        return trellis::launch_gemv_rows(x, M, codes, d.lay, scales, lut, y, d.rows, d.nb, k, st);
+    return trellis::launch_axis1(x, M, codes, d.lay, scales, lut, y, d.rows, d.nb, k, st);
 }
 
 }  // namespace
@@ -99,7 +103,7 @@ int trellis_gemv(const uint16_t* x, const uint32_t* codes, const float* scales, 
     if (st) return st;
     if (g->axis != 1) return TRELLIS_ERR_GEOMETRY;
     if ((st = check_operands(codes, scales, lut)) || (st = check_io(x, y))) return st;
-    return status_of(launch_axis1_m1(x, codes, scales, lut, y, d, g->k, stream));
+    return status_of(launch_axis1_any(x, 1, codes, scales, lut, y, d, g->k, stream));
 }
 
 int trellis_gemv_scatter(const uint16_t* x, const uint32_t* codes, const float* scales,
@@ -126,11 +130,7 @@ int trellis_prefill(const uint16_t* x, int32_t M, const uint32_t* codes, const f
     if (M < 0 || M > TRELLIS_MAX_M) return TRELLIS_ERR_GEOMETRY;
     if (M == 0) return TRELLIS_OK;
     if ((st = check_operands(codes, scales, lut)) || (st = check_io(x, y))) return st;
-    if (g->axis == 1 && M == 1)
-        return status_of(launch_axis1_m1(x, codes, scales, lut, y, d, g->k, stream));
-    if (g->axis == 1)
-        return status_of(trellis::launch_axis1(x, M, codes, d.lay, scales, lut, y, d.rows, d.nb, g->k,
-                                               stream));
+    if (g->axis == 1) return status_of(launch_axis1_any(x, M, codes, scales, lut, y, d, g->k, stream));
     if (!workspace) return TRELLIS_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return TRELLIS_ERR_ALIGN;
     if (workspace_bytes < axis0_workspace(d, M)) return TRELLIS_ERR_WORKSPACE;

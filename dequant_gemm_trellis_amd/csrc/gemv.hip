@@ -284,6 +284,230 @@ hipError_t launch_gemv_k(const uint16_t* x, const uint32_t* codes, CodeLayout la
                          y, lay, N, nb);
 }
 
+// ---------------------------------------------------------------------------
+// Several activation rows, 1 <= M <= 8, in the GEMV's work mapping (the
+// M-row counterpart of wide-prefill.ts's multi-vector GEMV on page 60).
+//
+// Units, steps, the code prefetch and the decode are those of gemv_kernel;
+// only the multiply differs. Lane l = 16 c + j still decodes run c of the
+// step's unit j into B fragments, but the A fragment of lane (c, m = j) now
+// holds activation row m (rows m >= M repeat row M - 1) at the run-c
+// positions of a block, so D[m][j] of the 16x16 tile is row m against unit j:
+// the MFMA yields M outputs per unit instead of one diagonal entry. A holds
+// one block, so a step whose 16 units straddle a block edge (workgroups own
+// at least 16 rows, so at most two blocks) multiplies again with the next
+// block's fragments and each lane keeps the product of its own unit's block.
+// Unlike tiled-prefill.ts-style 16-row tasks, no row slots are left empty
+// when a workgroup's row count is not a multiple of 16.
+//
+// Each unit's M partials go to LDS in unit order, M rounded up to 4 or 8
+// (lane (c, j) stores D[4c .. 4c + 3][j], one 16-byte write); each output is
+// the sum of its row's block partials in ascending block order. Rows are
+// split into equal chunks whose partials fit beside the table. Activation
+// fragments are loaded straight from global memory in A layout (M x 4 cache
+// lines per instruction), one block ahead of use: xf holds the step's first
+// block, xn the next one.
+// Chunks for a workgroup of `rows` rows when at most `max_rows` rows' partials
+// fit: the fewest balanced chunks, or 0 if one would hold fewer than 16 rows.
+__host__ __device__ inline int rows_chunks(int rows, int max_rows) {
+    if (max_rows < 16 || rows < 16) return 0;
+    const int n = (rows + max_rows - 1) / max_rows;
+    return rows / n >= 16 ? n : 0;
+}
+
+template <int K>
+struct RowsLds {
+    static constexpr bool pair = K == 2;
+    static constexpr int tab_floats = pair ? 2 * kPairEntries : kLutEntries;
+    static constexpr int part_floats = pair ? 7936 : 32768;  // the rest of 160 KB
+};
+
+// Activation fragments of block b in A layout from xa (row m = j, column 64 c).
+__device__ __forceinline__ void load_xa(XFrag& xn, const uint16_t* xa, uint32_t b) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(xa + b * kT);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) xn.v[s] = p[s];
+}
+
+// The same through an opaque global-address-space pointer, for the prologue
+// (through the restrict kernel pointer the loads would be sunk to first use).
+__device__ __forceinline__ void load_xa_opaque(XFrag& xn, const uint16_t* xa, uint32_t b) {
+    using gu32x4 = const __attribute__((address_space(1))) u32x4*;
+    gu32x4 p = (gu32x4)(xa + b * kT);
+    asm volatile("" : "+v"(p));
+#pragma unroll
+    for (int s = 0; s < 8; ++s) xn.v[s] = p[s];
+}
+
+// One step of 16 units: eight fragments, gathers two ahead as in run_step.
+// STRAD: the step's units reach into block blo + 1, multiplied against xn.
+template <int K, bool STRAD>
+__device__ __forceinline__ void run_rows_step(Step<K> st, const XFrag& xf, const XFrag& xn,
+                                              uint32_t blo, const float* __restrict__ tab,
+                                              float* __restrict__ part, int u, int u_end, int c,
+                                              int m4) {
+    constexpr bool P = RowsLds<K>::pair;
+    constexpr int D = GemvLds<K>::depth;
+    st.w[2 * K] = next_run_word(st.w[0]);
+    floatx4 d1 = {0.f, 0.f, 0.f, 0.f}, d2 = {0.f, 0.f, 0.f, 0.f};
+    Gathered<P> g[8];
+    static_for<0, D>([&](auto ic) {
+        constexpr int S = 7 - decltype(ic)::value;
+        g[S] = gather_run64<K, S, P>(st.w, tab);
+    });
+    static_for<0, 8>([&](auto ic) {
+        constexpr int S = 7 - decltype(ic)::value;
+        if constexpr (S >= D) g[S - D] = gather_run64<K, S - D, P>(st.w, tab);
+        const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g[S], st.scale));
+        d1 = mfma16x16x32(as_bf16x8(xf.v[S]), bfrag, d1);
+        if constexpr (STRAD) d2 = mfma16x16x32(as_bf16x8(xn.v[S]), bfrag, d2);
+    });
+    if constexpr (STRAD) {
+        if (st.b != blo) d1 = d2;
+    }
+    if (4 * c < m4 && u < u_end) *reinterpret_cast<floatx4*>(part + u * m4 + 4 * c) = d1;
+}
+
+template <int K, bool PAIRS>
+__global__ __launch_bounds__(kThreads) void gemv_rows_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
+    const float* __restrict__ scales, const float* __restrict__ lut,
+    uint16_t* __restrict__ y, CodeLayout lay, int N, int nb, int M) {
+    using Lds = RowsLds<K>;
+    __shared__ __attribute__((aligned(16))) float lds[Lds::tab_floats + Lds::part_floats];
+    float* const tab = lds;
+    float* const part = lds + Lds::tab_floats;
+
+    const int G = gridDim.x, g = blockIdx.x;
+    const int r0 = static_cast<int>(static_cast<long>(g) * N / G);
+    const int r1 = static_cast<int>(static_cast<long>(g + 1) * N / G);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, c = lane >> 4;
+    const int m4 = M > 4 ? 8 : 4;
+    // Balanced row chunks whose unit partials fit; chunk q is rows
+    // [r0 + q rows / n, r0 + (q + 1) rows / n). The launcher guarantees at
+    // least 16 rows per chunk (rows_chunks).
+    const int rows = r1 - r0;
+    const int nchunks = rows_chunks(rows, Lds::part_floats / (m4 * nb));
+    const long in = static_cast<long>(nb) * kT;
+    const uint16_t* const xa = x + (j < M ? j : M - 1) * in + 64 * c;
+
+    Ctx cx{codes + static_cast<size_t>(r0) * lay.row_words, lay, scales + r0, nb, 1, 0u, 3 - c};
+    Step<K> sa, sb, sc;
+    XFrag xf, xn;
+    // Prologue: the table sources first, then the first two steps' code words
+    // and the first two blocks' activation fragments (all unconditional), so
+    // the table stores wait only for their own data.
+    constexpr bool kPair = Lds::pair;
+    TableSrc<kThreads, kPair> tsrc;
+    fetch_table<kThreads, kPair>(tsrc, lut);
+    asm volatile("" ::: "memory");
+    int CR = rows / nchunks, U = CR * nb;
+    int ub = wave * U / kWaves, ue = (wave + 1) * U / kWaves;
+    cx.cr = CR;
+    cx.magic = div_magic(CR);
+    uint32_t xb = static_cast<uint32_t>((ub < U ? ub : U - 1) / CR);
+    load_step<K, PAIRS>(sa, cx, ub + j, ue > 1 ? ue : 1);
+    load_step<K, PAIRS>(sb, cx, ub + 16 + j, ue > 1 ? ue : 1);
+    load_xa_opaque(xf, xa, xb);
+    load_xa_opaque(xn, xa, xb + 1 < static_cast<uint32_t>(nb) ? xb + 1 : xb);
+    asm volatile("" ::: "memory");
+    store_table<kThreads, kPair>(tsrc, tab);
+    __syncthreads();
+
+    for (int q = 0; q < nchunks; ++q) {
+        const int cr0 = r0 + q * rows / nchunks;
+        CR = r0 + (q + 1) * rows / nchunks - cr0;
+        U = CR * nb;
+        ub = wave * U / kWaves;
+        ue = (wave + 1) * U / kWaves;
+        if (cr0 != r0 && ue > ub) {
+            cx.codes = codes + static_cast<size_t>(cr0) * lay.row_words;
+            cx.scales = scales + cr0;
+            cx.cr = CR;
+            cx.magic = div_magic(CR);
+            load_step<K, PAIRS>(sa, cx, ub + j, ue);
+            load_step<K, PAIRS>(sb, cx, ub + 16 + j, ue);
+            xb = static_cast<uint32_t>(ub / CR);
+            load_xa(xf, xa, xb);
+            load_xa(xn, xa, xb + 1 < static_cast<uint32_t>(nb) ? xb + 1 : xb);
+        }
+        // One step: advance the activation blocks when the step starts in the
+        // next block (steps move at most one block on: CR >= 16), then decode
+        // and multiply, twice if the step reaches into the block after.
+        auto step = [&](const Step<K>& st, int u0) {
+            const uint32_t blo = static_cast<uint32_t>(u0 / CR);
+            const int ulast = (u0 + 15 < ue ? u0 + 15 : ue - 1);
+            const bool strad = static_cast<uint32_t>(ulast / CR) != blo;
+            if (blo != xb) {
+                xb = blo;
+                xf = xn;
+                load_xa(xn, xa, blo + 1 < static_cast<uint32_t>(nb) ? blo + 1 : blo);
+            }
+            // k = 3, 4: the second multiply on every step measured 1-2% faster
+            // than a branch (the compiler hoists the branch's common gathers
+            // and waits for all of them at it); k = 2: the branch.
+            if constexpr (K != 2) {
+                (void)strad;
+                run_rows_step<K, true>(st, xf, xn, blo, tab, part, u0 + j, ue, c, m4);
+            } else if (strad) {
+                run_rows_step<K, true>(st, xf, xn, blo, tab, part, u0 + j, ue, c, m4);
+            } else {
+                run_rows_step<K, false>(st, xf, xn, blo, tab, part, u0 + j, ue, c, m4);
+            }
+        };
+        // Three register sets rotate as in gemv_kernel; every load is
+        // unconditional, only the steps are guarded.
+        for (int u0 = ub; u0 < ue; u0 += 48) {
+            load_step<K, PAIRS>(sc, cx, u0 + 32 + j, ue);
+            step(sa, u0);
+            load_step<K, PAIRS>(sa, cx, u0 + 48 + j, ue);
+            if (u0 + 16 < ue) step(sb, u0 + 16);
+            load_step<K, PAIRS>(sb, cx, u0 + 64 + j, ue);
+            if (u0 + 32 < ue) step(sc, u0 + 32);
+        }
+        __syncthreads();
+        // y[m][row] = sum over blocks, ascending, of the unit partials.
+        for (int o = tid; o < CR * M; o += kThreads) {
+            const int m = o / CR, rl = o - m * CR;
+            const float* pr = part + rl * m4 + m;
+            const int bstride = CR * m4;
+            float s = 0.f;
+            int bq = 0;
+            for (; bq + 8 <= nb; bq += 8) {  // reads issued together, added in order
+                float v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = pr[(bq + i) * bstride];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s += v[i];
+            }
+            for (; bq < nb; ++bq) s += pr[bq * bstride];
+            y[static_cast<size_t>(m) * N + cr0 + rl] = round_bf16(s);
+        }
+        __syncthreads();
+    }
+}
+
+// One workgroup per compute unit, but at least 16 rows each, so a step's 16
+// units span at most two blocks.
+int rows_grid(int N) {
+    const int G = N / 16 < cu_count() ? N / 16 : cu_count();
+    return G < 1 ? 1 : G;
+}
+
+template <int K>
+hipError_t launch_gemv_rows_k(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
+                              const float* scales, const float* lut, uint16_t* y, int N, int nb,
+                              hipStream_t st) {
+    const int G = rows_grid(N);
+    if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
+        return launch_kernel(gemv_rows_kernel<K, false>, dim3(G), dim3(kThreads), st, x, codes,
+                             scales, lut, y, lay, N, nb, M);
+    return launch_kernel(gemv_rows_kernel<K, true>, dim3(G), dim3(kThreads), st, x, codes, scales,
+                         lut, y, lay, N, nb, M);
+}
+
 }  // namespace
 
 int cu_count() {
@@ -310,6 +534,31 @@ hipError_t launch_gemv(const uint16_t* x, const uint32_t* codes, CodeLayout lay,
     case 2: return launch_gemv_k<2>(x, codes, lay, scales, lut, y, N, nb, st);
     case 3: return launch_gemv_k<3>(x, codes, lay, scales, lut, y, N, nb, st);
     case 4: return launch_gemv_k<4>(x, codes, lay, scales, lut, y, N, nb, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool gemv_rows_supported(int M, int N, int nb, int k) {
+    if (M < 1 || M > kGemvRowsMaxM || N < 16 || nb < 1) return false;
+    // k = 2 beyond 4 rows: beside the 128 KB pair table only about 49 rows'
+    // partials of 8 floats fit at 5120 inputs, and the second chunk (pipeline
+    // restart, a second epilogue, a block edge every other step) measured
+    // 14-21% slower than the 16-row-group kernel.
+    if (k == 2 && M > 4) return false;
+    const int m4 = M > 4 ? 8 : 4;
+    const int max_rows = (k == 2 ? RowsLds<2>::part_floats : RowsLds<4>::part_floats) / (m4 * nb);
+    const int G = rows_grid(N);
+    // workgroups own floor(N / G) or ceil(N / G) rows
+    return rows_chunks(N / G, max_rows) > 0 && rows_chunks((N + G - 1) / G, max_rows) > 0;
+}
+
+hipError_t launch_gemv_rows(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
+                            const float* scales, const float* lut, uint16_t* y, int N, int nb,
+                            int k, hipStream_t st) {
+    switch (k) {
+    case 2: return launch_gemv_rows_k<2>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    case 3: return launch_gemv_rows_k<3>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    case 4: return launch_gemv_rows_k<4>(x, M, codes, lay, scales, lut, y, N, nb, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -45,6 +45,16 @@ hipError_t launch_gemv(const uint16_t* x, const uint32_t* codes, CodeLayout lay,
                        const float* lut, uint16_t* y, int N, int nb, int k, hipStream_t st);
 int gemv_max_blocks(int k);
 
+// Axis 1, 1 <= M <= kGemvRowsMaxM, in the GEMV's unit mapping (one workgroup
+// per compute unit, at least 16 rows each); gemv_rows_supported says whether
+// the geometry fits it (at least 16 rows, 16 rows' unit partials fit in LDS)
+// and it measured faster than launch_axis1 there (k = 2 only up to M = 4).
+constexpr int kGemvRowsMaxM = 8;
+bool gemv_rows_supported(int M, int N, int nb, int k);
+hipError_t launch_gemv_rows(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
+                            const float* scales, const float* lut, uint16_t* y, int N, int nb,
+                            int k, hipStream_t st);
+
 // Axis 1, 1 <= M <= 32: y[M][N] from x[M][nb*256] and codes [N][nb][8k].
 // Persistent workgroups of at most 80 rows; any nb.
 hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,

@@ -51,8 +51,13 @@ def test_library_exports_every_declared_symbol(T):
 
 
 def test_library_does_not_link_torch(T):
-    out = subprocess.run(["ldd", LIB], capture_output=True, text=True).stdout
-    assert "torch" not in out and "c10" not in out
+    """The library's own link dependencies (DT_NEEDED), independent of the
+    environment's library search path."""
+    r = subprocess.run(["readelf", "-d", LIB], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    needed = re.findall(r"\(NEEDED\)\s+Shared library: \[([^\]]+)\]", r.stdout)
+    assert needed, r.stdout
+    assert not [n for n in needed if "torch" in n or "c10" in n], needed
 
 
 FAKE = 0x10000  # 16-byte aligned, never dereferenced (every call below fails validation)

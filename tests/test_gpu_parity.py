@@ -286,6 +286,63 @@ def test_prefill_one_hot_rows_bit_exact(gpu_lib):
         assert np.array_equal(y[m, SAMPLE_ROWS], W[:, c]), (m, c)
 
 
+# ------------------------------------- axis 1, up to 8 rows in the GEMV's unit mapping
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("N", [16, 31, 300, 4111])
+@pytest.mark.parametrize("M", [2, 4, 5, 8])
+def test_rows_kernel_ragged(gpu_lib, N, M, k):
+    """Up to 8 activation rows (4 at k = 2) take the GEMV's unit mapping with
+    M outputs per unit: one workgroup of exactly 16 rows, one of 31,
+    workgroups of 16-17 rows (a step can straddle a block edge right after
+    entering a block), and 4111 rows over every compute unit. k = 2 with more
+    than 4 rows takes the 16-row-group kernel."""
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, k, 1024, N)
+    p = synth.make_problem(shape, M, CFG["test"], proj=700 + M)
+    say(f"rows kernel in=1024 out={N} M={M} k={k}")
+    y = bf16_to_f64(run(T, Dev(p, T)))
+    assert gate(y, oracle_y(p)) <= TOL
+
+
+def test_rows_kernel_two_chunks_k4(gpu_lib):
+    """Rows of 128 blocks at M = 6: 32 rows' partials fit beside the codebook,
+    so 34-row workgroups run two chunks of 17 rows."""
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, 4, 32768, 8704)
+    p = synth.make_problem(shape, 6, CFG["test"], proj=710)
+    say("rows kernel in=32768 out=8704 M=6 k=4")
+    y = bf16_to_f64(run(T, Dev(p, T)))
+    rows = np.concatenate([np.arange(0, 40), np.arange(4340, 4380), np.arange(8664, 8704)])
+    assert gate(y[:, rows], oracle_y(row_subset(p, rows))) <= TOL
+
+
+def test_rows_kernel_falls_back_when_partials_do_not_fit(gpu_lib):
+    """64 blocks per row at M = 8, k = 2: fewer than 16 rows' partials fit
+    beside the pair table, so the call takes the 16-row-group kernel."""
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, 2, 16384, 300)
+    p = synth.make_problem(shape, 8, CFG["test"], proj=720)
+    say("rows kernel fallback in=16384 out=300 M=8 k=2")
+    y = bf16_to_f64(run(T, Dev(p, T)))
+    assert gate(y, oracle_y(p)) <= TOL
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_rows_kernel_one_hot_bit_exact(gpu_lib, k):
+    """Eight one-hot activation rows at the Qwen-up shape: each output row is
+    one stored column exactly."""
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, k, QWEN_IN, QWEN_OUT)
+    cols = [0, 255, 256, 2047, 2048, 4095, 5119, 1000]
+    p0 = synth.make_problem(shape, 8, CFG["qwen_up_prefill"], proj=730)
+    p = with_x(p0, synth.one_hot_x(8, QWEN_IN, cols))
+    say(f"rows kernel one-hot M=8 k={k}")
+    y = bf16_bits(run(T, Dev(p, T)))
+    W = oracle_W(row_subset(p, SAMPLE_ROWS))
+    for m, c in enumerate(cols):
+        assert np.array_equal(y[m, SAMPLE_ROWS], W[:, c]), (m, c)
+
+
 @pytest.mark.parametrize("M", [5, 8, 32])
 def test_prefill_axis0_qwen_down_sampled(gpu_lib, M):
     T = gpu_lib
