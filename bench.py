@@ -131,13 +131,58 @@ def gemv_bench(T, torch, dev, k, steps, warmup):
     return res, first
 
 
-def extra_bench(T, torch, dev, steps, warmup):
+def extra_bench(T, torch, dev, steps, warmup, only=None):
     """Other workloads: axis-0 scatter k=3, prefill M=2/4/5/8/16/32, MLP k=4 M=1/32,
     and the scatter and the k=2 GEMV on block-interleave-2 codes (the same
     uniform random words, read in the pair layout)."""
     from dequant_gemm_trellis_amd import synth
 
     out = {}
+    C = synth.CONFIG_IDS
+
+    def want(*names):
+        return only is None or any(n in only for n in names)
+
+    if want("scatter_qwen_down_k3", "scatter_qwen_down_k3_interleave2"):
+        scatter_bench(T, torch, dev, steps, warmup, only, out)
+    if want("gemv_qwen_up_k2_interleave2"):
+        sh = synth.Shape(1, 256, 12, 2, QWEN_IN, QWEN_OUT, 2)
+        cb = sh.rows * sh.words_per_row * 4
+        sets = Sets(sh, 1, C["qwen_up_gemv"], n_sets_for(cb), T, torch, dev)
+        y = torch.empty(QWEN_OUT, dtype=torch.bfloat16, device=dev)
+        g2 = T.Geometry.of(sh)
+        ms = time_calls(torch, lambda i: T.gemv(*sets.items[i], g2, y=y), len(sets.items), steps,
+                        warmup)
+        out["gemv_qwen_up_k2_interleave2"] = {"us_per_call": ms * 1e3,
+                                              "gbps": cb / (ms * 1e-3) / 1e9}
+        del sets
+    for k in (2, 3, 4):
+        sh = synth.Shape(1, 256, 12, k, QWEN_IN, QWEN_OUT)
+        cb = sh.rows * sh.words_per_row * 4
+        for M in (2, 4, 5, 8, 16, 32):
+            name = f"prefill_qwen_up_k{k}_M{M}"
+            if not want(name):
+                continue
+            sets = Sets(sh, M, C["qwen_up_prefill"], n_sets_for(cb), T, torch, dev)
+            y = torch.empty((M, QWEN_OUT), dtype=torch.bfloat16, device=dev)
+            g = T.Geometry.of(sh)
+            ms = time_calls(torch, lambda i: T.prefill(*sets.items[i], g, y=y),
+                            len(sets.items), steps, warmup)
+            flops = 2.0 * M * QWEN_IN * QWEN_OUT
+            out[name] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9,
+                         "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+            del sets
+    for M in (1, 32):
+        if want(f"mlp_k4_M{M}"):
+            mlp_bench(T, torch, dev, M, steps, warmup, out)
+    torch.cuda.empty_cache()
+    return out
+
+
+def scatter_bench(T, torch, dev, steps, warmup, only, out):
+    """Axis-0 scatter k=3, on row-major and on block-interleave-2 codes."""
+    from dequant_gemm_trellis_amd import synth
+
     C = synth.CONFIG_IDS
     sh = synth.Shape(0, 256, 12, 3, QWEN_OUT, QWEN_IN)
     cb = sh.rows * sh.words_per_row * 4
@@ -155,61 +200,42 @@ def extra_bench(T, torch, dev, steps, warmup):
     out["scatter_qwen_down_k3_interleave2"] = {"us_per_call": ms * 1e3,
                                                "gbps": cb / (ms * 1e-3) / 1e9}
     del sets
-    sh = synth.Shape(1, 256, 12, 2, QWEN_IN, QWEN_OUT, 2)
-    cb = sh.rows * sh.words_per_row * 4
-    sets = Sets(sh, 1, C["qwen_up_gemv"], n_sets_for(cb), T, torch, dev)
-    y = torch.empty(QWEN_OUT, dtype=torch.bfloat16, device=dev)
-    g2 = T.Geometry.of(sh)
-    ms = time_calls(torch, lambda i: T.gemv(*sets.items[i], g2, y=y), len(sets.items), steps,
-                    warmup)
-    out["gemv_qwen_up_k2_interleave2"] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
-    del sets
-    for k in (2, 3, 4):
-        sh = synth.Shape(1, 256, 12, k, QWEN_IN, QWEN_OUT)
-        cb = sh.rows * sh.words_per_row * 4
-        for M in (2, 4, 5, 8, 16, 32):
-            sets = Sets(sh, M, C["qwen_up_prefill"], n_sets_for(cb), T, torch, dev)
-            y = torch.empty((M, QWEN_OUT), dtype=torch.bfloat16, device=dev)
-            g = T.Geometry.of(sh)
-            ms = time_calls(torch, lambda i: T.prefill(*sets.items[i], g, y=y),
-                            len(sets.items), steps, warmup)
-            flops = 2.0 * M * QWEN_IN * QWEN_OUT
-            out[f"prefill_qwen_up_k{k}_M{M}"] = {
-                "us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9,
-                "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
-            del sets
-    for M in (1, 32):
-        shapes = [synth.Shape(1, 256, 12, 4, QWEN_IN, QWEN_OUT),
-                  synth.Shape(1, 256, 12, 4, QWEN_IN, QWEN_OUT),
-                  synth.Shape(0, 256, 12, 4, QWEN_OUT, QWEN_IN)]
-        cb = 3 * shapes[0].rows * shapes[0].words_per_row * 4
-        n = n_sets_for(cb)
-        projs = [Sets(s, M, C["qwen_mlp"], n, T, torch, dev, proj0=10 * j)
-                 for j, s in enumerate(shapes)]
-        geoms = [T.Geometry.of(s) for s in shapes]
-        ys = [torch.empty((M, s.out_features), dtype=torch.bfloat16, device=dev) for s in shapes]
-        ws = torch.empty(max(T.workspace_bytes(shapes[2], M, T.OP_PREFILL), 16) // 4,
-                         dtype=torch.float32, device=dev)
 
-        def mlp(i):
-            for j in range(3):
-                x, codes, scales, lut = projs[j].items[i]
-                if M == 1:
-                    if j < 2:
-                        T.gemv(x, codes, scales, lut, geoms[j], y=ys[j].reshape(-1))
-                    else:
-                        T.gemv_scatter(x, codes, scales, lut, geoms[j],
-                                       workspace=ws[: T.workspace_bytes(shapes[2], 1,
-                                                                        T.OP_GEMV_SCATTER) // 4],
-                                       y=ys[j].reshape(-1))
+
+def mlp_bench(T, torch, dev, M, steps, warmup, out):
+    """The MLP workload: gate and up (axis 1) then down (axis 0), k=4."""
+    from dequant_gemm_trellis_amd import synth
+
+    C = synth.CONFIG_IDS
+    shapes = [synth.Shape(1, 256, 12, 4, QWEN_IN, QWEN_OUT),
+              synth.Shape(1, 256, 12, 4, QWEN_IN, QWEN_OUT),
+              synth.Shape(0, 256, 12, 4, QWEN_OUT, QWEN_IN)]
+    cb = 3 * shapes[0].rows * shapes[0].words_per_row * 4
+    n = n_sets_for(cb)
+    projs = [Sets(s, M, C["qwen_mlp"], n, T, torch, dev, proj0=10 * j)
+             for j, s in enumerate(shapes)]
+    geoms = [T.Geometry.of(s) for s in shapes]
+    ys = [torch.empty((M, s.out_features), dtype=torch.bfloat16, device=dev) for s in shapes]
+    ws = torch.empty(max(T.workspace_bytes(shapes[2], M, T.OP_PREFILL), 16) // 4,
+                     dtype=torch.float32, device=dev)
+
+    def mlp(i):
+        for j in range(3):
+            x, codes, scales, lut = projs[j].items[i]
+            if M == 1:
+                if j < 2:
+                    T.gemv(x, codes, scales, lut, geoms[j], y=ys[j].reshape(-1))
                 else:
-                    T.prefill(x, codes, scales, lut, geoms[j], workspace=ws, y=ys[j])
+                    T.gemv_scatter(x, codes, scales, lut, geoms[j],
+                                   workspace=ws[: T.workspace_bytes(shapes[2], 1,
+                                                                    T.OP_GEMV_SCATTER) // 4],
+                                   y=ys[j].reshape(-1))
+            else:
+                T.prefill(x, codes, scales, lut, geoms[j], workspace=ws, y=ys[j])
 
-        ms = time_calls(torch, mlp, n, max(steps // 3, 10), warmup)
-        out[f"mlp_k4_M{M}"] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
-        del projs
-    torch.cuda.empty_cache()
-    return out
+    ms = time_calls(torch, mlp, n, max(steps // 3, 10), warmup)
+    out[f"mlp_k4_M{M}"] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
+    del projs
 
 
 def cpu_baseline(p, seconds: float):
@@ -260,6 +286,9 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only-k", type=int, default=0, help="time only this k (profiling runs)")
+    ap.add_argument("--only-extra", default="",
+                    help="comma-separated extra workload names to time (implies --extra; "
+                         "profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain device copy of 512 MiB (scales the FETCH_SIZE/WRITE_SIZE "
                          "counters of the traffic figure) and exit")
@@ -304,9 +333,10 @@ def main() -> int:
     head = per_k.get("2") or next(iter(per_k.values()))
 
     extra = None
-    if args.extra:
+    if args.extra or args.only_extra:
         log("bench: extra workloads")
-        extra = extra_bench(T, torch, dev, max(args.steps // 4, 20), 10)
+        extra = extra_bench(T, torch, dev, max(args.steps // 4, 20), 10,
+                            only=set(args.only_extra.split(",")) if args.only_extra else None)
 
     cpu = None
     if not args.no_cpu and first is not None:

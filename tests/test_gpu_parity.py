@@ -304,6 +304,25 @@ def test_rows_kernel_ragged(gpu_lib, N, M, k):
     assert gate(y, oracle_y(p)) <= TOL
 
 
+@pytest.mark.parametrize("i", [256, 512])
+@pytest.mark.parametrize("M", [3, 7])
+def test_rows_kernel_one_or_two_blocks_per_row(gpu_lib, i, M):
+    """One block per row (no step can straddle) and two (the interleaved
+    layout coincides with the row-major one)."""
+    T = gpu_lib
+    k = 3
+    for il in (0, 2):
+        if il and i // 256 % 2:
+            continue
+        shape = synth.Shape(1, 256, L, k, i, 300, il)
+        p = synth.make_problem(shape, M, CFG["test"], proj=740 + M)
+        say(f"rows kernel in={i} out=300 M={M} k={k} interleave={il}")
+        y = bf16_to_f64(run(T, Dev(p, T)))
+        ref = oracle.fused_f64(p.x, p.codes, p.scales, p.lut, 1, 256, L, k, i, 300,
+                               block_interleave=il)
+        assert gate(y, ref) <= TOL
+
+
 def test_rows_kernel_two_chunks_k4(gpu_lib):
     """Rows of 128 blocks at M = 6: 32 rows' partials fit beside the codebook,
     so 34-row workgroups run two chunks of 17 rows."""
