@@ -132,7 +132,8 @@ def gemv_bench(T, torch, dev, k, steps, warmup):
 
 
 def extra_bench(T, torch, dev, steps, warmup, only=None):
-    """Other workloads: axis-0 scatter k=3, prefill M=2/4/5/8/16/32, MLP k=4 M=1/32,
+    """Other workloads: axis-0 scatter k=3 (and its geometry at M=2/4/8), prefill
+    M=2/4/5/8/16/32, MLP k=4 M=1/32,
     and the scatter and the k=2 GEMV on block-interleave-2 codes (the same
     uniform random words, read in the pair layout)."""
     from dequant_gemm_trellis_amd import synth
@@ -172,6 +173,22 @@ def extra_bench(T, torch, dev, steps, warmup, only=None):
             out[name] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9,
                          "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
             del sets
+    # axis 0 at the scatter's geometry with several activation rows (decode once per row set)
+    sh = synth.Shape(0, 256, 12, 3, QWEN_OUT, QWEN_IN)
+    cb = sh.rows * sh.words_per_row * 4
+    for M in (2, 4, 8):
+        name = f"prefill_qwen_down_k3_M{M}"
+        if not want(name):
+            continue
+        sets = Sets(sh, M, C["qwen_down_scatter"], n_sets_for(cb), T, torch, dev)
+        y = torch.empty((M, QWEN_IN), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(T.workspace_bytes(sh, M, T.OP_PREFILL) // 4, dtype=torch.float32,
+                         device=dev)
+        g = T.Geometry.of(sh)
+        ms = time_calls(torch, lambda i: T.prefill(*sets.items[i], g, workspace=ws, y=y),
+                        len(sets.items), steps, warmup)
+        out[name] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
+        del sets
     for M in (1, 32):
         if want(f"mlp_k4_M{M}"):
             mlp_bench(T, torch, dev, M, steps, warmup, out)
