@@ -401,6 +401,55 @@ def test_prefill_deterministic(gpu_lib):
     assert np.array_equal(bf16_bits(run(T, d)), bf16_bits(run(T, d)))
 
 
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("axis,M", [(1, 3), (1, 6), (1, 12), (1, 24), (0, 1), (0, 4), (0, 20)])
+def test_prefill_integer_codebook_bit_exact(gpu_lib, axis, M, k):
+    """Integer codebook, scales in {0.5, 1, 2}, integer activations: every
+    partial sum is exact in float32, so the bf16 output is unique whatever the
+    summation order. Covers each axis-1 path (the GEMV-mapped kernel, directly
+    loaded and LDS-staged activations, two M tiles) and axis 0."""
+    T = gpu_lib
+    shape = synth.Shape(axis, 256, L, k, 1024 if axis else 1000, 600 if axis else 512)
+    g = np.random.default_rng(50 + 10 * M + k + axis)
+    p0 = synth.make_problem(shape, M, CFG["test"], proj=800 + M)
+    xi = g.integers(-3, 4, (M, shape.in_features)).astype(np.float32)
+    p = synth.Problem(shape, M, p0.codes, synth.integer_lut(),
+                      g.choice(np.array([0.5, 1.0, 2.0], np.float32), shape.rows),
+                      synth.to_bf16_bits(xi))
+    say(f"prefill integer codebook axis={axis} M={M} k={k}")
+    y = bf16_bits(run(T, Dev(p, T)))
+    exact = oracle_y(p)
+    assert np.all(np.abs(exact) < 2**24)
+    assert np.array_equal(y, synth.to_bf16_bits(exact.astype(np.float32)))
+
+
+@pytest.mark.parametrize("axis,M,k", [(1, 4, 2), (1, 7, 3), (0, 8, 3)])
+def test_small_batch_deterministic(gpu_lib, axis, M, k):
+    """The GEMV-mapped axis-1 kernel and the axis-0 prefill give the same bits
+    on repeated calls."""
+    T = gpu_lib
+    shape = (synth.Shape(1, 256, L, k, QWEN_IN, QWEN_OUT) if axis
+             else synth.Shape(0, 256, L, k, QWEN_OUT, QWEN_IN))
+    d = Dev(synth.make_problem(shape, M, CFG["test"], proj=820 + M), T)
+    say(f"determinism axis={axis} M={M} k={k}")
+    assert np.array_equal(bf16_bits(run(T, d)), bf16_bits(run(T, d)))
+
+
+def test_prefill_axis0_one_hot_bit_exact(gpu_lib):
+    """Axis 0, eight one-hot activation rows: output row m is stored row
+    cols[m] of W exactly."""
+    T = gpu_lib
+    shape = synth.Shape(0, 256, L, 3, 2000, 1024)
+    cols = [0, 1, 7, 8, 999, 1000, 1998, 1999]
+    p0 = synth.make_problem(shape, 8, CFG["test"], proj=830)
+    p = with_x(p0, synth.one_hot_x(8, 2000, cols))
+    say("prefill axis0 one-hot M=8 k=3")
+    y = bf16_bits(run(T, Dev(p, T)))
+    W = oracle_W(p)
+    for m, r in enumerate(cols):
+        assert np.array_equal(y[m], W[r]), (m, r)
+
+
 # ------------------------------------------------------ MLP (k=4, M=1/32)
 @pytest.mark.parametrize("M", [1, 32])
 def test_mlp_projections_sampled(gpu_lib, M):
