@@ -1,7 +1,9 @@
-// Axis-1 trellis kernels for gfx950: the fused decode + bf16 MFMA kernel for
-// several activation rows (1 <= M <= 32; also the M = 1 GEMV when a row is too
-// long for the activation-staging GEMV kernel), and the diagnostic expand
-// kernel. Both decode through the same fragment builder.
+// Axis-1 trellis kernels for gfx950: the fused decode + bf16 MFMA kernel of
+// 16-row groups for several activation rows (1 <= M <= 32; the library sends
+// small batches to the GEMV-mapped kernel in gemv.hip when that fits and
+// measured faster, and long single rows here when neither GEMV kernel takes
+// them), and the diagnostic expand kernel. Both decode through the same
+// fragment builder.
 //
 // Pages cited: diff views of "@mlx-bun/inference" 0.0.0-stage -> 1.0.0,
 // page 60: tiled-prefill.ts (axis-1 tile decode + matrix multiply, bf16

@@ -55,8 +55,8 @@ hipError_t launch_gemv_rows(const uint16_t* x, int M, const uint32_t* codes, Cod
                             const float* scales, const float* lut, uint16_t* y, int N, int nb,
                             int k, hipStream_t st);
 
-// Axis 1, 1 <= M <= 32: y[M][N] from x[M][nb*256] and codes [N][nb][8k].
-// Persistent workgroups of at most 80 rows; any nb.
+// Axis 1, 1 <= M <= 32: y[M][N] from x[M][nb*256] and codes [N][nb][8k]
+// (16-row groups). Persistent workgroups of at most 80 rows; any nb.
 hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                         const float* scales, const float* lut, uint16_t* y, int N, int nb, int k,
                         hipStream_t st);
