@@ -41,6 +41,8 @@
 //
 // Code words are prefetched two steps ahead into registers: measured under
 // load, a memory round trip takes longer than one step of decode.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -510,18 +512,20 @@ hipError_t launch_gemv_rows_k(const uint16_t* x, int M, const uint32_t* codes, C
 
 }  // namespace
 
+// Per-device cache; atomic so that host threads calling the library at the
+// same time only ever race to store the same value.
 int cu_count() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] <= 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 int gemv_max_blocks(int k) {
