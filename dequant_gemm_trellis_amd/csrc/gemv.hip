@@ -56,16 +56,42 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kPartialCap = 2048;    // unit partials held in LDS per row chunk
 constexpr int kXStride = 528;        // bytes per staged activation block (512 + 16)
 
+// Decode table: the k = 2 pair table, or for k = 3, 4 the codebook in
+// bank-partitioned copies (kRepCopies, 128 KB); both leave 32 KB of LDS.
 template <int K>
 struct GemvLds {
     static constexpr bool pair = K == 2;
-    static constexpr int tab_floats = pair ? 2 * kPairEntries : kLutEntries;
+    static constexpr bool rep = !pair;
+    static constexpr int tab_floats = pair ? 2 * kPairEntries : kRepFloats;
     // activation bytes that fit beside the table and the partials in 160 KB
-    static constexpr int x_bytes = pair ? 24576 : 65536;
+    static constexpr int x_bytes = 24576;
     static constexpr int max_blocks = x_bytes / kXStride;
     // fragments whose gathers are in flight ahead of the one being packed
     // (3 and 4 measured no faster)
     static constexpr int depth = 2;
+};
+
+// Fragment S's gathers from the kernel's decode table.
+template <int K, int S>
+__device__ __forceinline__ Gathered<GemvLds<K>::pair> gemv_gather(const uint32_t (&w)[2 * K + 1],
+                                                                  const float* __restrict__ tab) {
+    if constexpr (GemvLds<K>::rep) return gather_run64_rep<K, S>(w, tab, rep_lane_offset());
+    else return gather_run64<K, S, GemvLds<K>::pair>(w, tab);
+}
+
+// Table staging in two phases (fetch into registers, store to LDS).
+template <int K>
+struct GemvTable {
+    static constexpr bool rep = GemvLds<K>::rep;
+    using Src = std::conditional_t<rep, RepSrc<kThreads>, TableSrc<kThreads, GemvLds<K>::pair>>;
+    static __device__ __forceinline__ void fetch(Src& s, const float* lut) {
+        if constexpr (rep) fetch_rep<kThreads>(s, lut);
+        else fetch_table<kThreads, GemvLds<K>::pair>(s, lut);
+    }
+    static __device__ __forceinline__ void store(const Src& s, float* tab) {
+        if constexpr (rep) store_rep<kThreads>(s, tab);
+        else store_table<kThreads, GemvLds<K>::pair>(s, tab);
+    }
 };
 
 // Code words of one step for one lane, plus the unit's block and the
@@ -151,11 +177,11 @@ __device__ __forceinline__ void run_step(Step<K> st, XFrag& xf, uint32_t& xb,
     Gathered<P> g[8];
     static_for<0, D>([&](auto ic) {
         constexpr int S = 7 - decltype(ic)::value;
-        g[S] = gather_run64<K, S, P>(st.w, tab);
+        g[S] = gemv_gather<K, S>(st.w, tab);
     });
     static_for<0, 8>([&](auto ic) {
         constexpr int S = 7 - decltype(ic)::value;
-        if constexpr (S >= D) g[S - D] = gather_run64<K, S - D, P>(st.w, tab);
+        if constexpr (S >= D) g[S - D] = gemv_gather<K, S - D>(st.w, tab);
         const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g[S], st.scale));
         acc = mfma16x16x32(as_bf16x8(xf.v[S]), bfrag, acc);
     });
@@ -195,10 +221,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     // first two steps' code words; the table and activation stores then wait
     // only for their own data (memory-counter waits retire in issue order),
     // while the code words are still on their way from HBM.
-    constexpr bool kPair = GemvLds<K>::pair;
     constexpr int kXChunks = (GemvLds<K>::max_blocks * 32 + kThreads - 1) / kThreads;
-    TableSrc<kThreads, kPair> tsrc;
-    fetch_table<kThreads, kPair>(tsrc, lut);
+    typename GemvTable<K>::Src tsrc;
+    GemvTable<K>::fetch(tsrc, lut);
     u32x4 xv[kXChunks];
 #pragma unroll
     for (int q = 0; q < kXChunks; ++q) {  // 16-byte chunks of x, 32 per block
@@ -217,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     cx.magic = div_magic(CR);
     load_step<K, PAIRS>(sa, cx, ub + j, ue > 1 ? ue : 1);
     load_step<K, PAIRS>(sb, cx, ub + 16 + j, ue > 1 ? ue : 1);
-    store_table<kThreads, kPair>(tsrc, tab);
+    GemvTable<K>::store(tsrc, tab);
 #pragma unroll
     for (int q = 0; q < kXChunks; ++q) {
         const int i = tid + q * kThreads;
