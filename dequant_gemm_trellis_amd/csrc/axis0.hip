@@ -51,10 +51,14 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
 }
 
+// Decode table: the k = 2 pair table, or for k = 3, 4 the bank-partitioned
+// codebook copies (both 128 KB).
 template <int K>
 struct A0Lds {
     static constexpr bool pair = K == 2;
-    static constexpr int tab_floats = pair ? 2 * kPairEntries : kLutEntries;
+    static constexpr bool rep = !pair;
+    using Table = DecodeTable<kA0Threads, pair, rep>;
+    static constexpr int tab_floats = Table::floats;
     static constexpr int red_floats = kA0Waves * 16 * kTileCols;  // one M tile of wave partials
     static constexpr int floats = tab_floats > red_floats ? tab_floats : red_floats;
 };
@@ -82,9 +86,8 @@ struct A0Ctx {
 // the last stored row), so the loads are unconditional. With VEC (R % 8 == 0,
 // scales 16-byte aligned) a lane's 8 rows are all stored rows or all past the
 // end: its A fragment is one aligned 16-byte load and, with VSC, its 8 scales
-// two (VSC is off where it measured slower: two M tiles at k = 2 then spill
-// registers); otherwise x is read element by element with the row count
-// applied.
+// two (VSC is off for two M tiles, where the kernels then spill registers);
+// otherwise x is read element by element with the row count applied.
 template <int MT, bool VEC, bool VSC>
 __device__ __forceinline__ void a0_load(A0Step<MT>& st, const A0Ctx& cx, int s) {
     const int rc = 32 * s + 8 * cx.c;
@@ -127,7 +130,8 @@ __device__ __forceinline__ void a0_load(A0Step<MT>& st, const A0Ctx& cx, int s) 
 // while one is packed and multiplied.
 template <int K, int MT, bool VEC>
 __device__ __forceinline__ void a0_decode(const A0Step<MT>& st, const A0Ctx& cx, int sh,
-                                          const float* __restrict__ tab, floatx4 (&acc)[8][MT]) {
+                                          const float* __restrict__ tab, uint32_t cofs,
+                                          floatx4 (&acc)[8][MT]) {
     uint32_t g[8][2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -167,11 +171,12 @@ __device__ __forceinline__ void a0_decode(const A0Step<MT>& st, const A0Ctx& cx,
             }
         });
     } else {
-        // weight t0 + e starts (7 - e) k bits above the lane's lowest window
+        // weight t0 + e starts (7 - e) k bits above the lane's lowest window;
+        // the lane reads its own codebook copy (byte offset cofs)
         auto gather = [&](auto ec, float (&v)[8]) {
             constexpr int o = (7 - decltype(ec)::value) * K;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = lds_lut(tab, lut_byte_offset<o>(g[i]));
+            for (int i = 0; i < 8; ++i) v[i] = lds_lut(tab, field_offset<o, kL, 5>(g[i]) | cofs);
         };
         float va[8], vb[8];
         gather(std::integral_constant<int, 0>{}, va);
@@ -196,7 +201,6 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const float* __restrict__ scales, const float* __restrict__ lut,
     float* __restrict__ partial, CodeLayout lay, int R, int C, int M, int P) {
     constexpr int wpb = Bits<K>::wpb;
-    constexpr bool kPair = A0Lds<K>::pair;
     __shared__ __attribute__((aligned(16))) float lds[A0Lds<K>::floats];
     float* const tab = lds;
 
@@ -232,27 +236,28 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     // The table sources first, then the first step's loads (unconditional; a
     // wave without steps reads a valid clamped step), so the table stores do
     // not wait for them.
-    TableSrc<kA0Threads, kPair> tsrc;
-    fetch_table<kA0Threads, kPair>(tsrc, lut);
+    typename A0Lds<K>::Table::Src tsrc;
+    A0Lds<K>::Table::fetch(tsrc, lut);
     asm volatile("" ::: "memory");
     A0Step<MT> sa, sb;
-    constexpr bool kVsc = VEC && !(K == 2 && MT == 2);
+    constexpr bool kVsc = VEC && MT == 1;
     a0_load<MT, VEC, kVsc>(sa, cx, s0);
-    store_table<kA0Threads, kPair>(tsrc, tab);
+    A0Lds<K>::Table::store(tsrc, tab);
     __syncthreads();
 
     // Two register sets alternate: the next step's loads are in flight while
     // one is decoded. Inside the loop every load feeds an unconditional decode
     // (a load used only under a branch gets sunk into it, behind the waits);
     // an odd last step is decoded after the loop.
+    const uint32_t cofs = rep_lane_offset();  // the lane's codebook copy (k = 3, 4)
     int s = s0;
     for (; s + 1 < s1; s += 2) {
         a0_load<MT, VEC, kVsc>(sb, cx, s + 1);
-        a0_decode<K, MT, VEC>(sa, cx, sh, tab, acc);
+        a0_decode<K, MT, VEC>(sa, cx, sh, tab, cofs, acc);
         a0_load<MT, VEC, kVsc>(sa, cx, s + 2);
-        a0_decode<K, MT, VEC>(sb, cx, sh, tab, acc);
+        a0_decode<K, MT, VEC>(sb, cx, sh, tab, cofs, acc);
     }
-    if (s < s1) a0_decode<K, MT, VEC>(sa, cx, sh, tab, acc);
+    if (s < s1) a0_decode<K, MT, VEC>(sa, cx, sh, tab, cofs, acc);
     __syncthreads();  // the table is dead from here on; its space takes the wave partials
 
     // Sum the waves' tiles in wave order, one M tile at a time.

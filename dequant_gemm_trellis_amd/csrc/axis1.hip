@@ -69,9 +69,13 @@ struct PrefillShape {
 template <int K, int MT, bool DIRECT>
 struct PrefillLds {
     static constexpr bool pair = K == 2;
-    static constexpr int tab_floats = pair ? 2 * kPairEntries : kLutEntries;
+    // k = 3, 4: the 16 KB codebook. The bank-partitioned copies (128 KB) leave
+    // room for only a one-line activation slot and measured 0-2% slower here.
+    static constexpr bool rep = false;
+    using Table = DecodeTable<PrefillShape<MT>::threads, pair, rep>;
+    static constexpr int tab_floats = Table::floats;
     static constexpr int waves = PrefillShape<MT>::waves;
-    static constexpr int lines = pair ? 1 : 4;
+    static constexpr int lines = tab_floats > kLutEntries ? 1 : 4;
     static constexpr int slot_chunks = DIRECT ? 0 : MT * lines * 16 * 8;
     static constexpr int decode_floats = tab_floats + waves * slot_chunks * 4;
     static constexpr int part_floats = waves * kGroups * 256;  // one M tile of wave partials
@@ -276,6 +280,7 @@ __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& 
                                          const XSource<MT>& xs, floatx4 (&acc)[kGroups][MT],
                                          const float* __restrict__ tab, int lane, int j, int c) {
     constexpr bool P = PrefillLds<K, MT, DIRECT>::pair;
+    constexpr bool REP = PrefillLds<K, MT, DIRECT>::rep;
     if (t.b != xb) {
         xb = t.b;
         if constexpr (DIRECT) {
@@ -303,12 +308,12 @@ __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& 
     });
     // Fragments 7 .. 0: only fragment 0 reads the word from the neighbouring
     // lane, which thus has the whole task to arrive.
-    Gathered<P> g0 = gather_run64<K, 7, P>(t.w, tab);
-    Gathered<P> g1 = gather_run64<K, 6, P>(t.w, tab);
+    Gathered<P> g0 = gather_tab<K, 7, P, REP>(t.w, tab);
+    Gathered<P> g1 = gather_tab<K, 6, P, REP>(t.w, tab);
     static_for<0, 8>([&](auto ic) {
         constexpr int S = 7 - decltype(ic)::value;
         Gathered<P> g2;
-        if constexpr (S >= 2) g2 = gather_run64<K, S - 2, P>(t.w, tab);
+        if constexpr (S >= 2) g2 = gather_tab<K, S - 2, P, REP>(t.w, tab);
         const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g0, t.scale));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -378,9 +383,8 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     // on the direct path, the first block's activation fragments
     // (unconditionally: a wave without tasks re-reads a valid one, and a load
     // under a branch would make the table stores wait for the code words too).
-    constexpr bool kPair = Lds::pair;
-    TableSrc<kThreadsP, kPair> tsrc;
-    fetch_table<kThreadsP, kPair>(tsrc, lut);
+    typename Lds::Table::Src tsrc;
+    Lds::Table::fetch(tsrc, lut);
     asm volatile("" ::: "memory");
     Task<K> ta, tb, tc;
     load_task_opaque<K, PAIRS>(ta, cx, tau0, tau1 > 1 ? tau1 : 1);
@@ -388,7 +392,7 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     XFrags<MT> xn;
     if constexpr (DIRECT) load_x_frags_opaque<MT>(xn, xs.xa, ta.b);
     asm volatile("" ::: "memory");
-    store_table<kThreadsP, kPair>(tsrc, tab);
+    Lds::Table::store(tsrc, tab);
     __syncthreads();
 
     // Three register sets rotate: the words of the next two tasks are in

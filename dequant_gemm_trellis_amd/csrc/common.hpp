@@ -241,11 +241,11 @@ __device__ __forceinline__ Gathered<false> gather_run64_rep(const uint32_t (&w)[
 }
 
 // Staging of the replicated codebook in two phases as fetch_table/store_table:
-// 16-byte chunk q of the table holds four copies of entry q >> 1, so thread
-// tid writes chunks tid + NTHREADS i, all lanes of a store contiguous.
+// entry e fills the two 16-byte chunks at byte e << 5 (four copies each);
+// thread tid stages entries tid + NTHREADS i, one register each.
 template <int NTHREADS>
 struct RepSrc {
-    static constexpr int n = kRepFloats / 4 / NTHREADS;
+    static constexpr int n = kLutEntries / NTHREADS;
     float a[n];
 };
 
@@ -255,7 +255,7 @@ __device__ __forceinline__ void fetch_rep(RepSrc<NTHREADS>& src, const float* lu
     gf32 l = (gf32)lut;
     asm volatile("" : "+s"(l));
 #pragma unroll
-    for (int i = 0; i < RepSrc<NTHREADS>::n; ++i) src.a[i] = l[(threadIdx.x + NTHREADS * i) >> 1];
+    for (int i = 0; i < RepSrc<NTHREADS>::n; ++i) src.a[i] = l[threadIdx.x + NTHREADS * i];
 }
 
 template <int NTHREADS>
@@ -264,7 +264,9 @@ __device__ __forceinline__ void store_rep(const RepSrc<NTHREADS>& src, float* __
 #pragma unroll
     for (int i = 0; i < RepSrc<NTHREADS>::n; ++i) {
         const float a = src.a[i];
-        dst[threadIdx.x + NTHREADS * i] = float4{a, a, a, a};
+        const int e = threadIdx.x + NTHREADS * i;
+        dst[2 * e] = float4{a, a, a, a};
+        dst[2 * e + 1] = float4{a, a, a, a};
     }
 }
 
@@ -347,6 +349,32 @@ __device__ __forceinline__ void stage_pair_table(float* __restrict__ tab,
     fetch_table<NTHREADS, true>(src, lut);
     store_table<NTHREADS, true>(src, tab);
 }
+
+// Fragment S's gathers from a kernel's decode table (DecodeTable kinds).
+template <int K, int S, bool PAIR, bool REP>
+__device__ __forceinline__ Gathered<PAIR> gather_tab(const uint32_t (&w)[2 * K + 1],
+                                                     const float* __restrict__ tab) {
+    if constexpr (REP) return gather_run64_rep<K, S>(w, tab, rep_lane_offset());
+    else return gather_run64<K, S, PAIR>(w, tab);
+}
+
+// Staging of a kernel's decode table in two phases (fetch into registers,
+// store to LDS): the 16 KB codebook, the k = 2 pair table (PAIR) or the
+// bank-partitioned codebook copies (REP).
+template <int NTHREADS, bool PAIR, bool REP>
+struct DecodeTable {
+    static_assert(!(PAIR && REP), "one table kind");
+    using Src = std::conditional_t<REP, RepSrc<NTHREADS>, TableSrc<NTHREADS, PAIR>>;
+    static constexpr int floats = PAIR ? 2 * kPairEntries : REP ? kRepFloats : kLutEntries;
+    static __device__ __forceinline__ void fetch(Src& s, const float* lut) {
+        if constexpr (REP) fetch_rep<NTHREADS>(s, lut);
+        else fetch_table<NTHREADS, PAIR>(s, lut);
+    }
+    static __device__ __forceinline__ void store(const Src& s, float* __restrict__ tab) {
+        if constexpr (REP) store_rep<NTHREADS>(s, tab);
+        else store_table<NTHREADS, PAIR>(s, tab);
+    }
+};
 
 __device__ __forceinline__ uint16_t round_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));

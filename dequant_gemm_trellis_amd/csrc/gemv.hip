@@ -75,24 +75,11 @@ struct GemvLds {
 template <int K, int S>
 __device__ __forceinline__ Gathered<GemvLds<K>::pair> gemv_gather(const uint32_t (&w)[2 * K + 1],
                                                                   const float* __restrict__ tab) {
-    if constexpr (GemvLds<K>::rep) return gather_run64_rep<K, S>(w, tab, rep_lane_offset());
-    else return gather_run64<K, S, GemvLds<K>::pair>(w, tab);
+    return gather_tab<K, S, GemvLds<K>::pair, GemvLds<K>::rep>(w, tab);
 }
 
-// Table staging in two phases (fetch into registers, store to LDS).
 template <int K>
-struct GemvTable {
-    static constexpr bool rep = GemvLds<K>::rep;
-    using Src = std::conditional_t<rep, RepSrc<kThreads>, TableSrc<kThreads, GemvLds<K>::pair>>;
-    static __device__ __forceinline__ void fetch(Src& s, const float* lut) {
-        if constexpr (rep) fetch_rep<kThreads>(s, lut);
-        else fetch_table<kThreads, GemvLds<K>::pair>(s, lut);
-    }
-    static __device__ __forceinline__ void store(const Src& s, float* tab) {
-        if constexpr (rep) store_rep<kThreads>(s, tab);
-        else store_table<kThreads, GemvLds<K>::pair>(s, tab);
-    }
-};
+using GemvTable = DecodeTable<kThreads, GemvLds<K>::pair, GemvLds<K>::rep>;
 
 // Code words of one step for one lane, plus the unit's block and the
 // row-major index (row * nb + block) of its partial.
@@ -342,11 +329,16 @@ __host__ __device__ inline int rows_chunks(int rows, int max_rows) {
     return rows / n >= 16 ? n : 0;
 }
 
-template <int K>
+// REP (k = 3, 4): the bank-partitioned codebook copies, which leave room for
+// the partials of fewer rows (one chunk of 68 rows up to 4 activation rows at
+// 5120 inputs); else the 16 KB codebook.
+template <int K, bool REP>
 struct RowsLds {
     static constexpr bool pair = K == 2;
-    static constexpr int tab_floats = pair ? 2 * kPairEntries : kLutEntries;
-    static constexpr int part_floats = pair ? 7936 : 32768;  // the rest of 160 KB
+    static constexpr bool rep = REP;
+    using Table = DecodeTable<kThreads, pair, rep>;
+    static constexpr int tab_floats = Table::floats;
+    static constexpr int part_floats = (pair || rep) ? 7936 : 32768;  // the rest of 160 KB
 };
 
 // Activation fragments of block b in A layout from xa (row m = j, column 64 c).
@@ -368,23 +360,23 @@ __device__ __forceinline__ void load_xa_opaque(XFrag& xn, const uint16_t* xa, ui
 
 // One step of 16 units: eight fragments, gathers two ahead as in run_step.
 // STRAD: the step's units reach into block blo + 1, multiplied against xn.
-template <int K, bool STRAD>
+template <int K, bool REP, bool STRAD>
 __device__ __forceinline__ void run_rows_step(Step<K> st, const XFrag& xf, const XFrag& xn,
                                               uint32_t blo, const float* __restrict__ tab,
                                               float* __restrict__ part, int u, int u_end, int c,
                                               int m4) {
-    constexpr bool P = RowsLds<K>::pair;
+    constexpr bool P = RowsLds<K, REP>::pair;
     constexpr int D = GemvLds<K>::depth;
     st.w[2 * K] = next_run_word(st.w[0]);
     floatx4 d1 = {0.f, 0.f, 0.f, 0.f}, d2 = {0.f, 0.f, 0.f, 0.f};
     Gathered<P> g[8];
     static_for<0, D>([&](auto ic) {
         constexpr int S = 7 - decltype(ic)::value;
-        g[S] = gather_run64<K, S, P>(st.w, tab);
+        g[S] = gather_tab<K, S, P, REP>(st.w, tab);
     });
     static_for<0, 8>([&](auto ic) {
         constexpr int S = 7 - decltype(ic)::value;
-        if constexpr (S >= D) g[S - D] = gather_run64<K, S - D, P>(st.w, tab);
+        if constexpr (S >= D) g[S - D] = gather_tab<K, S - D, P, REP>(st.w, tab);
         const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g[S], st.scale));
         d1 = mfma16x16x32(as_bf16x8(xf.v[S]), bfrag, d1);
         if constexpr (STRAD) d2 = mfma16x16x32(as_bf16x8(xn.v[S]), bfrag, d2);
@@ -395,12 +387,12 @@ __device__ __forceinline__ void run_rows_step(Step<K> st, const XFrag& xf, const
     if (4 * c < m4 && u < u_end) *reinterpret_cast<floatx4*>(part + u * m4 + 4 * c) = d1;
 }
 
-template <int K, bool PAIRS>
+template <int K, bool PAIRS, bool REP>
 __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
     const float* __restrict__ scales, const float* __restrict__ lut,
     uint16_t* __restrict__ y, CodeLayout lay, int N, int nb, int M) {
-    using Lds = RowsLds<K>;
+    using Lds = RowsLds<K, REP>;
     __shared__ __attribute__((aligned(16))) float lds[Lds::tab_floats + Lds::part_floats];
     float* const tab = lds;
     float* const part = lds + Lds::tab_floats;
@@ -426,9 +418,8 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(
     // Prologue: the table sources first, then the first two steps' code words
     // and the first two blocks' activation fragments (all unconditional), so
     // the table stores wait only for their own data.
-    constexpr bool kPair = Lds::pair;
-    TableSrc<kThreads, kPair> tsrc;
-    fetch_table<kThreads, kPair>(tsrc, lut);
+    typename Lds::Table::Src tsrc;
+    Lds::Table::fetch(tsrc, lut);
     asm volatile("" ::: "memory");
     int CR = rows / nchunks, U = CR * nb;
     int ub = wave * U / kWaves, ue = (wave + 1) * U / kWaves;
@@ -440,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(
     load_xa_opaque(xf, xa, xb);
     load_xa_opaque(xn, xa, xb + 1 < static_cast<uint32_t>(nb) ? xb + 1 : xb);
     asm volatile("" ::: "memory");
-    store_table<kThreads, kPair>(tsrc, tab);
+    Lds::Table::store(tsrc, tab);
     __syncthreads();
 
     for (int q = 0; q < nchunks; ++q) {
@@ -477,11 +468,11 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(
             // and waits for all of them at it); k = 2: the branch.
             if constexpr (K != 2) {
                 (void)strad;
-                run_rows_step<K, true>(st, xf, xn, blo, tab, part, u0 + j, ue, c, m4);
+                run_rows_step<K, REP, true>(st, xf, xn, blo, tab, part, u0 + j, ue, c, m4);
             } else if (strad) {
-                run_rows_step<K, true>(st, xf, xn, blo, tab, part, u0 + j, ue, c, m4);
+                run_rows_step<K, REP, true>(st, xf, xn, blo, tab, part, u0 + j, ue, c, m4);
             } else {
-                run_rows_step<K, false>(st, xf, xn, blo, tab, part, u0 + j, ue, c, m4);
+                run_rows_step<K, REP, false>(st, xf, xn, blo, tab, part, u0 + j, ue, c, m4);
             }
         };
         // Three register sets rotate as in gemv_kernel; every load is
@@ -523,16 +514,39 @@ int rows_grid(int N) {
     return G < 1 ? 1 : G;
 }
 
+template <int K, bool REP>
+hipError_t launch_gemv_rows_kr(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
+                               const float* scales, const float* lut, uint16_t* y, int N, int nb,
+                               hipStream_t st) {
+    const int G = rows_grid(N);
+    if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
+        return launch_kernel(gemv_rows_kernel<K, false, REP>, dim3(G), dim3(kThreads), st, x,
+                             codes, scales, lut, y, lay, N, nb, M);
+    return launch_kernel(gemv_rows_kernel<K, true, REP>, dim3(G), dim3(kThreads), st, x, codes,
+                         scales, lut, y, lay, N, nb, M);
+}
+
+// Every workgroup's partials fit in one chunk beside a RowsLds<K, REP> table.
+template <int K, bool REP>
+bool rows_one_chunk(int M, int N, int nb) {
+    const int m4 = M > 4 ? 8 : 4;
+    const int max_rows = RowsLds<K, REP>::part_floats / (m4 * nb);
+    const int G = rows_grid(N);
+    // workgroups own floor(N / G) or ceil(N / G) rows
+    return rows_chunks(N / G, max_rows) == 1 && rows_chunks((N + G - 1) / G, max_rows) == 1;
+}
+
 template <int K>
 hipError_t launch_gemv_rows_k(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                               const float* scales, const float* lut, uint16_t* y, int N, int nb,
                               hipStream_t st) {
-    const int G = rows_grid(N);
-    if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
-        return launch_kernel(gemv_rows_kernel<K, false>, dim3(G), dim3(kThreads), st, x, codes,
-                             scales, lut, y, lay, N, nb, M);
-    return launch_kernel(gemv_rows_kernel<K, true>, dim3(G), dim3(kThreads), st, x, codes, scales,
-                         lut, y, lay, N, nb, M);
+    // k = 3, 4: the replicated codebook when every workgroup's partials fit in
+    // one chunk beside it.
+    if constexpr (K != 2) {
+        if (rows_one_chunk<K, true>(M, N, nb))
+            return launch_gemv_rows_kr<K, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    }
+    return launch_gemv_rows_kr<K, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
 }
 
 }  // namespace
@@ -575,7 +589,8 @@ bool gemv_rows_supported(int M, int N, int nb, int k) {
     // 14-21% slower than the 16-row-group kernel.
     if (k == 2 && M > 4) return false;
     const int m4 = M > 4 ? 8 : 4;
-    const int max_rows = (k == 2 ? RowsLds<2>::part_floats : RowsLds<4>::part_floats) / (m4 * nb);
+    const int max_rows =
+        (k == 2 ? RowsLds<2, false>::part_floats : RowsLds<4, false>::part_floats) / (m4 * nb);
     const int G = rows_grid(N);
     // workgroups own floor(N / G) or ceil(N / G) rows
     return rows_chunks(N / G, max_rows) > 0 && rows_chunks((N + G - 1) / G, max_rows) > 0;
