@@ -45,6 +45,7 @@ constexpr int kTileCols = 128;
 constexpr int kA0Threads = 512;     // 8 waves, two per SIMD
 constexpr int kA0Waves = kA0Threads / kWave;
 constexpr int kA0TargetGroups = 256;  // tiles x parts is about this
+constexpr int kXcds = 8;              // accelerator dies, each with its own L2
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     floatx2 p = {a, b};
@@ -80,7 +81,18 @@ struct A0Ctx {
     const uint16_t* xr[2];  // A rows m = j and 16 + j (rows past M read row 0)
     size_t row_words;
     int w0, w1, R, c;
+    // Buffer-addressed loads (BUF): raw buffer resources over the tile's
+    // codes and the scales, and 32-bit byte offsets into them.
+    __amdgpu_buffer_rsrc_t rcodes, rscales;
+    uint32_t row_bytes;     // stored-row stride of the codes
+    uint32_t wb0, wb1;      // byte offsets of words w0, w1 within a row
 };
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+    // dword 3 of a raw (untyped, unswizzled) buffer resource on this family
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                             0x00020000);
+}
 
 // Issue step s's loads; every address is valid whatever s is (rows clamp to
 // the last stored row), so the loads are unconditional. With VEC (R % 8 == 0,
@@ -88,10 +100,38 @@ struct A0Ctx {
 // end: its A fragment is one aligned 16-byte load and, with VSC, its 8 scales
 // two (VSC is off for two M tiles, where the kernels then spill registers);
 // otherwise x is read element by element with the row count applied.
-template <int MT, bool VEC, bool VSC>
+//
+// With BUF (VEC, and every byte offset below 2^31) the same loads go through
+// raw buffer resources: one 32-bit lane offset per step, the row stride as
+// the uniform scalar offset, so no 64-bit address arithmetic per row (the
+// scales always as eight 4-byte loads, which the compiler merges; x as in VEC).
+template <int MT, bool VEC, bool VSC, bool BUF>
 __device__ __forceinline__ void a0_load(A0Step<MT>& st, const A0Ctx& cx, int s) {
     const int rc = 32 * s + 8 * cx.c;
     st.rc = rc;
+    if constexpr (BUF) {
+        static_assert(VEC, "buffer loads take whole 8-row chunks");
+        const uint32_t rcc = static_cast<uint32_t>(rc < cx.R ? rc : cx.R - 8);
+        const uint32_t vo = rcc * cx.row_bytes;
+        static_for<0, 8>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const int so = static_cast<int>(i * cx.row_bytes);
+            st.a[i] = __builtin_amdgcn_raw_buffer_load_b32(cx.rcodes, static_cast<int>(vo + cx.wb0), so, 0);
+            st.b[i] = __builtin_amdgcn_raw_buffer_load_b32(cx.rcodes, static_cast<int>(vo + cx.wb1), so, 0);
+        });
+        // 4-byte loads only (adjacent ones are merged into wide loads); this
+        // compiler lowers the 16-byte raw buffer load builtin to one dword.
+        static_for<0, 8>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            st.sc[i] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(cx.rscales, static_cast<int>(4 * rcc + 4 * i), 0, 0));
+        });
+        static_for<0, MT>([&](auto mc) {  // one 16-byte global load
+            constexpr int mt = decltype(mc)::value;
+            st.x[mt] = *reinterpret_cast<const u32x4*>(cx.xr[mt] + rcc);
+        });
+        return;
+    }
     static_for<0, 8>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         const int r = rc + i < cx.R ? rc + i : cx.R - 1;
@@ -195,7 +235,7 @@ __device__ __forceinline__ void a0_decode(const A0Step<MT>& st, const A0Ctx& cx,
     }
 }
 
-template <int K, int MT, bool VEC>
+template <int K, int MT, bool VEC, bool BUF>
 __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
     const float* __restrict__ scales, const float* __restrict__ lut,
@@ -207,8 +247,15 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, c = lane >> 4;
-    const int tile = blockIdx.x / P;
-    const int part = blockIdx.x - tile * P;
+    // Workgroup b runs on XCD b % 8 (round-robin dispatch). The (part, tile)
+    // pairs are numbered part-major and each XCD takes a contiguous range of
+    // them, so that neighbouring tiles of a part, whose code rows share cache
+    // lines (a k = 3 tile reads 48 bytes of each row), meet in one L2.
+    const int G = static_cast<int>(gridDim.x), tiles = G / P;
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int L = xcd * (G / kXcds) + min(xcd, G % kXcds) + slot;
+    const int part = L / tiles;
+    const int tile = L - part * tiles;
     const int col0 = tile * kTileCols;
     const int blk = col0 / kT;
     const int t0 = (col0 % kT) + 8 * j;         // first weight of this lane's 8 columns
@@ -223,9 +270,24 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const int s0 = p0 + wave * (p1 - p0) / kA0Waves;
     const int s1 = p0 + (wave + 1) * (p1 - p0) / kA0Waves;
 
-    A0Ctx cx{codes + block_word<K>(lay, 0, blk), scales,
-             {x + static_cast<size_t>(j < M ? j : 0) * R, x + static_cast<size_t>(16 + j < M ? 16 + j : 0) * R},
-             lay.row_words, w0, w1, R, c};
+    A0Ctx cx;
+    cx.cbase = codes + block_word<K>(lay, 0, blk);
+    cx.scales = scales;
+    cx.xr[0] = x + static_cast<size_t>(j < M ? j : 0) * R;
+    cx.xr[1] = x + static_cast<size_t>(16 + j < M ? 16 + j : 0) * R;
+    cx.row_words = lay.row_words;
+    cx.w0 = w0;
+    cx.w1 = w1;
+    cx.R = R;
+    cx.c = c;
+    if constexpr (BUF) {
+        // the launcher checked that R rows of codes span less than 2^31 bytes
+        cx.row_bytes = static_cast<uint32_t>(lay.row_words * 4);
+        cx.rcodes = raw_rsrc(cx.cbase, static_cast<uint32_t>(R) * cx.row_bytes);
+        cx.rscales = raw_rsrc(scales, 4u * static_cast<uint32_t>(R));
+        cx.wb0 = 4u * static_cast<uint32_t>(w0);
+        cx.wb1 = 4u * static_cast<uint32_t>(w1);
+    }
 
     floatx4 acc[8][MT];
 #pragma unroll
@@ -241,7 +303,7 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     asm volatile("" ::: "memory");
     A0Step<MT> sa, sb;
     constexpr bool kVsc = VEC && MT == 1;
-    a0_load<MT, VEC, kVsc>(sa, cx, s0);
+    a0_load<MT, VEC, kVsc, BUF>(sa, cx, s0);
     A0Lds<K>::Table::store(tsrc, tab);
     __syncthreads();
 
@@ -252,9 +314,9 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const uint32_t cofs = rep_lane_offset();  // the lane's codebook copy (k = 3, 4)
     int s = s0;
     for (; s + 1 < s1; s += 2) {
-        a0_load<MT, VEC, kVsc>(sb, cx, s + 1);
+        a0_load<MT, VEC, kVsc, BUF>(sb, cx, s + 1);
         a0_decode<K, MT, VEC>(sa, cx, sh, tab, cofs, acc);
-        a0_load<MT, VEC, kVsc>(sa, cx, s + 2);
+        a0_load<MT, VEC, kVsc, BUF>(sa, cx, s + 2);
         a0_decode<K, MT, VEC>(sb, cx, sh, tab, cofs, acc);
     }
     if (s < s1) a0_decode<K, MT, VEC>(sa, cx, sh, tab, cofs, acc);
@@ -318,22 +380,27 @@ __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
     if (q == 0 && i < MC) y[i] = round_bf16(((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
 }
 
-template <int K, int MT, bool VEC>
+template <int K, int MT, bool VEC, bool BUF>
 hipError_t launch_axis0_k(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                           const float* scales, const float* lut, float* partial, int R, int C, int P,
                           hipStream_t st) {
     const dim3 grid(static_cast<unsigned>((C / kTileCols) * P));
-    return launch_kernel(axis0_mma_kernel<K, MT, VEC>, grid, dim3(kA0Threads), st, x, codes, scales,
-                         lut, partial, lay, R, C, M, P);
+    return launch_kernel(axis0_mma_kernel<K, MT, VEC, BUF>, grid, dim3(kA0Threads), st, x, codes,
+                         scales, lut, partial, lay, R, C, M, P);
 }
 
 template <int K, int MT>
 hipError_t launch_axis0_v(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                           const float* scales, const float* lut, float* partial, int R, int C, int P,
                           hipStream_t st) {
-    if (R % 8 == 0 && reinterpret_cast<uintptr_t>(scales) % 16 == 0)
-        return launch_axis0_k<K, MT, true>(x, M, codes, lay, scales, lut, partial, R, C, P, st);
-    return launch_axis0_k<K, MT, false>(x, M, codes, lay, scales, lut, partial, R, C, P, st);
+    if (R % 8 == 0 && reinterpret_cast<uintptr_t>(scales) % 16 == 0) {
+        // buffer loads when every byte offset they form fits in 31 bits
+        const uint64_t lim = 1ull << 31;
+        if (static_cast<uint64_t>(R) * lay.row_words * 4 < lim)
+            return launch_axis0_k<K, MT, true, true>(x, M, codes, lay, scales, lut, partial, R, C, P, st);
+        return launch_axis0_k<K, MT, true, false>(x, M, codes, lay, scales, lut, partial, R, C, P, st);
+    }
+    return launch_axis0_k<K, MT, false, false>(x, M, codes, lay, scales, lut, partial, R, C, P, st);
 }
 
 }  // namespace
