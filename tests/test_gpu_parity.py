@@ -541,6 +541,21 @@ def test_gemv_most_rows(gpu_lib):
     assert gate(y[:, rows], oracle_y(row_subset(p, rows))) <= TOL
 
 
+@pytest.mark.parametrize("C", [7936, 8192])
+def test_axis0_codes_near_2gib(gpu_lib, C):
+    """Axis 0, 2^19 stored rows at k = 4: 7936 columns give 1.94 GiB of codes
+    (buffer-addressed loads with lane offsets just below 2^31), 8192 columns
+    exactly 2 GiB (the 64-bit pointer path). Checked on sampled columns."""
+    T = gpu_lib
+    shape = synth.Shape(0, 256, L, 4, MAXF, C)
+    p = synth.make_problem(shape, 1, CFG["test"], proj=990 + C // 256)
+    say(f"scatter in=2^19 out={C} k=4 ({p.codes.nbytes / 2**30:.2f} GiB of codes)")
+    y = bf16_to_f64(run(T, Dev(p, T), op="scatter"))
+    for a, b in ((0, 16), (C // 2 - 8, C // 2 + 8), (C - 16, C)):
+        ref = oracle_y(p, a, b)[:, a:b]
+        assert gate(y[:, a:b], ref) <= TOL, (a, b)
+
+
 @pytest.mark.parametrize("M", [1, 4])
 def test_axis0_most_input_rows(gpu_lib, M):
     """Axis 0 with 2^19 stored (input) rows over 256 output columns: 4096 rows
