@@ -313,8 +313,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; the multi-GPU sharding is a design "
-              "note (see the design document), so --gpus must be 1.", file=sys.stderr)
+        print("bench.py: the kernels run on one GPU (a GPU's share of a sharded layer is the "
+              "same kernel on fewer rows); nothing here runs across GPUs, so --gpus must be 1.",
+              file=sys.stderr)
         return 2
 
     import torch
