@@ -221,7 +221,8 @@ def scatter_bench(T, torch, dev, steps, warmup, only, out):
 
 
 def mlp_bench(T, torch, dev, M, steps, warmup, out):
-    """The MLP workload: gate and up (axis 1) then down (axis 0), k=4."""
+    """The MLP workload: gate and up (axis 1, the same activations; at M=1 one
+    dual-GEMV launch, also timed as two GEMVs) then down (axis 0), k=4."""
     from dequant_gemm_trellis_amd import synth
 
     C = synth.CONFIG_IDS
@@ -237,22 +238,39 @@ def mlp_bench(T, torch, dev, M, steps, warmup, out):
     ws = torch.empty(max(T.workspace_bytes(shapes[2], M, T.OP_PREFILL), 16) // 4,
                      dtype=torch.float32, device=dev)
 
+    ws1 = ws[: T.workspace_bytes(shapes[2], 1, T.OP_GEMV_SCATTER) // 4]
+
+    def down(i):
+        x, codes, scales, lut = projs[2].items[i]
+        if M == 1:
+            T.gemv_scatter(x, codes, scales, lut, geoms[2], workspace=ws1, y=ys[2].reshape(-1))
+        else:
+            T.prefill(x, codes, scales, lut, geoms[2], workspace=ws, y=ys[2])
+
     def mlp(i):
-        for j in range(3):
-            x, codes, scales, lut = projs[j].items[i]
-            if M == 1:
-                if j < 2:
-                    T.gemv(x, codes, scales, lut, geoms[j], y=ys[j].reshape(-1))
-                else:
-                    T.gemv_scatter(x, codes, scales, lut, geoms[j],
-                                   workspace=ws[: T.workspace_bytes(shapes[2], 1,
-                                                                    T.OP_GEMV_SCATTER) // 4],
-                                   y=ys[j].reshape(-1))
-            else:
-                T.prefill(x, codes, scales, lut, geoms[j], workspace=ws, y=ys[j])
+        # gate and up read the same activations (the gate set's x)
+        x = projs[0].items[i][0]
+        if M == 1:
+            T.gemv_dual(x, projs[0].items[i][1:], projs[1].items[i][1:], geoms[0],
+                        y_a=ys[0].reshape(-1), y_b=ys[1].reshape(-1))
+        else:
+            for j in range(2):
+                _, codes, scales, lut = projs[j].items[i]
+                T.prefill(x, codes, scales, lut, geoms[j], y=ys[j])
+        down(i)
+
+    def mlp_separate(i):
+        x = projs[0].items[i][0]
+        for j in range(2):
+            _, codes, scales, lut = projs[j].items[i]
+            T.gemv(x, codes, scales, lut, geoms[j], y=ys[j].reshape(-1))
+        down(i)
 
     ms = time_calls(torch, mlp, n, max(steps // 3, 10), warmup)
     out[f"mlp_k4_M{M}"] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
+    if M == 1:
+        ms = time_calls(torch, mlp_separate, n, max(steps // 3, 10), warmup)
+        out["mlp_k4_M1_separate_gemvs"] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
     del projs
 
 

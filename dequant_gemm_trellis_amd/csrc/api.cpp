@@ -106,6 +106,30 @@ int trellis_gemv(const uint16_t* x, const uint32_t* codes, const float* scales, 
     return status_of(launch_axis1_any(x, 1, codes, scales, lut, y, d, g->k, stream));
 }
 
+int trellis_gemv_dual(const uint16_t* x, const uint32_t* codes_a, const float* scales_a,
+                      const float* lut_a, uint16_t* y_a, const uint32_t* codes_b,
+                      const float* scales_b, const float* lut_b, uint16_t* y_b,
+                      const trellis_geometry* g, hipStream_t stream) {
+    Dims d;
+    int st = check_geometry(g, &d);
+    if (st) return st;
+    if (g->axis != 1) return TRELLIS_ERR_GEOMETRY;
+    if ((st = check_operands(codes_a, scales_a, lut_a)) || (st = check_io(x, y_a)) ||
+        (st = check_operands(codes_b, scales_b, lut_b)) || (st = check_io(x, y_b)))
+        return st;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(y_a), b = reinterpret_cast<uintptr_t>(y_b);
+    const uintptr_t bytes = static_cast<uintptr_t>(d.rows) * sizeof(uint16_t);
+    if (a < b + bytes && b < a + bytes) return TRELLIS_ERR_OVERLAP;
+    if (d.nb <= trellis::gemv_max_blocks(g->k))
+        return status_of(trellis::launch_gemv_dual(x, codes_a, scales_a, lut_a, y_a, codes_b,
+                                                   scales_b, lut_b, y_b, d.lay, d.rows, d.nb,
+                                                   g->k, stream));
+    // rows too long to stage: the two projections one after the other
+    if ((st = status_of(launch_axis1_any(x, 1, codes_a, scales_a, lut_a, y_a, d, g->k, stream))))
+        return st;
+    return status_of(launch_axis1_any(x, 1, codes_b, scales_b, lut_b, y_b, d, g->k, stream));
+}
+
 int trellis_gemv_scatter(const uint16_t* x, const uint32_t* codes, const float* scales,
                          const float* lut, const trellis_geometry* g, float* workspace,
                          size_t workspace_bytes, uint16_t* y, hipStream_t stream) {

@@ -53,7 +53,7 @@ namespace {
 // queue); 4 or 6 were slower.
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kPartialCap = 2048;    // unit partials held in LDS per row chunk
+constexpr int kPartialCap = 2048;    // LDS for unit partials beyond the activation staging
 constexpr int kXStride = 528;        // bytes per staged activation block (512 + 16)
 
 // Decode table: the k = 2 pair table, or for k = 3, 4 the codebook in
@@ -178,27 +178,42 @@ __device__ __forceinline__ void run_step(Step<K> st, XFrag& xf, uint32_t& xb,
     }
 }
 
+// Two projections of the same shape and the same activations (the gate and
+// up projections of an MLP) can share one launch: workgroups below G0 compute
+// y_a from (codes_a, scales_a, lut_a), the others y_b from the b operands,
+// each set of workgroups splitting the N rows evenly. A single projection
+// passes G0 = gridDim.x.
 template <int K, bool PAIRS>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
-    const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
-    const float* __restrict__ scales, const float* __restrict__ lut,
-    uint16_t* __restrict__ y, CodeLayout lay, int N, int nb) {
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes_a,
+    const float* __restrict__ scales_a, const float* __restrict__ lut_a,
+    uint16_t* __restrict__ y_a, const uint32_t* __restrict__ codes_b,
+    const float* __restrict__ scales_b, const float* __restrict__ lut_b,
+    uint16_t* __restrict__ y_b, int G0, CodeLayout lay, int N, int nb) {
     // One LDS array with the table first: a gather address then needs no base
     // added (the table at 64 KB, past the 16-bit instruction offset, costs a
-    // VALU op per weight).
+    // VALU op per weight). The unit partials take what the nb staged
+    // activation blocks leave of the rest.
     __shared__ __attribute__((aligned(16)))
     float lds[GemvLds<K>::tab_floats + GemvLds<K>::x_bytes / 4 + kPartialCap];
     float* const tab = lds;
     char* const xs = reinterpret_cast<char*>(lds + GemvLds<K>::tab_floats);
-    float* const part = lds + GemvLds<K>::tab_floats + GemvLds<K>::x_bytes / 4;
+    float* const part = reinterpret_cast<float*>(xs + nb * kXStride);
+    const int part_cap = (GemvLds<K>::x_bytes - nb * kXStride) / 4 + kPartialCap;
 
-    const int G = gridDim.x, g = blockIdx.x;
+    const bool second = static_cast<int>(blockIdx.x) >= G0;
+    const uint32_t* const codes = second ? codes_b : codes_a;
+    const float* const scales = second ? scales_b : scales_a;
+    const float* const lut = second ? lut_b : lut_a;
+    uint16_t* const y = second ? y_b : y_a;
+    const int G = second ? static_cast<int>(gridDim.x) - G0 : G0;
+    const int g = second ? static_cast<int>(blockIdx.x) - G0 : static_cast<int>(blockIdx.x);
     const int r0 = static_cast<int>(static_cast<long>(g) * N / G);
     const int r1 = static_cast<int>(static_cast<long>(g + 1) * N / G);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, c = lane >> 4;
-    const int chunk_rows = kPartialCap / nb;
+    const int chunk_rows = part_cap / nb;
 
     Ctx cx{codes + static_cast<size_t>(r0) * lay.row_words, lay, scales + r0, nb, 1, 0u, 3 - c};
     Step<K> sa, sb, sc;
@@ -284,18 +299,31 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     }
 }
 
+// One projection on min(N, CUs) workgroups, or two (the b operands non-null)
+// on min(N, CUs / 2) workgroups each, so that every CU runs one workgroup.
 template <int K>
-hipError_t launch_gemv_k(const uint16_t* x, const uint32_t* codes, CodeLayout lay,
-                         const float* scales, const float* lut, uint16_t* y, int N, int nb,
-                         hipStream_t st) {
-    const int G = N < cu_count() ? N : cu_count();
+hipError_t launch_gemv_k(const uint16_t* x, const uint32_t* codes, const float* scales,
+                         const float* lut, uint16_t* y, const uint32_t* codes_b,
+                         const float* scales_b, const float* lut_b, uint16_t* y_b, CodeLayout lay,
+                         int N, int nb, hipStream_t st) {
+    const bool dual = codes_b != nullptr;
+    int G0 = dual ? cu_count() / 2 : cu_count();
+    if (G0 < 1) G0 = 1;
+    if (G0 > N) G0 = N;
+    const int G = dual ? 2 * G0 : G0;
+    if (!dual) {
+        codes_b = codes;
+        scales_b = scales;
+        lut_b = lut;
+        y_b = y;
+    }
     // Row-major iff a row's blocks are contiguous (with two blocks per row the
     // two layouts coincide).
     if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
         return launch_kernel(gemv_kernel<K, false>, dim3(G), dim3(kThreads), st, x, codes, scales,
-                             lut, y, lay, N, nb);
+                             lut, y, codes_b, scales_b, lut_b, y_b, G0, lay, N, nb);
     return launch_kernel(gemv_kernel<K, true>, dim3(G), dim3(kThreads), st, x, codes, scales, lut,
-                         y, lay, N, nb);
+                         y, codes_b, scales_b, lut_b, y_b, G0, lay, N, nb);
 }
 
 // ---------------------------------------------------------------------------
@@ -574,9 +602,21 @@ int gemv_max_blocks(int k) {
 hipError_t launch_gemv(const uint16_t* x, const uint32_t* codes, CodeLayout lay, const float* scales,
                        const float* lut, uint16_t* y, int N, int nb, int k, hipStream_t st) {
     switch (k) {
-    case 2: return launch_gemv_k<2>(x, codes, lay, scales, lut, y, N, nb, st);
-    case 3: return launch_gemv_k<3>(x, codes, lay, scales, lut, y, N, nb, st);
-    case 4: return launch_gemv_k<4>(x, codes, lay, scales, lut, y, N, nb, st);
+    case 2: return launch_gemv_k<2>(x, codes, scales, lut, y, nullptr, nullptr, nullptr, nullptr, lay, N, nb, st);
+    case 3: return launch_gemv_k<3>(x, codes, scales, lut, y, nullptr, nullptr, nullptr, nullptr, lay, N, nb, st);
+    case 4: return launch_gemv_k<4>(x, codes, scales, lut, y, nullptr, nullptr, nullptr, nullptr, lay, N, nb, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemv_dual(const uint16_t* x, const uint32_t* codes_a, const float* scales_a,
+                            const float* lut_a, uint16_t* y_a, const uint32_t* codes_b,
+                            const float* scales_b, const float* lut_b, uint16_t* y_b,
+                            CodeLayout lay, int N, int nb, int k, hipStream_t st) {
+    switch (k) {
+    case 2: return launch_gemv_k<2>(x, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    case 3: return launch_gemv_k<3>(x, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    case 4: return launch_gemv_k<4>(x, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -45,6 +45,13 @@ hipError_t launch_gemv(const uint16_t* x, const uint32_t* codes, CodeLayout lay,
                        const float* lut, uint16_t* y, int N, int nb, int k, hipStream_t st);
 int gemv_max_blocks(int k);
 
+// Two axis-1 GEMVs of one shape over the same x in one launch (half of the
+// compute units each); same conditions as launch_gemv.
+hipError_t launch_gemv_dual(const uint16_t* x, const uint32_t* codes_a, const float* scales_a,
+                            const float* lut_a, uint16_t* y_a, const uint32_t* codes_b,
+                            const float* scales_b, const float* lut_b, uint16_t* y_b,
+                            CodeLayout lay, int N, int nb, int k, hipStream_t st);
+
 // Axis 1, 1 <= M <= kGemvRowsMaxM, in the GEMV's unit mapping (one workgroup
 // per compute unit, at least 16 rows each); gemv_rows_supported says whether
 // the geometry fits it (at least 16 rows, 16 rows' unit partials fit in LDS)

@@ -36,8 +36,9 @@ OP_PREFILL = 2
 MAX_M = 32
 
 # Every function trellis.h declares, for the export check.
-EXPORTED = ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_scatter", "trellis_prefill",
-            "trellis_workspace_bytes", "trellis_expand", "trellis_repack", "trellis_strerror")
+EXPORTED = ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_dual", "trellis_gemv_scatter",
+            "trellis_prefill", "trellis_workspace_bytes", "trellis_expand", "trellis_repack",
+            "trellis_strerror")
 
 
 class Geometry(C.Structure):
@@ -55,6 +56,7 @@ _vp = C.c_void_p
 _GP = C.POINTER(Geometry)
 _lib.trellis_lut_upload.argtypes = [_vp, C.c_int32, _vp, _vp]
 _lib.trellis_gemv.argtypes = [_vp, _vp, _vp, _vp, _GP, _vp, _vp]
+_lib.trellis_gemv_dual.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _GP, _vp]
 _lib.trellis_gemv_scatter.argtypes = [_vp, _vp, _vp, _vp, _GP, _vp, C.c_size_t, _vp, _vp]
 _lib.trellis_prefill.argtypes = [_vp, C.c_int32, _vp, _vp, _vp, _GP, _vp, C.c_size_t, _vp, _vp]
 _lib.trellis_workspace_bytes.argtypes = [_GP, C.c_int32, C.c_int32]
@@ -63,8 +65,8 @@ _lib.trellis_expand.argtypes = [_vp, _vp, _vp, _GP, _vp, _vp]
 _lib.trellis_repack.argtypes = [_vp, _vp, _GP, C.c_int32, _vp]
 _lib.trellis_strerror.argtypes = [C.c_int]
 _lib.trellis_strerror.restype = C.c_char_p
-for _f in ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_scatter", "trellis_prefill",
-           "trellis_expand", "trellis_repack"):
+for _f in ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_dual", "trellis_gemv_scatter",
+           "trellis_prefill", "trellis_expand", "trellis_repack"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -131,6 +133,21 @@ def gemv(x, codes, scales, lut, g, y=None, stream=None) -> torch.Tensor:
     _check("trellis_gemv", _lib.trellis_gemv(_dev(x), _dev(codes), _dev(scales), _dev(lut),
                                              C.byref(geom), _dev(y), _stream(stream)))
     return y
+
+
+def gemv_dual(x, a, b, g, y_a=None, y_b=None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Two axis-1 GEMVs over the same x in one launch; a and b are
+    (codes, scales, lut) triples of the same geometry g."""
+    geom = _geom(g)
+    if y_a is None:
+        y_a = torch.empty(geom.out_features, dtype=torch.bfloat16, device=x.device)
+    if y_b is None:
+        y_b = torch.empty(geom.out_features, dtype=torch.bfloat16, device=x.device)
+    (ca, sa, la), (cb, sb, lb) = a, b
+    _check("trellis_gemv_dual", _lib.trellis_gemv_dual(
+        _dev(x), _dev(ca), _dev(sa), _dev(la), _dev(y_a), _dev(cb), _dev(sb), _dev(lb),
+        _dev(y_b), C.byref(geom), _stream(stream)))
+    return y_a, y_b
 
 
 def gemv_scatter(x, codes, scales, lut, g, workspace=None, y=None, stream=None) -> torch.Tensor:

@@ -116,6 +116,25 @@ int trellis_gemv(const uint16_t *x, const uint32_t *codes, const float *scales,
                  hipStream_t stream);
 
 /*
+ * Two axis-1 GEMVs of the same geometry over the same activation row, in one
+ * launch: the gate and up projections of a decoder MLP at a decode step.
+ *   y_a[n] = bf16( sum_k x[k] * Wa[n][k] ),  y_b[n] = bf16( sum_k x[k] * Wb[n][k] )
+ * with Wa from (codes_a, scales_a, lut_a) and Wb from (codes_b, scales_b,
+ * lut_b), each laid out as for trellis_gemv; g (axis 1) describes both. The
+ * results are bit-identical to two trellis_gemv calls; one launch saves the
+ * second launch and its codebook staging. (The pages run each projection on
+ * its own, page 60 wide-prefill.ts; the shared launch is this library's.)
+ * y_a and y_b must not overlap (TRELLIS_ERR_OVERLAP). For rows too long to
+ * stage in one launch the two projections are enqueued one after the other;
+ * should the runtime then reject the second launch (TRELLIS_ERR_HIP), the
+ * first one stays enqueued.
+ */
+int trellis_gemv_dual(const uint16_t *x, const uint32_t *codes_a, const float *scales_a,
+                      const float *lut_a, uint16_t *y_a, const uint32_t *codes_b,
+                      const float *scales_b, const float *lut_b, uint16_t *y_b,
+                      const trellis_geometry *g, hipStream_t stream);
+
+/*
  * Axis-0 "scatter" GEMV, one activation row (page 59 scatter.ts: split-K over
  * the stored rows, float32 partials per row range, then their sum and a cast):
  *   partial[s][n] = sum over stored rows r in range s of x[r] * W[r][n]

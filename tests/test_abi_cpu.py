@@ -100,6 +100,31 @@ def test_gemv_rejects_misaligned(T, arg, addr):
     assert call_gemv(T, geom(T), **{arg: addr}) == T.ERR_ALIGN
 
 
+def call_dual(T, g, **kw):
+    a = dict(x=FAKE, codes_a=FAKE, scales_a=FAKE, lut_a=FAKE, y_a=FAKE, codes_b=FAKE,
+             scales_b=FAKE, lut_b=FAKE, y_b=FAKE + 4096)
+    a.update(kw)
+    order = ("x", "codes_a", "scales_a", "lut_a", "y_a", "codes_b", "scales_b", "lut_b", "y_b")
+    return T.raw().trellis_gemv_dual(*[C.c_void_p(a[n]) for n in order],
+                                     C.byref(g) if g is not None else None, C.c_void_p(0))
+
+
+def test_gemv_dual_validation(T):
+    g = geom(T)  # 256 output rows: y spans 512 bytes
+    assert call_dual(T, None) == T.ERR_NULL
+    assert call_dual(T, geom(T, axis=0, i=256, o=512)) == T.ERR_GEOMETRY
+    assert call_dual(T, geom(T, k=5)) == T.ERR_GEOMETRY
+    for arg in ("x", "codes_a", "scales_a", "lut_a", "y_a", "codes_b", "scales_b", "lut_b", "y_b"):
+        assert call_dual(T, g, **{arg: 0}) == T.ERR_NULL, arg
+    for arg, addr in (("x", FAKE + 2), ("codes_b", FAKE + 4), ("lut_b", FAKE + 8),
+                      ("y_b", FAKE + 4096 + 2), ("scales_a", FAKE + 2)):
+        assert call_dual(T, g, **{arg: addr}) == T.ERR_ALIGN, arg
+    # the outputs must not overlap
+    assert call_dual(T, g, y_b=FAKE) == T.ERR_OVERLAP
+    assert call_dual(T, g, y_b=FAKE + 496) == T.ERR_OVERLAP
+    assert call_dual(T, g, y_a=FAKE + 4096 + 256) == T.ERR_OVERLAP
+
+
 def test_scatter_validation(T):
     lib = T.raw()
     g = geom(T, axis=0, i=17408, o=5120, k=3)

@@ -26,7 +26,8 @@ L = 12
 def oracle_y(p, n_begin=0, n_end=None):
     s = p.shape
     return oracle.fused_f64(p.x, p.codes, p.scales, p.lut, s.axis, s.T, s.L, s.k,
-                            s.in_features, s.out_features, n_begin, n_end)
+                            s.in_features, s.out_features, n_begin, n_end,
+                            block_interleave=s.block_interleave)
 
 
 def oracle_W(p):
@@ -512,6 +513,52 @@ def test_graph_capture_replays_match_eager(gpu_lib):
         for r, y in zip(ref, (y1, y2, y3)):
             assert np.array_equal(bf16_bits(y), r), rep
     assert gate(bf16_to_f64(y1.reshape(1, -1)), oracle_y(pu)) <= TOL
+
+
+# ------------------------------------------------------------ dual GEMV
+def dual_case(T, shape, proj, check_oracle=True):
+    """gate/up pair sharing x: bit-identical to two trellis_gemv calls, and
+    within tolerance of the oracle on each projection."""
+    pa = synth.make_problem(shape, 1, CFG["test"], proj=proj)
+    pb = with_x(synth.make_problem(shape, 1, CFG["test"], proj=proj + 1), pa.x)
+    da, db = Dev(pa, T), Dev(pb, T)
+    x = da.x.reshape(-1)
+    ya, yb = T.gemv_dual(x, (da.codes, da.scales, da.lut), (db.codes, db.scales, db.lut), da.shape)
+    ra = T.gemv(x, da.codes, da.scales, da.lut, da.shape)
+    rb = T.gemv(x, db.codes, db.scales, db.lut, db.shape)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(ya), bf16_bits(ra))
+    assert np.array_equal(bf16_bits(yb), bf16_bits(rb))
+    return pa, pb, ya.reshape(1, -1), yb.reshape(1, -1)
+
+
+@pytest.mark.parametrize("i,o,k,il", [(512, 256, 2, 0), (768, 300, 3, 0), (1024, 20, 4, 0),
+                                      (4096, 4111, 2, 2), (2048, 1000, 3, 2)])
+def test_gemv_dual_small(gpu_lib, i, o, k, il):
+    T = gpu_lib
+    say(f"gemv_dual in={i} out={o} k={k} interleave={il}")
+    pa, pb, ya, yb = dual_case(T, synth.Shape(1, 256, L, k, i, o, il), 1100 + k)
+    assert gate(bf16_to_f64(ya), oracle_y(pa)) <= TOL
+    assert gate(bf16_to_f64(yb), oracle_y(pb)) <= TOL
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_gemv_dual_qwen_sampled(gpu_lib, k):
+    T = gpu_lib
+    say(f"gemv_dual qwen-up k={k}")
+    pa, pb, ya, yb = dual_case(T, synth.Shape(1, 256, L, k, QWEN_IN, QWEN_OUT), 1110 + k)
+    rows = np.unique(np.concatenate([np.arange(0, QWEN_OUT, 997), np.arange(QWEN_OUT - 20, QWEN_OUT)]))
+    assert gate(bf16_to_f64(ya)[:, rows], oracle_y(row_subset(pa, rows))) <= TOL
+    assert gate(bf16_to_f64(yb)[:, rows], oracle_y(row_subset(pb, rows))) <= TOL
+
+
+def test_gemv_dual_long_rows(gpu_lib):
+    """Rows too long to stage in LDS: the two projections run one after the other."""
+    T = gpu_lib
+    say("gemv_dual in=2^16 out=40 k=3")
+    pa, pb, ya, yb = dual_case(T, synth.Shape(1, 256, L, 3, 1 << 16, 40), 1120)
+    assert gate(bf16_to_f64(ya), oracle_y(pa)) <= TOL
+    assert gate(bf16_to_f64(yb), oracle_y(pb)) <= TOL
 
 
 # ------------------------------------------------------------ maximum sizes
