@@ -67,7 +67,7 @@ size_t axis0_workspace(const Dims& d, int M) {
 int status_of(hipError_t e) { return e == hipSuccess ? TRELLIS_OK : TRELLIS_ERR_HIP; }
 
 // Axis 1, M activation rows. M = 1: the persistent GEMV kernel, which stages
-// the whole activation vector in LDS. Up to 8 rows (and single rows too long
+// the whole activation vector in LDS. Up to 4 rows (and single rows too long
 // for that staging): the GEMV's unit mapping with M outputs per unit, when
 // the workgroups own at least 16 rows whose partials fit in LDS. Otherwise
 // the tiled kernel of 16-row groups.

@@ -69,9 +69,10 @@ struct PrefillShape {
 template <int K, int MT, bool DIRECT>
 struct PrefillLds {
     static constexpr bool pair = K == 2;
-    // k = 3, 4: the 16 KB codebook. The bank-partitioned copies (128 KB) leave
-    // room for only a one-line activation slot and measured 0-2% slower here.
-    static constexpr bool rep = false;
+    // k = 3, 4 with activations loaded directly (M <= 8): the bank-partitioned
+    // codebook copies (128 KB). Staged activations keep the 16 KB codebook:
+    // beside the copies only a one-line slot fits, which measured 0-2% slower.
+    static constexpr bool rep = !pair && DIRECT;
     using Table = DecodeTable<PrefillShape<MT>::threads, pair, rep>;
     static constexpr int tab_floats = Table::floats;
     static constexpr int waves = PrefillShape<MT>::waves;

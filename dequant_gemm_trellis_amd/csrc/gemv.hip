@@ -623,11 +623,14 @@ hipError_t launch_gemv_dual(const uint16_t* x, const uint32_t* codes_a, const fl
 
 bool gemv_rows_supported(int M, int N, int nb, int k) {
     if (M < 1 || M > kGemvRowsMaxM || N < 16 || nb < 1) return false;
-    // k = 2 beyond 4 rows: beside the 128 KB pair table only about 49 rows'
-    // partials of 8 floats fit at 5120 inputs, and the second chunk (pipeline
-    // restart, a second epilogue, a block edge every other step) measured
-    // 14-21% slower than the 16-row-group kernel.
-    if (k == 2 && M > 4) return false;
+    // Beyond 4 rows the 16-row-group kernel measured faster: at k = 2 only
+    // about 49 rows' partials of 8 floats fit beside the 128 KB pair table at
+    // 5120 inputs, and the second chunk (pipeline restart, a second epilogue,
+    // a block edge every other step) was 14-21% slower; at k = 3, 4 the
+    // 16-row-group kernel with directly loaded activations reads the
+    // codebook copies and was 0.5-4% faster than this kernel on one codebook
+    // (M = 5, 8).
+    if (M > 4) return false;
     const int m4 = M > 4 ? 8 : 4;
     const int max_rows =
         (k == 2 ? RowsLds<2, false>::part_floats : RowsLds<4, false>::part_floats) / (m4 * nb);

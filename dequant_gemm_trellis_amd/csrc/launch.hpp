@@ -55,7 +55,7 @@ hipError_t launch_gemv_dual(const uint16_t* x, const uint32_t* codes_a, const fl
 // Axis 1, 1 <= M <= kGemvRowsMaxM, in the GEMV's unit mapping (one workgroup
 // per compute unit, at least 16 rows each); gemv_rows_supported says whether
 // the geometry fits it (at least 16 rows, 16 rows' unit partials fit in LDS)
-// and it measured faster than launch_axis1 there (k = 2 only up to M = 4).
+// and it measured faster than launch_axis1 there (up to M = 4).
 constexpr int kGemvRowsMaxM = 8;
 bool gemv_rows_supported(int M, int N, int nb, int k);
 hipError_t launch_gemv_rows(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
