@@ -33,15 +33,18 @@
 // reusing the table's space. Lanes of rows past the workgroup's range decode
 // all-zero words, so their gathers all hit one LDS address.
 //
-// Activation fragments reach the lanes one of two ways, chosen by M:
-//   - direct (M <= kDirectMaxM): each lane loads its own fragments from
-//     global memory in A layout, one block ahead of use. Lanes of rows
-//     m >= M read row M - 1, so an instruction touches only M x 4 distinct
-//     cache lines, and nothing goes through the LDS, which the codebook
-//     gathers keep busy;
+// Activation fragments reach the lanes one of two ways, chosen by M and k:
+//   - direct (M <= kDirectMaxM at k = 2, one M tile at k = 3, 4): each lane
+//     loads its own fragments from global memory in A layout, one block
+//     ahead of use. Lanes of rows m >= M read row M - 1, so an instruction
+//     touches only M x 4 distinct cache lines, and nothing goes through the
+//     LDS, which the codebook gathers keep busy. At k = 3, 4 this path also
+//     leaves room for the bank-partitioned codebook copies;
 //   - staged (larger M): coalesced loads of 16 rows, transposed through a
-//     per-wave LDS slot when the block changes. Direct loads would touch 64
-//     lines per instruction there, which measured slower.
+//     per-wave LDS slot when the block changes. With the single table,
+//     direct loads of 16 rows (64 lines per instruction) measured slower;
+//     at k = 3, 4 the copies they make room for more than make up for it
+//     (M = 16: 0.4-1.6% faster).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -492,8 +495,9 @@ hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLay
                         const float* scales, const float* lut, uint16_t* y, int N, int nb, int k,
                         hipStream_t st) {
     // One M tile up to M = 16, two above; direct activation fragments up to
-    // kDirectMaxM.
-    const int shape = M > 16 ? 2 : M > kDirectMaxM ? 1 : 0;
+    // kDirectMaxM at k = 2, for one M tile at k = 3, 4.
+    const int dmax = k == 2 ? kDirectMaxM : 16;
+    const int shape = M > 16 ? 2 : M > dmax ? 1 : 0;
     switch (k * 4 + shape) {
     case 8: return launch_axis1_k<2, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
     case 9: return launch_axis1_k<2, 1, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
