@@ -515,6 +515,47 @@ def test_graph_capture_replays_match_eager(gpu_lib):
     assert gate(bf16_to_f64(y1.reshape(1, -1)), oracle_y(pu)) <= TOL
 
 
+# ------------------------------------------------------------ degenerate cases
+def exact_problem(shape, M, codes, seed):
+    """Integer codebook, scales in {0.5, 1, 2}, activations in -3..3: every
+    product and partial sum is exact in float32, so each bf16 output has one
+    correct value whatever the summation order."""
+    g = np.random.default_rng(seed)
+    xi = g.integers(-3, 4, (M, shape.in_features)).astype(np.float32)
+    return synth.Problem(shape, M, codes, synth.integer_lut(),
+                         g.choice(np.array([0.5, 1.0, 2.0], np.float32), shape.rows),
+                         synth.to_bf16_bits(xi))
+
+
+@pytest.mark.parametrize("word", [0x00000000, 0xFFFFFFFF, 0x55555555])
+@pytest.mark.parametrize("op,axis,M,k", [("gemv", 1, 1, 2), ("gemv", 1, 1, 4), ("scatter", 0, 1, 3),
+                                         (None, 1, 3, 3), (None, 1, 12, 4), (None, 1, 32, 2),
+                                         (None, 0, 8, 4)])
+def test_constant_code_words_bit_exact(gpu_lib, word, op, axis, M, k):
+    """Every code word equal: all windows of a block hold one value (0, 0xFFF,
+    or a fixed pattern), so every row decodes to one repeated weight."""
+    T = gpu_lib
+    shape = synth.Shape(axis, 256, L, k, 1024, 768)
+    codes = np.full((shape.rows, shape.words_per_row), word, dtype=np.uint32)
+    p = exact_problem(shape, M, codes, seed=word % 1000 + 7 * M + k)
+    say(f"constant words {word:#010x} op={op or 'prefill'} axis={axis} M={M} k={k}")
+    y = bf16_bits(run(T, Dev(p, T), op=op))
+    assert np.array_equal(y, synth.to_bf16_bits(oracle_y(p).astype(np.float32)))
+
+
+@pytest.mark.parametrize("op,axis,i,o,M,k", [("gemv", 1, 256, 1, 1, 2), ("gemv", 1, 256, 1, 1, 3),
+                                             ("scatter", 0, 1, 256, 1, 3), ("scatter", 0, 1, 256, 1, 2),
+                                             (None, 1, 256, 1, 32, 4), (None, 1, 256, 17, 3, 3),
+                                             (None, 0, 1, 256, 32, 2), (None, 0, 9, 256, 17, 4)])
+def test_minimal_shapes(gpu_lib, op, axis, i, o, M, k):
+    """One block per row, a single output row, a single stored row."""
+    T = gpu_lib
+    p = synth.make_problem(synth.Shape(axis, 256, L, k, i, o), M, CFG["test"], proj=1200 + i + o)
+    say(f"minimal op={op or 'prefill'} axis={axis} in={i} out={o} M={M} k={k}")
+    y = bf16_to_f64(run(T, Dev(p, T), op=op))
+    assert gate(y, oracle_y(p)) <= TOL
+
+
 # ------------------------------------------------------------ dual GEMV
 def dual_case(T, shape, proj, check_oracle=True):
     """gate/up pair sharing x: bit-identical to two trellis_gemv calls, and
