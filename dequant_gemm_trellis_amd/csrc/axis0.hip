@@ -27,7 +27,8 @@
 // part, and the reduce kernel sums the parts in a fixed order. Every order is
 // fixed, so repeated calls give identical bits.
 //
-// The codebook (or pair table) is staged once per workgroup, and the next
+// The decode table (the k = 2 pair table, or eight bank-partitioned copies of
+// the codebook for k = 3, 4) is staged once per workgroup, and the next
 // step's words, scales and activations are in flight in registers while one
 // step is decoded (the first-generation kernel, one wave per split, four per
 // workgroup, restaged the codebook in 1280 workgroups and waited on every

@@ -245,6 +245,7 @@ __device__ __forceinline__ Gathered<false> gather_run64_rep(const uint32_t (&w)[
 // thread tid stages entries tid + NTHREADS i, one register each.
 template <int NTHREADS>
 struct RepSrc {
+    static_assert(kLutEntries % NTHREADS == 0, "every thread stages the same number of entries");
     static constexpr int n = kLutEntries / NTHREADS;
     float a[n];
 };

@@ -13,7 +13,8 @@
 // moves 4 or 8 bytes per lane, so for k = 2 the kernel reads a pair table
 // instead (one gather per two weights; see stage_pair_table). For k = 3 and 4
 // the pair index would be 15/16 bits (256/512 KB) and does not fit in LDS, so
-// those read the 16 KB codebook directly.
+// those read the codebook itself, from eight bank-partitioned copies that cut
+// the bank conflicts (see kRepCopies).
 //
 // Work mapping. The grid is persistent: one 512-thread workgroup (8 waves)
 // per compute unit, workgroup g owning rows [g N / G, (g+1) N / G), so every CU gets the
