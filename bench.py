@@ -54,9 +54,16 @@ def log(msg: str) -> None:
 
 
 def kernel_hash() -> str:
+    """Hash of the GEMV kernel's sources with comments and whitespace removed,
+    so that the stored traffic counters stay valid across comment edits."""
+    import re
+
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(open(f, "rb").read())
+        text = open(f, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
