@@ -198,7 +198,9 @@ __device__ __forceinline__ void a0_decode(const A0Step<MT>& st, const A0Ctx& cx,
             constexpr int p = decltype(pc)::value;
             floatx2 (&cur)[8] = (p & 1) ? vb : va;
             floatx2 (&nxt)[8] = (p & 1) ? va : vb;
+            __builtin_amdgcn_s_setprio(2);
             if constexpr (p + 1 < 4) gather(std::integral_constant<int, p + 1>{}, nxt);
+            __builtin_amdgcn_s_setprio(0);
             u32x4 b0, b1;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
@@ -225,7 +227,9 @@ __device__ __forceinline__ void a0_decode(const A0Step<MT>& st, const A0Ctx& cx,
             constexpr int e = decltype(ec)::value;
             float (&cur)[8] = (e & 1) ? vb : va;
             float (&nxt)[8] = (e & 1) ? va : vb;
+            __builtin_amdgcn_s_setprio(2);  // the gathers issue at raised priority
             if constexpr (e + 1 < 8) gather(std::integral_constant<int, e + 1>{}, nxt);
+            __builtin_amdgcn_s_setprio(0);
             u32x4 bq;
 #pragma unroll
             for (int d = 0; d < 4; ++d)

@@ -317,7 +317,9 @@ __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& 
     static_for<0, 8>([&](auto ic) {
         constexpr int S = 7 - decltype(ic)::value;
         Gathered<P> g2;
+        __builtin_amdgcn_s_setprio(2);  // the gathers issue at raised priority
         if constexpr (S >= 2) g2 = gather_tab<K, S - 2, P, REP>(t.w, tab);
+        __builtin_amdgcn_s_setprio(0);
         const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g0, t.scale));
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)

@@ -169,7 +169,13 @@ __device__ __forceinline__ void run_step(Step<K> st, XFrag& xf, uint32_t& xb,
     });
     static_for<0, 8>([&](auto ic) {
         constexpr int S = 7 - decltype(ic)::value;
+        // Raised wave priority while a fragment's gathers issue, so the other
+        // wave of the SIMD does not hold them back with its packing work and
+        // the LDS queue stays fed (1-2% faster; around the packing instead,
+        // no faster).
+        __builtin_amdgcn_s_setprio(2);
         if constexpr (S >= D) g[S - D] = gemv_gather<K, S - D>(st.w, tab);
+        __builtin_amdgcn_s_setprio(0);
         const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g[S], st.scale));
         acc = mfma16x16x32(as_bf16x8(xf.v[S]), bfrag, acc);
     });
@@ -405,7 +411,9 @@ __device__ __forceinline__ void run_rows_step(Step<K> st, const XFrag& xf, const
     });
     static_for<0, 8>([&](auto ic) {
         constexpr int S = 7 - decltype(ic)::value;
+        __builtin_amdgcn_s_setprio(2);  // as in run_step
         if constexpr (S >= D) g[S - D] = gather_tab<K, S - D, P, REP>(st.w, tab);
+        __builtin_amdgcn_s_setprio(0);
         const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g[S], st.scale));
         d1 = mfma16x16x32(as_bf16x8(xf.v[S]), bfrag, d1);
         if constexpr (STRAD) d2 = mfma16x16x32(as_bf16x8(xn.v[S]), bfrag, d2);
