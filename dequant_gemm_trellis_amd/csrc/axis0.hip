@@ -166,9 +166,9 @@ __device__ __forceinline__ void a0_load(A0Step<MT>& st, const A0Ctx& cx, int s) 
     });
 }
 
-// Decode a step's 8 x 8 patch and multiply, column by column (k = 3, 4) or
-// column pair by column pair (k = 2), the next column's gathers in flight
-// while one is packed and multiplied.
+// Decode a step's 8 x 8 patch and multiply, column by column (k = 3, 4; the
+// next two columns' gathers in flight while one is packed and multiplied) or
+// column pair by column pair (k = 2, the next pair's gathers in flight).
 template <int K, int MT, bool VEC>
 __device__ __forceinline__ void a0_decode(const A0Step<MT>& st, const A0Ctx& cx, int sh,
                                           const float* __restrict__ tab, uint32_t cofs,
@@ -221,14 +221,14 @@ __device__ __forceinline__ void a0_decode(const A0Step<MT>& st, const A0Ctx& cx,
 #pragma unroll
             for (int i = 0; i < 8; ++i) v[i] = lds_lut(tab, field_offset<o, kL, 5>(g[i]) | cofs);
         };
-        float va[8], vb[8];
-        gather(std::integral_constant<int, 0>{}, va);
+        float v3[3][8];
+        gather(std::integral_constant<int, 0>{}, v3[0]);
+        gather(std::integral_constant<int, 1>{}, v3[1]);
         static_for<0, 8>([&](auto ec) {
             constexpr int e = decltype(ec)::value;
-            float (&cur)[8] = (e & 1) ? vb : va;
-            float (&nxt)[8] = (e & 1) ? va : vb;
+            float (&cur)[8] = v3[e % 3];
             __builtin_amdgcn_s_setprio(2);  // the gathers issue at raised priority
-            if constexpr (e + 1 < 8) gather(std::integral_constant<int, e + 1>{}, nxt);
+            if constexpr (e + 2 < 8) gather(std::integral_constant<int, e + 2>{}, v3[(e + 2) % 3]);
             __builtin_amdgcn_s_setprio(0);
             u32x4 bq;
 #pragma unroll
