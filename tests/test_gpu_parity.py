@@ -394,6 +394,29 @@ def test_axis0_workspace_reused_across_shapes(gpu_lib):
         assert gate(bf16_to_f64(y.reshape(M, -1)), oracle_y(p)) <= TOL
 
 
+@pytest.mark.parametrize("fill", [0x00, 0xFF])
+def test_axis0_workspace_contents_do_not_matter(gpu_lib, fill):
+    """Workspace bytes all zero or all ones on entry, then the same call five
+    times in a row on it (each call leaves its flags behind for the next):
+    every result bit-identical and within tolerance of the oracle."""
+    T = gpu_lib
+    sh = synth.Shape(0, 256, L, 3, 3000, 1024)
+    for M in (1, 4, 20):
+        p = synth.make_problem(sh, M, CFG["test"], proj=760 + M)
+        d = Dev(p, T)
+        nbytes = T.workspace_bytes(sh, M, T.OP_PREFILL)
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda:0").view(torch.float32)
+        say(f"axis0 workspace filled {fill:#04x} M={M}")
+        ys = []
+        for _ in range(5):
+            y = (T.gemv_scatter(d.x.reshape(-1), d.codes, d.scales, d.lut, sh, workspace=ws)
+                 if M == 1 else T.prefill(d.x, d.codes, d.scales, d.lut, sh, workspace=ws))
+            ys.append(bf16_bits(y.reshape(M, -1)).copy())
+        torch.cuda.synchronize()
+        assert all(np.array_equal(ys[0], v) for v in ys[1:])
+        assert gate(bf16_to_f64(y.reshape(M, -1)), oracle_y(p)) <= TOL
+
+
 def test_prefill_deterministic(gpu_lib):
     T = gpu_lib
     shape = synth.Shape(1, 256, L, 2, QWEN_IN, QWEN_OUT)
