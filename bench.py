@@ -36,11 +36,12 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, AMD published
 CUS, CLOCK_HZ = 256, 2.4e9      # MI355X compute units and peak engine clock
 # Codebook-gather ceiling, decoded weights per clock per CU, measured on MI355X
-# with a random-index LDS gather microbenchmark (uniform 12-bit indices, 8
-# waves per CU): ds_read_b64 from the 128 KB k = 2 pair table (two weights per
-# lane) and ds_read_b32 from the eight bank-partitioned codebook copies the
-# k = 3, 4 GEMV reads (128 KB; a single 16 KB copy gives 8.4).
-GATHER_PEAK_W_PER_CLK = {2: 17.07, 3: 10.43, 4: 10.43}
+# with a random-index LDS gather microbenchmark (uniform random indices into a
+# 128 KB table, 512-thread workgroups, 8 waves per CU): ds_read_b64 as from the
+# k = 2 pair table (two weights per lane, 7.21 clocks per wave-wide read) and
+# ds_read_b32 from eight bank-partitioned codebook copies as the k = 3, 4 GEMV
+# reads them (6.14 clocks; a single copy gives 8.4 values per clock).
+GATHER_PEAK_W_PER_CLK = {2: 17.75, 3: 10.43, 4: 10.43}
 MALL_BYTES = 256 << 20
 QWEN_IN, QWEN_OUT = 5120, 17408
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_qwen_up_k2.json")
