@@ -88,17 +88,22 @@ def test_gemv_small(gpu_lib, i, o, k):
     assert gate(y, oracle_y(p)) <= TOL
 
 
+@pytest.mark.parametrize("i,o", [(QWEN_IN, 80000), (46 * 256, 30000)])
 @pytest.mark.parametrize("k", [2, 4])
-def test_gemv_rows_in_several_chunks(gpu_lib, k):
-    """30000 rows of 5120: 118 rows per workgroup, more than the 102 unit
-    partials of 20 blocks the persistent kernel holds in LDS at once, so each
-    workgroup runs two row chunks. Checked on rows spread over the range."""
+def test_gemv_rows_in_several_chunks(gpu_lib, i, o, k):
+    """More rows per workgroup than the unit partials the persistent kernel
+    holds in LDS at once (what the staged activations leave: 5552 units, i.e.
+    277 rows of 20 blocks, or 2120 units, 46 rows of 46 blocks), so each
+    workgroup runs several row chunks: 313 rows of 20 blocks (two chunks) and
+    118 rows of 46 blocks, the longest rows the kernel stages (three).
+    Checked on rows spread over the range."""
     T = gpu_lib
-    shape = synth.Shape(1, 256, L, k, QWEN_IN, 30000)
+    shape = synth.Shape(1, 256, L, k, i, o)
     p = synth.make_problem(shape, 1, CFG["test"], proj=800 + k)
-    say(f"gemv in=5120 out=30000 k={k} (two row chunks per workgroup)")
+    say(f"gemv in={i} out={o} k={k} (several row chunks per workgroup)")
     y = bf16_to_f64(run(T, Dev(p, T), op="gemv"))
-    rows = np.unique(np.concatenate([np.arange(0, 30000, 97), np.arange(100, 120), [29999]]))
+    rows = np.unique(np.concatenate([np.arange(0, o, 97), np.arange(100, 120),
+                                     np.arange(o - 20, o)]))
     assert gate(y[:, rows], oracle_y(row_subset(p, rows))) <= TOL
 
 
