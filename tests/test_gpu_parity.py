@@ -292,16 +292,17 @@ def test_prefill_one_hot_rows_bit_exact(gpu_lib):
         assert np.array_equal(y[m, SAMPLE_ROWS], W[:, c]), (m, c)
 
 
-# ------------------------------------- axis 1, up to 8 rows in the GEMV's unit mapping
+# ------------------------------------- axis 1, up to 4 rows in the GEMV's unit mapping
 @pytest.mark.parametrize("k", [2, 3, 4])
 @pytest.mark.parametrize("N", [16, 31, 300, 4111])
-@pytest.mark.parametrize("M", [2, 4, 5, 8])
+@pytest.mark.parametrize("M", [2, 3, 4, 5, 8])
 def test_rows_kernel_ragged(gpu_lib, N, M, k):
-    """Up to 8 activation rows (4 at k = 2) take the GEMV's unit mapping with
-    M outputs per unit: one workgroup of exactly 16 rows, one of 31,
-    workgroups of 16-17 rows (a step can straddle a block edge right after
-    entering a block), and 4111 rows over every compute unit. k = 2 with more
-    than 4 rows takes the 16-row-group kernel."""
+    """Up to 4 activation rows take the GEMV's unit mapping with M outputs per
+    unit (at k = 3, 4 on the codebook copies when the partials fit in one
+    chunk): one workgroup of exactly 16 rows, one of 31, workgroups of 16-17
+    rows (a step can straddle a block edge right after entering a block), and
+    4111 rows over every compute unit. 5 and 8 rows take the 16-row-group
+    kernel with directly loaded activations."""
     T = gpu_lib
     shape = synth.Shape(1, 256, L, k, 1024, N)
     p = synth.make_problem(shape, M, CFG["test"], proj=700 + M)
@@ -314,7 +315,8 @@ def test_rows_kernel_ragged(gpu_lib, N, M, k):
 @pytest.mark.parametrize("M", [3, 7])
 def test_rows_kernel_one_or_two_blocks_per_row(gpu_lib, i, M):
     """One block per row (no step can straddle) and two (the interleaved
-    layout coincides with the row-major one)."""
+    layout coincides with the row-major one); M = 3 in the GEMV's unit
+    mapping, M = 7 in 16-row groups."""
     T = gpu_lib
     k = 3
     for il in (0, 2):
@@ -330,38 +332,41 @@ def test_rows_kernel_one_or_two_blocks_per_row(gpu_lib, i, M):
 
 
 def test_rows_kernel_two_chunks_k4(gpu_lib):
-    """Rows of 128 blocks at M = 6: 32 rows' partials fit beside the codebook,
-    so 34-row workgroups run two chunks of 17 rows."""
+    """Rows of 256 blocks at M = 4: beside the codebook copies fewer than 16
+    rows' partials fit, so the kernel reads the single codebook, beside which
+    32 rows' partials fit: 40-row workgroups run two chunks of 20 rows."""
     T = gpu_lib
-    shape = synth.Shape(1, 256, L, 4, 32768, 8704)
-    p = synth.make_problem(shape, 6, CFG["test"], proj=710)
-    say("rows kernel in=32768 out=8704 M=6 k=4")
+    shape = synth.Shape(1, 256, L, 4, 65536, 10240)
+    p = synth.make_problem(shape, 4, CFG["test"], proj=710)
+    say("rows kernel in=65536 out=10240 M=4 k=4")
     y = bf16_to_f64(run(T, Dev(p, T)))
-    rows = np.concatenate([np.arange(0, 40), np.arange(4340, 4380), np.arange(8664, 8704)])
+    rows = np.concatenate([np.arange(0, 45), np.arange(5100, 5140), np.arange(10200, 10240)])
     assert gate(y[:, rows], oracle_y(row_subset(p, rows))) <= TOL
 
 
 def test_rows_kernel_falls_back_when_partials_do_not_fit(gpu_lib):
-    """64 blocks per row at M = 8, k = 2: fewer than 16 rows' partials fit
+    """128 blocks per row at M = 4, k = 2: fewer than 16 rows' partials fit
     beside the pair table, so the call takes the 16-row-group kernel."""
     T = gpu_lib
-    shape = synth.Shape(1, 256, L, 2, 16384, 300)
-    p = synth.make_problem(shape, 8, CFG["test"], proj=720)
-    say("rows kernel fallback in=16384 out=300 M=8 k=2")
+    shape = synth.Shape(1, 256, L, 2, 32768, 300)
+    p = synth.make_problem(shape, 4, CFG["test"], proj=720)
+    say("rows kernel fallback in=32768 out=300 M=4 k=2")
     y = bf16_to_f64(run(T, Dev(p, T)))
     assert gate(y, oracle_y(p)) <= TOL
 
 
+@pytest.mark.parametrize("M", [4, 8])
 @pytest.mark.parametrize("k", [2, 3, 4])
-def test_rows_kernel_one_hot_bit_exact(gpu_lib, k):
-    """Eight one-hot activation rows at the Qwen-up shape: each output row is
-    one stored column exactly."""
+def test_rows_kernel_one_hot_bit_exact(gpu_lib, k, M):
+    """Four one-hot activation rows (the GEMV's unit mapping) and eight
+    (16-row groups, activations loaded directly) at the Qwen-up shape: each
+    output row is one stored column exactly."""
     T = gpu_lib
     shape = synth.Shape(1, 256, L, k, QWEN_IN, QWEN_OUT)
-    cols = [0, 255, 256, 2047, 2048, 4095, 5119, 1000]
-    p0 = synth.make_problem(shape, 8, CFG["qwen_up_prefill"], proj=730)
-    p = with_x(p0, synth.one_hot_x(8, QWEN_IN, cols))
-    say(f"rows kernel one-hot M=8 k={k}")
+    cols = [0, 255, 256, 2047, 2048, 4095, 5119, 1000][:M]
+    p0 = synth.make_problem(shape, M, CFG["qwen_up_prefill"], proj=730)
+    p = with_x(p0, synth.one_hot_x(M, QWEN_IN, cols))
+    say(f"rows kernel one-hot M={M} k={k}")
     y = bf16_bits(run(T, Dev(p, T)))
     W = oracle_W(row_subset(p, SAMPLE_ROWS))
     for m, c in enumerate(cols):
