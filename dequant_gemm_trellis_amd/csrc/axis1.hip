@@ -72,7 +72,7 @@ struct PrefillShape {
 template <int K, int MT, bool DIRECT>
 struct PrefillLds {
     static constexpr bool pair = K == 2;
-    // k = 3, 4 with activations loaded directly (M <= 8): the bank-partitioned
+    // k = 3, 4 with activations loaded directly (one M tile, M <= 16): the bank-partitioned
     // codebook copies (128 KB). Staged activations keep the 16 KB codebook:
     // beside the copies only a one-line slot fits, which measured 0-2% slower.
     static constexpr bool rep = !pair && DIRECT;
