@@ -36,6 +36,13 @@
  *     allocates nothing and keeps no reference after the call returns.
  *   - x, codes, lut, y and workspace must be 16-byte aligned; scales 4-byte.
  *     Arrays are dense and row-major (no strides).
+ *   - Outputs (y, workspace) must not overlap the inputs (x, codes, scales,
+ *     lut) or each other: kernels read inputs while other workgroups already
+ *     write outputs. Only the overlaps named at an entry point are checked;
+ *     any other gives undefined results.
+ *   - The arrays and the stream belong to the current HIP device; launch
+ *     shapes are sized from its compute-unit count (results do not depend on
+ *     it).
  *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
  *     without waiting. All validation happens on the host before anything is
  *     enqueued: on a negative status nothing was enqueued. A kernel fault
