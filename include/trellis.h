@@ -41,8 +41,8 @@
  *     write outputs. Only the overlaps named at an entry point are checked;
  *     any other gives undefined results.
  *   - The arrays and the stream belong to the current HIP device; launch
- *     shapes are sized from its compute-unit count (results do not depend on
- *     it).
+ *     shapes are sized from its compute-unit count (so bits can differ
+ *     between devices with different counts, never between calls on one).
  *   - Work is enqueued on `stream` (0 = the null stream) and the call returns
  *     without waiting. All validation happens on the host before anything is
  *     enqueued: on a negative status nothing was enqueued. A kernel fault
