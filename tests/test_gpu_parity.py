@@ -607,8 +607,11 @@ def dual_case(T, shape, proj, check_oracle=True):
 
 
 @pytest.mark.parametrize("i,o,k,il", [(512, 256, 2, 0), (768, 300, 3, 0), (1024, 20, 4, 0),
-                                      (4096, 4111, 2, 2), (2048, 1000, 3, 2)])
+                                      (4096, 4111, 2, 2), (2048, 1000, 3, 2),
+                                      (256, 1, 2, 0), (256, 1, 4, 0), (512, 1, 3, 2)])
 def test_gemv_dual_small(gpu_lib, i, o, k, il):
+    """Ragged row counts, both layouts, and one output row (one workgroup per
+    projection)."""
     T = gpu_lib
     say(f"gemv_dual in={i} out={o} k={k} interleave={il}")
     pa, pb, ya, yb = dual_case(T, synth.Shape(1, 256, L, k, i, o, il), 1100 + k)
