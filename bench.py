@@ -127,7 +127,10 @@ def gemv_bench(T, torch, dev, k, steps, warmup):
 
     ms = time_calls(torch, launch, len(sets.items), steps, warmup)
     warm = time_calls(torch, lambda i: launch(0), 1, max(steps // 4, 10), 5)
+    # every byte the call must move: codes, scales, x, y and the codebook
+    alg_bytes = code_bytes + 4 * shape.rows + 2 * shape.cols + 2 * shape.rows + 4 * 4096
     res = {"us_per_call": ms * 1e3, "gbps": code_bytes / (ms * 1e-3) / 1e9,
+           "alg_bytes": alg_bytes, "alg_gbps": alg_bytes / (ms * 1e-3) / 1e9,
            "frac_hbm": code_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "decode_w_per_clk_cu": shape.rows * shape.cols / (ms * 1e-3) / CUS / CLOCK_HZ,
            "frac_decode_ceiling": shape.rows * shape.cols / (ms * 1e-3) / CUS / CLOCK_HZ
