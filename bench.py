@@ -126,6 +126,8 @@ def gemv_bench(T, torch, dev, k, steps, warmup):
         T.gemv(x, codes, scales, lut, geom, y=y)
 
     ms = time_calls(torch, launch, len(sets.items), steps, warmup)
+    # five more timed runs of the same length: the spread behind the one figure
+    reps = sorted(time_calls(torch, launch, len(sets.items), steps, 0) * 1e3 for _ in range(5))
     warm = time_calls(torch, lambda i: launch(0), 1, max(steps // 4, 10), 5)
     # every byte the call must move: codes, scales, x, y and the codebook
     alg_bytes = code_bytes + 4 * shape.rows + 2 * shape.cols + 2 * shape.rows + 4 * 4096
@@ -135,6 +137,7 @@ def gemv_bench(T, torch, dev, k, steps, warmup):
            "decode_w_per_clk_cu": shape.rows * shape.cols / (ms * 1e-3) / CUS / CLOCK_HZ,
            "frac_decode_ceiling": shape.rows * shape.cols / (ms * 1e-3) / CUS / CLOCK_HZ
                                   / GATHER_PEAK_W_PER_CLK[k],
+           "us_per_call_5_reps": {"median": reps[2], "min": reps[0], "max": reps[4]},
            "code_bytes": code_bytes, "rotation_sets": len(sets.items),
            "us_per_call_mall_resident": warm * 1e3}
     first = sets.first
@@ -328,7 +331,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
+    # about 15 ms of GEMV calls: shorter warm-ups (50 calls) timed 3-5% slower
+    # than the same calls repeated right afterwards
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--extra", action="store_true", help="also time scatter, prefill and MLP")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -383,7 +388,7 @@ def main() -> int:
     extra = None
     if args.extra or args.only_extra:
         log("bench: extra workloads")
-        extra = extra_bench(T, torch, dev, max(args.steps // 4, 20), 10,
+        extra = extra_bench(T, torch, dev, max(args.steps // 4, 20), max(args.warmup // 4, 10),
                             only=set(args.only_extra.split(",")) if args.only_extra else None)
 
     cpu = None
