@@ -8,6 +8,7 @@ import ctypes as C
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -250,3 +251,12 @@ def test_repack_validation(T):
     assert rp(FAKE, FAKE, g, 2) == T.ERR_OVERLAP
     assert rp(FAKE, FAKE + 65536 - 16, g, 2) == T.ERR_OVERLAP
     assert rp(FAKE + 65536 - 16, FAKE, g, 0) == T.ERR_OVERLAP
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU; a request for more exits with status 2
+    and says why, before touching any device."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
