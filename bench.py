@@ -308,8 +308,17 @@ def cpu_baseline(p, seconds: float):
             break
     per_call = el * s.rows / rows_done
     code_bytes = s.rows * s.words_per_row * 4
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": code_bytes / per_call / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "us_per_call": per_call * 1e6,
+            "us_per_call": per_call * 1e6, "host_cpu": cpu_model,
             "sample": f"{rows_done} output rows x 5120 inputs of the k=2 GEMV "
                       f"({el:.1f} s), scaled to the full 17408-row call; "
                       f"host has {os.cpu_count()} logical cores"}
