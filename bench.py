@@ -148,7 +148,7 @@ def gemv_bench(T, torch, dev, k, steps, warmup):
 
 def extra_bench(T, torch, dev, steps, warmup, only=None):
     """Other workloads: axis-0 scatter k=3 (and its geometry at M=2/4/8), prefill
-    M=2/4/5/8/16/32, MLP k=4 M=1/32,
+    M=2/4/5/8/16/32, MLP k=4 M=1/8/32,
     and the scatter and the k=2 GEMV on block-interleave-2 codes (the same
     uniform random words, read in the pair layout)."""
     from dequant_gemm_trellis_amd import synth
@@ -204,7 +204,7 @@ def extra_bench(T, torch, dev, steps, warmup, only=None):
                         len(sets.items), steps, warmup)
         out[name] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
         del sets
-    for M in (1, 32):
+    for M in (1, 8, 32):
         if want(f"mlp_k4_M{M}"):
             mlp_bench(T, torch, dev, M, steps, warmup, out)
     torch.cuda.empty_cache()
@@ -235,8 +235,9 @@ def scatter_bench(T, torch, dev, steps, warmup, only, out):
 
 
 def mlp_bench(T, torch, dev, M, steps, warmup, out):
-    """The MLP workload: gate and up (axis 1, the same activations; at M=1 one
-    dual-GEMV launch, also timed as two GEMVs) then down (axis 0), k=4."""
+    """The MLP workload: gate and up (axis 1, the same activations, through the
+    dual entry points: one launch at M=1 and 5..16, also timed as two separate
+    calls) then down (axis 0), k=4."""
     from dequant_gemm_trellis_amd import synth
 
     C = synth.CONFIG_IDS
@@ -268,23 +269,26 @@ def mlp_bench(T, torch, dev, M, steps, warmup, out):
             T.gemv_dual(x, projs[0].items[i][1:], projs[1].items[i][1:], geoms[0],
                         y_a=ys[0].reshape(-1), y_b=ys[1].reshape(-1))
         else:
-            for j in range(2):
-                _, codes, scales, lut = projs[j].items[i]
-                T.prefill(x, codes, scales, lut, geoms[j], y=ys[j])
+            T.prefill_dual(x, projs[0].items[i][1:], projs[1].items[i][1:], geoms[0],
+                           y_a=ys[0], y_b=ys[1])
         down(i)
 
     def mlp_separate(i):
         x = projs[0].items[i][0]
         for j in range(2):
             _, codes, scales, lut = projs[j].items[i]
-            T.gemv(x, codes, scales, lut, geoms[j], y=ys[j].reshape(-1))
+            if M == 1:
+                T.gemv(x, codes, scales, lut, geoms[j], y=ys[j].reshape(-1))
+            else:
+                T.prefill(x, codes, scales, lut, geoms[j], y=ys[j])
         down(i)
 
     ms = time_calls(torch, mlp, n, max(steps // 3, 10), warmup)
     out[f"mlp_k4_M{M}"] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
-    if M == 1:
+    if M <= 16:
         ms = time_calls(torch, mlp_separate, n, max(steps // 3, 10), warmup)
-        out["mlp_k4_M1_separate_gemvs"] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
+        name = "mlp_k4_M1_separate_gemvs" if M == 1 else f"mlp_k4_M{M}_separate_prefills"
+        out[name] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
     del projs
 
 

@@ -162,6 +162,38 @@ int trellis_prefill(const uint16_t* x, int32_t M, const uint32_t* codes, const f
                                            d.cols, g->k, stream));
 }
 
+int trellis_prefill_dual(const uint16_t* x, int32_t M, const uint32_t* codes_a,
+                         const float* scales_a, const float* lut_a, uint16_t* y_a,
+                         const uint32_t* codes_b, const float* scales_b, const float* lut_b,
+                         uint16_t* y_b, const trellis_geometry* g, hipStream_t stream) {
+    Dims d;
+    int st = check_geometry(g, &d);
+    if (st) return st;
+    if (g->axis != 1) return TRELLIS_ERR_GEOMETRY;
+    if (M < 0 || M > TRELLIS_MAX_M) return TRELLIS_ERR_GEOMETRY;
+    if ((st = check_operands(codes_a, scales_a, lut_a)) || (st = check_io(x, y_a)) ||
+        (st = check_operands(codes_b, scales_b, lut_b)) || (st = check_io(x, y_b)))
+        return st;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(y_a), b = reinterpret_cast<uintptr_t>(y_b);
+    const uintptr_t bytes = static_cast<uintptr_t>(M) * static_cast<uintptr_t>(d.rows) * sizeof(uint16_t);
+    if (a < b + bytes && b < a + bytes) return TRELLIS_ERR_OVERLAP;
+    if (M == 0) return TRELLIS_OK;
+    if (M == 1)
+        return trellis_gemv_dual(x, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b,
+                                 g, stream);
+    // 2..16 rows: one launch of the 16-row-group kernel over both projections
+    // (at 5120 -> 17408 measured 16-24% faster than two launches at 5..16
+    // rows, and 10-13% faster than two launches of the small-batch kernel at
+    // 2..4). More than 16 rows take two M tiles, one launch per projection.
+    if (trellis::axis1_dual_supported(M, d.rows, g->k))
+        return status_of(trellis::launch_axis1_dual(x, M, codes_a, scales_a, lut_a, y_a, codes_b,
+                                                    scales_b, lut_b, y_b, d.lay, d.rows, d.nb,
+                                                    g->k, stream));
+    if ((st = status_of(launch_axis1_any(x, M, codes_a, scales_a, lut_a, y_a, d, g->k, stream))))
+        return st;
+    return status_of(launch_axis1_any(x, M, codes_b, scales_b, lut_b, y_b, d, g->k, stream));
+}
+
 size_t trellis_workspace_bytes(const trellis_geometry* g, int32_t M, int32_t op) {
     Dims d;
     if (check_geometry(g, &d)) return static_cast<size_t>(-1);

@@ -53,6 +53,7 @@ namespace {
 
 constexpr int kThreads = 256;    // expand kernel
 constexpr int kGroups = 5;       // 16-row groups per prefill workgroup (80 rows)
+constexpr int kDualGroups = 9;   // the same for the two-projection launch (144 rows)
 constexpr int kDirectMaxM = 8;   // largest M whose activation fragments are loaded directly
 
 // Prefill workgroup size: 8 waves, two per SIMD. For one M tile this
@@ -69,7 +70,7 @@ struct PrefillShape {
 // chunks of 16 bytes) of each of the 16 rows of each M tile. Beside the 128 KB
 // pair table only one line fits (2 KB per tile); beside the 16 KB codebook all
 // four do.
-template <int K, int MT, bool DIRECT>
+template <int K, int MT, bool DIRECT, int KG = kGroups>
 struct PrefillLds {
     static constexpr bool pair = K == 2;
     // k = 3, 4 with activations loaded directly (one M tile, M <= 16): the bank-partitioned
@@ -82,7 +83,7 @@ struct PrefillLds {
     static constexpr int lines = tab_floats > kLutEntries ? 1 : 4;
     static constexpr int slot_chunks = DIRECT ? 0 : MT * lines * 16 * 8;
     static constexpr int decode_floats = tab_floats + waves * slot_chunks * 4;
-    static constexpr int part_floats = waves * kGroups * 256;  // one M tile of wave partials
+    static constexpr int part_floats = waves * KG * 256;  // one M tile of wave partials
     static constexpr int floats = decode_floats > part_floats ? decode_floats : part_floats;
 };
 
@@ -279,9 +280,9 @@ struct XSource {
 // block change earlier (or in the prologue), which then fetches the next
 // block's; on the staged path through the LDS slot, the one memory wait that
 // covers the prefetched code words.
-template <int K, int MT, bool DIRECT>
+template <int K, int MT, bool DIRECT, int KG>
 __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& xn, int& xb,
-                                         const XSource<MT>& xs, floatx4 (&acc)[kGroups][MT],
+                                         const XSource<MT>& xs, floatx4 (&acc)[KG][MT],
                                          const float* __restrict__ tab, int lane, int j, int c) {
     constexpr bool P = PrefillLds<K, MT, DIRECT>::pair;
     constexpr bool REP = PrefillLds<K, MT, DIRECT>::rep;
@@ -302,7 +303,7 @@ __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& 
     // The group's accumulators move in and out under uniform branches (the
     // empty asm keeps each a branch: as selects they cost 36 VALU per task).
     floatx4 cur[MT];
-    static_for<0, kGroups>([&](auto gc) {
+    static_for<0, KG>([&](auto gc) {
         constexpr int G = decltype(gc)::value;
         if (t.g == G) {
             asm volatile("");
@@ -327,7 +328,7 @@ __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& 
         g0 = g1;
         if constexpr (S >= 2) g1 = g2;
     });
-    static_for<0, kGroups>([&](auto gc) {
+    static_for<0, KG>([&](auto gc) {
         constexpr int G = decltype(gc)::value;
         if (t.g == G) {
             asm volatile("");
@@ -337,23 +338,36 @@ __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& 
     });
 }
 
-template <int K, int MT, bool DIRECT, bool PAIRS>
+// Two projections of the same geometry over the same activation rows (an
+// MLP's gate and up) can share one launch: workgroups below G0 compute y_a
+// from (codes_a, scales_a, lut_a), the others y_b from the b operands, each
+// half splitting its rows as one launch of its own would. A single
+// projection passes G0 = gridDim.x.
+template <int K, int MT, bool DIRECT, bool PAIRS, int KG>
 __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kernel(
-    const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
-    const float* __restrict__ scales, const float* __restrict__ lut,
-    uint16_t* __restrict__ y, CodeLayout lay, int N, int nb, int M) {
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes_a,
+    const float* __restrict__ scales_a, const float* __restrict__ lut_a,
+    uint16_t* __restrict__ y_a, const uint32_t* __restrict__ codes_b,
+    const float* __restrict__ scales_b, const float* __restrict__ lut_b,
+    uint16_t* __restrict__ y_b, int G0, CodeLayout lay, int N, int nb, int M) {
     constexpr int kThreadsP = PrefillShape<MT>::threads, kWaves = PrefillShape<MT>::waves;
-    using Lds = PrefillLds<K, MT, DIRECT>;
+    using Lds = PrefillLds<K, MT, DIRECT, KG>;
     __shared__ __attribute__((aligned(16))) float lds[Lds::floats];
     float* const tab = lds;
 
-    const int G = gridDim.x, wg = blockIdx.x;
+    const bool second = static_cast<int>(blockIdx.x) >= G0;
+    const uint32_t* const codes = second ? codes_b : codes_a;
+    const float* const scales = second ? scales_b : scales_a;
+    const float* const lut = second ? lut_b : lut_a;
+    uint16_t* const y = second ? y_b : y_a;
+    const int G = second ? static_cast<int>(gridDim.x) - G0 : G0;
+    const int wg = second ? static_cast<int>(blockIdx.x) - G0 : static_cast<int>(blockIdx.x);
     const int r0 = static_cast<int>(static_cast<long>(wg) * N / G);
     const int r1 = static_cast<int>(static_cast<long>(wg + 1) * N / G);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, c = lane >> 4, cp = 3 - c;
-    const int gc = (r1 - r0 + 15) >> 4;  // groups in this workgroup, <= kGroups
+    const int gc = (r1 - r0 + 15) >> 4;  // groups in this workgroup, <= KG
     const int tasks = gc * nb;
     const int tau0 = static_cast<int>(static_cast<long>(wave) * tasks / kWaves);
     const int tau1 = static_cast<int>(static_cast<long>(wave + 1) * tasks / kWaves);
@@ -379,9 +393,9 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     xs.nb = nb;
 
     TaskCtx cx{codes, lay, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp};
-    floatx4 acc[kGroups][MT];
+    floatx4 acc[KG][MT];
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g)
+    for (int g = 0; g < KG; ++g)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[g][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -408,11 +422,11 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     int xb = -1;  // block whose fragments xf holds
     for (int t0 = tau0; t0 < tau1; t0 += 3) {
         load_task<K, PAIRS>(tc, cx, t0 + 2, tau1);
-        run_task<K, MT, DIRECT>(ta, xf, xn, xb, xs, acc, tab, lane, j, c);
+        run_task<K, MT, DIRECT, KG>(ta, xf, xn, xb, xs, acc, tab, lane, j, c);
         load_task<K, PAIRS>(ta, cx, t0 + 3, tau1);
-        if (t0 + 1 < tau1) run_task<K, MT, DIRECT>(tb, xf, xn, xb, xs, acc, tab, lane, j, c);
+        if (t0 + 1 < tau1) run_task<K, MT, DIRECT, KG>(tb, xf, xn, xb, xs, acc, tab, lane, j, c);
         load_task<K, PAIRS>(tb, cx, t0 + 4, tau1);
-        if (t0 + 2 < tau1) run_task<K, MT, DIRECT>(tc, xf, xn, xb, xs, acc, tab, lane, j, c);
+        if (t0 + 2 < tau1) run_task<K, MT, DIRECT, KG>(tc, xf, xn, xb, xs, acc, tab, lane, j, c);
     }
     __syncthreads();  // the table is dead from here on; its space takes the partials
 
@@ -421,15 +435,15 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g)
+        for (int g = 0; g < KG; ++g)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                part[((wave * kGroups + g) * 16 + 4 * c + v) * 16 + j] = acc[g][mt][v];
+                part[((wave * KG + g) * 16 + 4 * c + v) * 16 + j] = acc[g][mt][v];
         __syncthreads();
         for (int idx = tid; idx < gc * 256; idx += kThreadsP) {
             const int g = idx >> 8, m = (idx >> 4) & 15, jj = idx & 15;
             float s = 0.f;
-            for (int w = 0; w < kWaves; ++w) s += part[((w * kGroups + g) * 16 + m) * 16 + jj];
+            for (int w = 0; w < kWaves; ++w) s += part[((w * KG + g) * 16 + m) * 16 + jj];
             const int row = r0 + 16 * g + jj, mm = 16 * mt + m;
             if (mm < M && row < r1) y[static_cast<size_t>(mm) * N + row] = round_bf16(s);
         }
@@ -474,12 +488,37 @@ hipError_t launch_axis1_k(const uint16_t* x, int M, const uint32_t* codes, CodeL
     // Row-major iff a row's blocks are contiguous (with two blocks per row the
     // two layouts coincide).
     if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
-        return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, false>, dim3(G),
-                             dim3(PrefillShape<MT>::threads), st, x, codes, scales, lut, y, lay, N,
-                             nb, M);
-    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, true>, dim3(G),
-                         dim3(PrefillShape<MT>::threads), st, x, codes, scales, lut, y, lay, N, nb,
-                         M);
+        return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, false, kGroups>, dim3(G),
+                             dim3(PrefillShape<MT>::threads), st, x, codes, scales, lut, y, codes,
+                             scales, lut, y, G, lay, N, nb, M);
+    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, true, kGroups>, dim3(G),
+                         dim3(PrefillShape<MT>::threads), st, x, codes, scales, lut, y, codes,
+                         scales, lut, y, G, lay, N, nb, M);
+}
+
+// Workgroups per projection of the two-projection launch: half the compute
+// units each, or one per 16-row group when there are fewer.
+int axis1_dual_groups(int N) {
+    const int groups = (N + 15) / 16;
+    const int half = cu_count() / 2 > 0 ? cu_count() / 2 : 1;
+    return groups < half ? groups : half;
+}
+
+template <int K, bool DIRECT>
+hipError_t launch_axis1_dual_k(const uint16_t* x, int M, const uint32_t* codes_a,
+                               const float* scales_a, const float* lut_a, uint16_t* y_a,
+                               const uint32_t* codes_b, const float* scales_b,
+                               const float* lut_b, uint16_t* y_b, CodeLayout lay, int N, int nb,
+                               hipStream_t st) {
+    const int G0 = axis1_dual_groups(N);
+    if ((N + G0 - 1) / G0 > 16 * kDualGroups) return hipErrorInvalidValue;  // checked by the caller
+    if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
+        return launch_kernel(axis1_prefill_kernel<K, 1, DIRECT, false, kDualGroups>, dim3(2 * G0),
+                             dim3(PrefillShape<1>::threads), st, x, codes_a, scales_a, lut_a, y_a,
+                             codes_b, scales_b, lut_b, y_b, G0, lay, N, nb, M);
+    return launch_kernel(axis1_prefill_kernel<K, 1, DIRECT, true, kDualGroups>, dim3(2 * G0),
+                         dim3(PrefillShape<1>::threads), st, x, codes_a, scales_a, lut_a, y_a,
+                         codes_b, scales_b, lut_b, y_b, G0, lay, N, nb, M);
 }
 
 template <int K>
@@ -510,6 +549,29 @@ hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLay
     case 16: return launch_axis1_k<4, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
     case 17: return launch_axis1_k<4, 1, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
     case 18: return launch_axis1_k<4, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool axis1_dual_supported(int M, int N, int k) {
+    if (M < 1 || M > 16 || N < 1 || k < 2 || k > 4) return false;
+    const int G0 = axis1_dual_groups(N);
+    return (N + G0 - 1) / G0 <= 16 * kDualGroups;
+}
+
+hipError_t launch_axis1_dual(const uint16_t* x, int M, const uint32_t* codes_a,
+                             const float* scales_a, const float* lut_a, uint16_t* y_a,
+                             const uint32_t* codes_b, const float* scales_b, const float* lut_b,
+                             uint16_t* y_b, CodeLayout lay, int N, int nb, int k,
+                             hipStream_t st) {
+    if (!axis1_dual_supported(M, N, k)) return hipErrorInvalidValue;
+    // one M tile; directly loaded activations as for the single launch
+    const bool direct = k == 2 ? M <= kDirectMaxM : true;
+    switch (k * 2 + (direct ? 1 : 0)) {
+    case 4: return launch_axis1_dual_k<2, false>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    case 5: return launch_axis1_dual_k<2, true>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    case 7: return launch_axis1_dual_k<3, true>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    case 9: return launch_axis1_dual_k<4, true>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
     default: return hipErrorInvalidValue;
     }
 }

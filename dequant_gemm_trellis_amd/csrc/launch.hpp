@@ -68,6 +68,17 @@ hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLay
                         const float* scales, const float* lut, uint16_t* y, int N, int nb, int k,
                         hipStream_t st);
 
+// Two axis-1 projections of one geometry over the same x[M][nb*256], 1 <= M
+// <= 16, in one launch of the 16-row-group kernel (half the compute units
+// each, at most 144 rows per workgroup); axis1_dual_supported says whether
+// the geometry fits.
+bool axis1_dual_supported(int M, int N, int k);
+hipError_t launch_axis1_dual(const uint16_t* x, int M, const uint32_t* codes_a,
+                             const float* scales_a, const float* lut_a, uint16_t* y_a,
+                             const uint32_t* codes_b, const float* scales_b, const float* lut_b,
+                             uint16_t* y_b, CodeLayout lay, int N, int nb, int k,
+                             hipStream_t st);
+
 // Axis 0, 1 <= M <= 32: per-part partials, then the ordered reduce over the
 // parts into y[M][C]. `partial` holds axis0_parts(R, C) * M * C floats.
 hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,

@@ -37,8 +37,8 @@ MAX_M = 32
 
 # Every function trellis.h declares, for the export check.
 EXPORTED = ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_dual", "trellis_gemv_scatter",
-            "trellis_prefill", "trellis_workspace_bytes", "trellis_expand", "trellis_repack",
-            "trellis_strerror")
+            "trellis_prefill", "trellis_prefill_dual", "trellis_workspace_bytes", "trellis_expand",
+            "trellis_repack", "trellis_strerror")
 
 
 class Geometry(C.Structure):
@@ -59,6 +59,8 @@ _lib.trellis_gemv.argtypes = [_vp, _vp, _vp, _vp, _GP, _vp, _vp]
 _lib.trellis_gemv_dual.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _GP, _vp]
 _lib.trellis_gemv_scatter.argtypes = [_vp, _vp, _vp, _vp, _GP, _vp, C.c_size_t, _vp, _vp]
 _lib.trellis_prefill.argtypes = [_vp, C.c_int32, _vp, _vp, _vp, _GP, _vp, C.c_size_t, _vp, _vp]
+_lib.trellis_prefill_dual.argtypes = [_vp, C.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _GP,
+                                      _vp]
 _lib.trellis_workspace_bytes.argtypes = [_GP, C.c_int32, C.c_int32]
 _lib.trellis_workspace_bytes.restype = C.c_size_t
 _lib.trellis_expand.argtypes = [_vp, _vp, _vp, _GP, _vp, _vp]
@@ -66,7 +68,7 @@ _lib.trellis_repack.argtypes = [_vp, _vp, _GP, C.c_int32, _vp]
 _lib.trellis_strerror.argtypes = [C.c_int]
 _lib.trellis_strerror.restype = C.c_char_p
 for _f in ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_dual", "trellis_gemv_scatter",
-           "trellis_prefill", "trellis_expand", "trellis_repack"):
+           "trellis_prefill", "trellis_prefill_dual", "trellis_expand", "trellis_repack"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -176,6 +178,22 @@ def prefill(x, codes, scales, lut, g, workspace=None, y=None, stream=None) -> to
         _dev(x), M, _dev(codes), _dev(scales), _dev(lut), C.byref(geom), _dev(workspace),
         ws_bytes, _dev(y), _stream(stream)))
     return y
+
+
+def prefill_dual(x, a, b, g, y_a=None, y_b=None, stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Two axis-1 prefills over the same x [M][in]; a and b are (codes,
+    scales, lut) triples of the same geometry g."""
+    geom = _geom(g)
+    M = x.shape[0] if x.dim() == 2 else 1
+    if y_a is None:
+        y_a = torch.empty((M, geom.out_features), dtype=torch.bfloat16, device=x.device)
+    if y_b is None:
+        y_b = torch.empty((M, geom.out_features), dtype=torch.bfloat16, device=x.device)
+    (ca, sa, la), (cb, sb, lb) = a, b
+    _check("trellis_prefill_dual", _lib.trellis_prefill_dual(
+        _dev(x), M, _dev(ca), _dev(sa), _dev(la), _dev(y_a), _dev(cb), _dev(sb), _dev(lb),
+        _dev(y_b), C.byref(geom), _stream(stream)))
+    return y_a, y_b
 
 
 def expand(codes, scales, lut, g, w=None, stream=None) -> torch.Tensor:

@@ -175,6 +175,27 @@ int trellis_prefill(const uint16_t *x, int32_t M, const uint32_t *codes, const f
                     size_t workspace_bytes, uint16_t *y, hipStream_t stream);
 
 /*
+ * Two axis-1 prefills of the same geometry over the same M activation rows,
+ * 0 <= M <= 32: the gate and up projections of a decoder MLP at prefill.
+ *   y_a[m][n] = bf16( sum_k x[m][k] * Wa[n][k] ),  y_b likewise with Wb
+ * with Wa from (codes_a, scales_a, lut_a) and Wb from (codes_b, scales_b,
+ * lut_b), each laid out as for trellis_prefill; g (axis 1) describes both;
+ * x: bf16 [M][in]; y_a, y_b: bf16 [M][out], not overlapping
+ * (TRELLIS_ERR_OVERLAP). For 2 <= M <= 16 one launch serves both (half the
+ * compute units each; the pages run each projection on its own, page 60
+ * tiled-prefill.ts, the shared launch is this library's); M = 1 is
+ * trellis_gemv_dual; other M enqueue the two projections one after the
+ * other, and should the runtime reject the second launch (TRELLIS_ERR_HIP),
+ * the first one stays enqueued. Results are within the prefill's tolerance of
+ * two trellis_prefill calls, not always bit-identical to them (the shared
+ * launch splits rows differently, which changes the float32 summation order).
+ */
+int trellis_prefill_dual(const uint16_t *x, int32_t M, const uint32_t *codes_a,
+                         const float *scales_a, const float *lut_a, uint16_t *y_a,
+                         const uint32_t *codes_b, const float *scales_b, const float *lut_b,
+                         uint16_t *y_b, const trellis_geometry *g, hipStream_t stream);
+
+/*
  * Workspace bytes an operation needs for geometry g and batch M (0 if it
  * needs none). Returns (size_t)-1 if g, M or op is not supported.
  */

@@ -126,6 +126,34 @@ def test_gemv_dual_validation(T):
     assert call_dual(T, g, y_a=FAKE + 4096 + 256) == T.ERR_OVERLAP
 
 
+def call_prefill_dual(T, g, M, **kw):
+    a = dict(x=FAKE, codes_a=FAKE, scales_a=FAKE, lut_a=FAKE, y_a=FAKE, codes_b=FAKE,
+             scales_b=FAKE, lut_b=FAKE, y_b=FAKE + (1 << 20))
+    a.update(kw)
+    names = ("codes_a", "scales_a", "lut_a", "y_a", "codes_b", "scales_b", "lut_b", "y_b")
+    return T.raw().trellis_prefill_dual(C.c_void_p(a["x"]), M, *[C.c_void_p(a[n]) for n in names],
+                                        C.byref(g) if g is not None else None, C.c_void_p(0))
+
+
+def test_prefill_dual_validation(T):
+    g = geom(T)  # 256 output rows: M rows of y span 512 M bytes
+    assert call_prefill_dual(T, None, 8) == T.ERR_NULL
+    assert call_prefill_dual(T, geom(T, axis=0, i=256, o=512), 8) == T.ERR_GEOMETRY
+    assert call_prefill_dual(T, g, -1) == T.ERR_GEOMETRY
+    assert call_prefill_dual(T, g, 33) == T.ERR_GEOMETRY
+    for arg in ("x", "codes_a", "scales_a", "lut_a", "y_a", "codes_b", "scales_b", "lut_b", "y_b"):
+        assert call_prefill_dual(T, g, 8, **{arg: 0}) == T.ERR_NULL, arg
+    for arg, addr in (("x", FAKE + 2), ("codes_b", FAKE + 4), ("lut_a", FAKE + 8),
+                      ("y_b", FAKE + (1 << 20) + 2), ("scales_b", FAKE + 2)):
+        assert call_prefill_dual(T, g, 8, **{arg: addr}) == T.ERR_ALIGN, arg
+    # the outputs must not overlap: 8 rows of y span 4096 bytes
+    assert call_prefill_dual(T, g, 8, y_b=FAKE) == T.ERR_OVERLAP
+    assert call_prefill_dual(T, g, 8, y_b=FAKE + 4096 - 16) == T.ERR_OVERLAP
+    assert call_prefill_dual(T, g, 8, y_a=FAKE + (1 << 20) + 4096 - 16) == T.ERR_OVERLAP
+    # M = 0 enqueues nothing once the arguments check out
+    assert call_prefill_dual(T, g, 0) == T.OK
+
+
 def test_scatter_validation(T):
     lib = T.raw()
     g = geom(T, axis=0, i=17408, o=5120, k=3)

@@ -638,6 +638,74 @@ def test_gemv_dual_long_rows(gpu_lib):
     assert gate(bf16_to_f64(yb), oracle_y(pb)) <= TOL
 
 
+# ------------------------------------------------------------ dual prefill
+def prefill_dual_case(T, shape, M, proj):
+    """gate/up pair sharing x [M][in]: each projection within tolerance of the
+    oracle and of its own trellis_prefill call; a second dual call repeats the
+    first bit for bit."""
+    pa = synth.make_problem(shape, M, CFG["test"], proj=proj)
+    pb = with_x(synth.make_problem(shape, M, CFG["test"], proj=proj + 1), pa.x)
+    da, db = Dev(pa, T), Dev(pb, T)
+    ya, yb = T.prefill_dual(da.x, (da.codes, da.scales, da.lut), (db.codes, db.scales, db.lut),
+                            da.shape)
+    ya2, yb2 = T.prefill_dual(da.x, (da.codes, da.scales, da.lut),
+                              (db.codes, db.scales, db.lut), da.shape)
+    ra = T.prefill(da.x, da.codes, da.scales, da.lut, da.shape)
+    rb = T.prefill(da.x, db.codes, db.scales, db.lut, db.shape)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(ya), bf16_bits(ya2))
+    assert np.array_equal(bf16_bits(yb), bf16_bits(yb2))
+    assert gate(bf16_to_f64(ya), bf16_to_f64(ra)) <= TOL
+    assert gate(bf16_to_f64(yb), bf16_to_f64(rb)) <= TOL
+    return pa, pb, bf16_to_f64(ya), bf16_to_f64(yb)
+
+
+@pytest.mark.parametrize("i,o,k,M,il", [(512, 300, 2, 5, 0), (768, 4111, 3, 8, 0),
+                                        (1024, 1000, 4, 16, 0), (2048, 700, 2, 12, 0),
+                                        (4096, 1000, 3, 6, 2), (512, 17, 4, 9, 0),
+                                        (256, 1, 2, 7, 0), (512, 300, 3, 3, 0),
+                                        (1024, 4111, 2, 2, 0), (512, 300, 4, 20, 0),
+                                        (768, 300, 2, 1, 0)])
+def test_prefill_dual_small(gpu_lib, i, o, k, M, il):
+    """One shared launch for 2..16 rows (direct and staged activations at
+    k = 2, ragged and single-row groups, interleaved codes); two launches at
+    20 rows; the dual GEMV at one row."""
+    T = gpu_lib
+    say(f"prefill_dual in={i} out={o} k={k} M={M} interleave={il}")
+    pa, pb, ya, yb = prefill_dual_case(T, synth.Shape(1, 256, L, k, i, o, il), M, 1300 + M + k)
+    assert gate(ya, oracle_y(pa)) <= TOL
+    assert gate(yb, oracle_y(pb)) <= TOL
+
+
+@pytest.mark.parametrize("M", [8, 16])
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_prefill_dual_qwen_sampled(gpu_lib, k, M):
+    T = gpu_lib
+    say(f"prefill_dual qwen-up k={k} M={M}")
+    pa, pb, ya, yb = prefill_dual_case(T, synth.Shape(1, 256, L, k, QWEN_IN, QWEN_OUT), M,
+                                       1320 + k + M)
+    rows = np.unique(np.concatenate([np.arange(0, QWEN_OUT, 997), np.arange(130, 150),
+                                     np.arange(QWEN_OUT - 20, QWEN_OUT)]))
+    assert gate(ya[:, rows], oracle_y(row_subset(pa, rows))) <= TOL
+    assert gate(yb[:, rows], oracle_y(row_subset(pb, rows))) <= TOL
+
+
+def test_prefill_dual_too_many_rows_for_one_launch(gpu_lib):
+    """More than 144 rows per workgroup on half the compute units: the two
+    projections run one launch each."""
+    T = gpu_lib
+    n = 144 * (T_cus() // 2) + 1
+    say(f"prefill_dual in=256 out={n} k=3 M=5")
+    pa, pb, ya, yb = prefill_dual_case(T, synth.Shape(1, 256, L, 3, 256, n), 5, 1340)
+    rows = np.unique(np.concatenate([np.arange(0, n, 389), np.arange(n - 20, n)]))
+    assert gate(ya[:, rows], oracle_y(row_subset(pa, rows))) <= TOL
+    assert gate(yb[:, rows], oracle_y(row_subset(pb, rows))) <= TOL
+
+
+def T_cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
 # ------------------------------------------------------------ maximum sizes
 MAXF = 1 << 19  # largest in/out feature count the library accepts
 
