@@ -181,10 +181,10 @@ int trellis_prefill_dual(const uint16_t* x, int32_t M, const uint32_t* codes_a,
     if (M == 1)
         return trellis_gemv_dual(x, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b,
                                  g, stream);
-    // 2..16 rows: one launch of the 16-row-group kernel over both projections
+    // 2..32 rows: one launch of the 16-row-group kernel over both projections
     // (at 5120 -> 17408 measured 16-24% faster than two launches at 5..16
     // rows, and 10-13% faster than two launches of the small-batch kernel at
-    // 2..4). More than 16 rows take two M tiles, one launch per projection.
+    // 2..4). Row ranges too long for one launch take one per projection.
     if (trellis::axis1_dual_supported(M, d.rows, g->k))
         return status_of(trellis::launch_axis1_dual(x, M, codes_a, scales_a, lut_a, y_a, codes_b,
                                                     scales_b, lut_b, y_b, d.lay, d.rows, d.nb,

@@ -504,7 +504,7 @@ int axis1_dual_groups(int N) {
     return groups < half ? groups : half;
 }
 
-template <int K, bool DIRECT>
+template <int K, int MT, bool DIRECT>
 hipError_t launch_axis1_dual_k(const uint16_t* x, int M, const uint32_t* codes_a,
                                const float* scales_a, const float* lut_a, uint16_t* y_a,
                                const uint32_t* codes_b, const float* scales_b,
@@ -513,11 +513,11 @@ hipError_t launch_axis1_dual_k(const uint16_t* x, int M, const uint32_t* codes_a
     const int G0 = axis1_dual_groups(N);
     if ((N + G0 - 1) / G0 > 16 * kDualGroups) return hipErrorInvalidValue;  // checked by the caller
     if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
-        return launch_kernel(axis1_prefill_kernel<K, 1, DIRECT, false, kDualGroups>, dim3(2 * G0),
-                             dim3(PrefillShape<1>::threads), st, x, codes_a, scales_a, lut_a, y_a,
+        return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, false, kDualGroups>, dim3(2 * G0),
+                             dim3(PrefillShape<MT>::threads), st, x, codes_a, scales_a, lut_a, y_a,
                              codes_b, scales_b, lut_b, y_b, G0, lay, N, nb, M);
-    return launch_kernel(axis1_prefill_kernel<K, 1, DIRECT, true, kDualGroups>, dim3(2 * G0),
-                         dim3(PrefillShape<1>::threads), st, x, codes_a, scales_a, lut_a, y_a,
+    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, true, kDualGroups>, dim3(2 * G0),
+                         dim3(PrefillShape<MT>::threads), st, x, codes_a, scales_a, lut_a, y_a,
                          codes_b, scales_b, lut_b, y_b, G0, lay, N, nb, M);
 }
 
@@ -554,7 +554,7 @@ hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLay
 }
 
 bool axis1_dual_supported(int M, int N, int k) {
-    if (M < 1 || M > 16 || N < 1 || k < 2 || k > 4) return false;
+    if (M < 1 || M > 32 || N < 1 || k < 2 || k > 4) return false;
     const int G0 = axis1_dual_groups(N);
     return (N + G0 - 1) / G0 <= 16 * kDualGroups;
 }
@@ -565,13 +565,17 @@ hipError_t launch_axis1_dual(const uint16_t* x, int M, const uint32_t* codes_a,
                              uint16_t* y_b, CodeLayout lay, int N, int nb, int k,
                              hipStream_t st) {
     if (!axis1_dual_supported(M, N, k)) return hipErrorInvalidValue;
-    // one M tile; directly loaded activations as for the single launch
-    const bool direct = k == 2 ? M <= kDirectMaxM : true;
-    switch (k * 2 + (direct ? 1 : 0)) {
-    case 4: return launch_axis1_dual_k<2, false>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
-    case 5: return launch_axis1_dual_k<2, true>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
-    case 7: return launch_axis1_dual_k<3, true>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
-    case 9: return launch_axis1_dual_k<4, true>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    // M tiles and activation loads as for the single launch
+    const int dmax = k == 2 ? kDirectMaxM : 16;
+    const int shape = M > 16 ? 2 : M > dmax ? 1 : 0;
+    switch (k * 4 + shape) {
+    case 8: return launch_axis1_dual_k<2, 1, true>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    case 9: return launch_axis1_dual_k<2, 1, false>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    case 10: return launch_axis1_dual_k<2, 2, false>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    case 12: return launch_axis1_dual_k<3, 1, true>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    case 14: return launch_axis1_dual_k<3, 2, false>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    case 16: return launch_axis1_dual_k<4, 1, true>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    case 18: return launch_axis1_dual_k<4, 2, false>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -69,7 +69,7 @@ hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLay
                         hipStream_t st);
 
 // Two axis-1 projections of one geometry over the same x[M][nb*256], 1 <= M
-// <= 16, in one launch of the 16-row-group kernel (half the compute units
+// <= 32, in one launch of the 16-row-group kernel (half the compute units
 // each, at most 144 rows per workgroup); axis1_dual_supported says whether
 // the geometry fits.
 bool axis1_dual_supported(int M, int N, int k);

@@ -181,11 +181,12 @@ int trellis_prefill(const uint16_t *x, int32_t M, const uint32_t *codes, const f
  * with Wa from (codes_a, scales_a, lut_a) and Wb from (codes_b, scales_b,
  * lut_b), each laid out as for trellis_prefill; g (axis 1) describes both;
  * x: bf16 [M][in]; y_a, y_b: bf16 [M][out], not overlapping
- * (TRELLIS_ERR_OVERLAP). For 2 <= M <= 16 one launch serves both (half the
+ * (TRELLIS_ERR_OVERLAP). For 2 <= M <= 32 one launch serves both (half the
  * compute units each; the pages run each projection on its own, page 60
- * tiled-prefill.ts, the shared launch is this library's); M = 1 is
- * trellis_gemv_dual; other M enqueue the two projections one after the
- * other, and should the runtime reject the second launch (TRELLIS_ERR_HIP),
+ * tiled-prefill.ts, the shared launch is this library's) when each
+ * workgroup's rows fit; M = 1 is trellis_gemv_dual; otherwise the two
+ * projections are enqueued one after the other, and should the runtime
+ * reject the second launch (TRELLIS_ERR_HIP),
  * the first one stays enqueued. Results are within the prefill's tolerance of
  * two trellis_prefill calls, not always bit-identical to them (the shared
  * launch splits rows differently, which changes the float32 summation order).

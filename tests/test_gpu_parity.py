@@ -665,11 +665,12 @@ def prefill_dual_case(T, shape, M, proj):
                                         (4096, 1000, 3, 6, 2), (512, 17, 4, 9, 0),
                                         (256, 1, 2, 7, 0), (512, 300, 3, 3, 0),
                                         (1024, 4111, 2, 2, 0), (512, 300, 4, 20, 0),
+                                        (1024, 1000, 2, 32, 0), (2048, 4111, 3, 17, 2),
                                         (768, 300, 2, 1, 0)])
 def test_prefill_dual_small(gpu_lib, i, o, k, M, il):
-    """One shared launch for 2..16 rows (direct and staged activations at
-    k = 2, ragged and single-row groups, interleaved codes); two launches at
-    20 rows; the dual GEMV at one row."""
+    """One shared launch for 2..32 rows (direct and staged activations, one
+    and two M tiles, ragged and single-row groups, interleaved codes); the
+    dual GEMV at one row."""
     T = gpu_lib
     say(f"prefill_dual in={i} out={o} k={k} M={M} interleave={il}")
     pa, pb, ya, yb = prefill_dual_case(T, synth.Shape(1, 256, L, k, i, o, il), M, 1300 + M + k)
@@ -677,7 +678,7 @@ def test_prefill_dual_small(gpu_lib, i, o, k, M, il):
     assert gate(yb, oracle_y(pb)) <= TOL
 
 
-@pytest.mark.parametrize("M", [8, 16])
+@pytest.mark.parametrize("M", [8, 16, 32])
 @pytest.mark.parametrize("k", [2, 3, 4])
 def test_prefill_dual_qwen_sampled(gpu_lib, k, M):
     T = gpu_lib
