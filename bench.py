@@ -285,10 +285,9 @@ def mlp_bench(T, torch, dev, M, steps, warmup, out):
 
     ms = time_calls(torch, mlp, n, max(steps // 3, 10), warmup)
     out[f"mlp_k4_M{M}"] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
-    if True:
-        ms = time_calls(torch, mlp_separate, n, max(steps // 3, 10), warmup)
-        name = "mlp_k4_M1_separate_gemvs" if M == 1 else f"mlp_k4_M{M}_separate_prefills"
-        out[name] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
+    ms = time_calls(torch, mlp_separate, n, max(steps // 3, 10), warmup)
+    name = "mlp_k4_M1_separate_gemvs" if M == 1 else f"mlp_k4_M{M}_separate_prefills"
+    out[name] = {"us_per_call": ms * 1e3, "gbps": cb / (ms * 1e-3) / 1e9}
     del projs
 
 
