@@ -1,11 +1,12 @@
 """GPU parity on seeded random geometries: every compute entry point (GEMV,
-dual GEMV, scatter, prefill on both axes) at random k, block counts, row
-counts (including 1, 16, 17, 68 and counts that leave ragged row groups),
-activation batch sizes and code layouts, against the CPU oracle, with a
-second call checked bit-identical to the first.
+dual GEMV, scatter, prefill on both axes, dual prefill) at random k, block
+counts, row counts (including 1, 16, 17, 68 and counts that leave ragged row
+groups), activation batch sizes and code layouts, against the CPU oracle,
+with a second call checked bit-identical to the first.
 
-The geometry of case c is drawn from its own generator (seed 20000 + c), so a
-failing case is named by its index alone and reruns unchanged.
+The geometry of case c is drawn from its own generator (seed 20000 + c, or
+40000 + c for the dual-prefill cases), so a failing case is named by its
+index alone and reruns unchanged.
 """
 import numpy as np
 import pytest
@@ -50,8 +51,26 @@ def call(T, d, op, M):
 
 @pytest.mark.parametrize("c", range(96))
 def test_random_geometry(gpu_lib, c):
+    run_case(gpu_lib, c, *draw_case(c))
+
+
+def draw_dual_prefill_case(c):
+    rng = np.random.default_rng(40000 + c)
+    k = int(rng.integers(2, 5))
+    nb = int(rng.integers(1, 25))
+    rows = int(rng.choice(ROW_CHOICES))
+    il = 2 if (nb % 2 == 0 and rng.random() < 0.3) else 0
+    M = int(rng.integers(1, 33))
+    return synth.Shape(1, 256, 12, k, 256 * nb, rows, il), "pdual", M
+
+
+@pytest.mark.parametrize("c", range(32))
+def test_random_geometry_dual_prefill(gpu_lib, c):
+    run_case(gpu_lib, 1000 + c, *draw_dual_prefill_case(c))
+
+
+def run_case(gpu_lib, c, sh, op, M):
     T = gpu_lib
-    sh, op, M = draw_case(c)
     say(f"random case {c}: axis={sh.axis} k={sh.k} in={sh.in_features} "
         f"out={sh.out_features} M={M} il={sh.block_interleave} op={op}")
     p = synth.make_problem(sh, M, synth.CONFIG_IDS["test"], proj=30000 + c)
@@ -68,6 +87,17 @@ def test_random_geometry(gpu_lib, c):
         assert np.array_equal(bf16_bits(yb), bf16_bits(rb))
         assert gate(bf16_to_f64(yb.reshape(1, -1)), oracle_y(pb)) <= TOL
         y, again = ya, ra
+    elif op == "pdual":
+        pb = with_x(synth.make_problem(sh, M, synth.CONFIG_IDS["test"], proj=31000 + c), p.x)
+        db = Dev(pb, T)
+        ya, yb = T.prefill_dual(d.x, (d.codes, d.scales, d.lut), (db.codes, db.scales, db.lut), sh)
+        ya2, yb2 = T.prefill_dual(d.x, (d.codes, d.scales, d.lut), (db.codes, db.scales, db.lut),
+                                  sh)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(ya), bf16_bits(ya2))
+        assert np.array_equal(bf16_bits(yb), bf16_bits(yb2))
+        assert gate(bf16_to_f64(yb.reshape(M, -1)), oracle_y(pb)) <= TOL
+        y = ya
     else:
         y = call(T, d, op, M)
         again = call(T, d, op, M)
