@@ -47,6 +47,10 @@ _lib.oracle_fused_f64.restype = C.c_int
 _lib.oracle_fused_f64.argtypes = [_u16p, C.c_int, _u32p, _f32p, _f32p, C.c_int, C.c_int,
                                   C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
                                   C.c_int, _f64p]
+_lib.oracle_silu.restype = C.c_double
+_lib.oracle_silu.argtypes = [C.c_double]
+_lib.oracle_swiglu_f64.restype = None
+_lib.oracle_swiglu_f64.argtypes = [_f64p, _f64p, C.c_long, _f64p]
 
 
 def _p(a: np.ndarray, t):
@@ -167,3 +171,33 @@ def deinterleave_blocks(codes: np.ndarray, rows: int, nb: int, wpb: int) -> np.n
         raise ValueError("block interleave 2 needs an even number of blocks per row")
     a = np.asarray(codes, dtype=np.uint32).reshape(nb // 2, rows, 2, wpb)
     return np.ascontiguousarray(a.transpose(1, 0, 2, 3)).reshape(-1)
+
+
+def silu(v: float) -> float:
+    """silu(v) = v / (1 + exp(-v)) in double."""
+    return float(_lib.oracle_silu(v))
+
+
+def swiglu_f64(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """h = silu(g) * u elementwise in double (the SwiGLU of an MLP's gate and
+    up projection outputs); g and u of the same shape."""
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    if g.shape != u.shape:
+        raise ValueError("gate and up outputs differ in shape")
+    h = np.empty_like(g)
+    _lib.oracle_swiglu_f64(_p(g, _f64p), _p(u, _f64p), g.size, _p(h, _f64p))
+    return h
+
+
+def mlp_up_swiglu_f64(x: np.ndarray, gate, up, T: int, L: int, k: int, in_features: int,
+                      out_features: int, n_begin: int = 0, n_end: int | None = None,
+                      block_interleave: int = 0) -> np.ndarray:
+    """h = silu(x Wg^T) * (x Wu^T) in double, [M, out_features]: gate and up
+    are (codes, scales, lut) of two axis-1 projections of one geometry; only
+    output columns [n_begin, n_end) are computed, the others are zero."""
+    g = fused_f64(x, *gate, 1, T, L, k, in_features, out_features, n_begin, n_end,
+                  block_interleave)
+    u = fused_f64(x, *up, 1, T, L, k, in_features, out_features, n_begin, n_end,
+                  block_interleave)
+    return swiglu_f64(g, u)

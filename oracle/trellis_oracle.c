@@ -215,3 +215,29 @@ int oracle_fused_f64(const uint16_t *x, int M, const uint32_t *codes, const floa
     }
     return 1;
 }
+
+/* ---------------------------------------------------------------------------
+ * SwiGLU epilogue of a decoder MLP's gate and up projections.
+ *
+ * The pages tune their kernels for the Qwen MLP geometry (the prefill's
+ * dispatch notes in [P60] tiled-prefill.ts; [P60] wide-prefill.ts takes the
+ * RMSNorm output of such a model as its activations) but print no activation
+ * function. The plainest reading of that MLP, taken here, is the SwiGLU of
+ * the gate and up projections, h = silu(g) * u with silu(v) = v / (1 + e^-v),
+ * whose product feeds the down projection. Computed in double from the
+ * double contraction results; the GPU's h (bf16) is compared to it within the
+ * output tolerance.
+ */
+#include <math.h>
+
+/* silu(v) = v * sigmoid(v) = v / (1 + exp(-v)), in double. */
+double oracle_silu(double v)
+{
+    return v / (1.0 + exp(-v));
+}
+
+/* h[i] = silu(g[i]) * u[i] for i < n, in double. */
+void oracle_swiglu_f64(const double *g, const double *u, long n, double *h)
+{
+    for (long i = 0; i < n; ++i) h[i] = oracle_silu(g[i]) * u[i];
+}

@@ -438,3 +438,69 @@ def test_interleave_needs_an_even_block_count():
     with pytest.raises(ValueError):
         oracle.expand(codes, scales, lut, 1, T, L, k, 3 * T, 2, block_interleave=1)
     oracle.expand(codes, scales, lut, 1, T, L, k, 3 * T, 2, block_interleave=0)
+
+
+# ------------------------------------------------------------ SwiGLU epilogue
+def test_silu_closed_forms():
+    """silu(0) = 0; sigmoid(ln 3) = 3/4, so silu(ln 3) = (3/4) ln 3 (this also
+    fails v * sigmoid(-v), which agrees with silu on the odd identity below);
+    silu(v) -> v far right, -> 0 far left."""
+    import math
+
+    assert oracle.silu(0.0) == 0.0
+    assert oracle.silu(math.log(3.0)) == pytest.approx(0.75 * math.log(3.0), rel=1e-15)
+    assert oracle.silu(-math.log(3.0)) == pytest.approx(-0.25 * math.log(3.0), rel=1e-15)
+    assert oracle.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert oracle.silu(-800.0) == 0.0
+
+
+def test_silu_odd_part_is_identity():
+    """silu(v) - silu(-v) = v (sigmoid(v) + sigmoid(-v) = 1)."""
+    rng = np.random.default_rng(7)
+    for v in rng.standard_normal(2000) * 6:
+        assert oracle.silu(v) - oracle.silu(-v) == pytest.approx(v, rel=1e-13, abs=1e-15)
+
+
+def test_silu_matches_torch():
+    """Against torch's CPU silu in float64 (a library routine)."""
+    rng = np.random.default_rng(8)
+    v = rng.standard_normal(100_000) * 20
+    ref = torch.nn.functional.silu(torch.from_numpy(v)).numpy()
+    got = np.array([oracle.silu(float(a)) for a in v[:5000]])
+    np.testing.assert_allclose(got, ref[:5000], rtol=1e-14, atol=1e-300)
+    h = oracle.swiglu_f64(v, np.ones_like(v))
+    np.testing.assert_allclose(h, ref, rtol=1e-14, atol=1e-300)
+
+
+def test_swiglu_applies_silu_to_the_gate():
+    """h = silu(g) * u, not silu(u) * g: g = ln 3, u = 4 gives 3 ln 3; a zero
+    gate gives zero whatever u is; the up operand enters linearly."""
+    import math
+
+    g = np.array([math.log(3.0), 0.0, math.log(3.0)])
+    u = np.array([4.0, 123.0, -8.0])
+    h = oracle.swiglu_f64(g, u)
+    assert h[0] == pytest.approx(3.0 * math.log(3.0), rel=1e-15)
+    assert h[1] == 0.0
+    assert h[2] == pytest.approx(-6.0 * math.log(3.0), rel=1e-15)
+    with pytest.raises(ValueError):
+        oracle.swiglu_f64(np.zeros(3), np.zeros(4))
+
+
+def test_mlp_up_swiglu_on_one_hot_rows_uses_the_stored_weights():
+    """One-hot activation rows select one stored column of each projection
+    exactly, so h[m][n] = silu(Wg[n][j_m]) * Wu[n][j_m] with both weights read
+    from the oracle's expand (pinned above by brute force)."""
+    T, k, i, o = 256, 3, 512, 40
+    sh = synth.Shape(1, T, L, k, i, o)
+    pg = synth.make_problem(sh, 1, synth.CONFIG_IDS["test"], proj=900)
+    pu = synth.make_problem(sh, 1, synth.CONFIG_IDS["test"], proj=901)
+    cols = [0, 255, 256, 511]
+    x = synth.one_hot_x(len(cols), i, cols)
+    h = oracle.mlp_up_swiglu_f64(x, (pg.codes, pg.scales, pg.lut), (pu.codes, pu.scales, pu.lut),
+                                 T, L, k, i, o)
+    Wg = oracle.bf16_bits_to_f64(oracle.expand(pg.codes, pg.scales, pg.lut, 1, T, L, k, i, o))
+    Wu = oracle.bf16_bits_to_f64(oracle.expand(pu.codes, pu.scales, pu.lut, 1, T, L, k, i, o))
+    for m, j in enumerate(cols):
+        want = torch.nn.functional.silu(torch.from_numpy(Wg[:, j])).numpy() * Wu[:, j]
+        np.testing.assert_allclose(h[m], want, rtol=1e-14, atol=0)
