@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtrellis.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["gemv.hip", "axis1.hip", "axis0.hip", "layout.hip", "api.cpp"]
+SOURCES = ["gemv.hip", "axis1.hip", "axis0.hip", "layout.hip", "probe.hip", "api.cpp"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

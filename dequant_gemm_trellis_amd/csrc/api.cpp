@@ -194,6 +194,28 @@ int trellis_prefill_dual(const uint16_t* x, int32_t M, const uint32_t* codes_a,
     return status_of(launch_axis1_any(x, M, codes_b, scales_b, lut_b, y_b, d, g->k, stream));
 }
 
+int trellis_gate_up_swiglu(const uint16_t* x, int32_t M, const uint32_t* codes_g,
+                           const float* scales_g, const float* lut_g, const uint32_t* codes_u,
+                           const float* scales_u, const float* lut_u, const trellis_geometry* g,
+                           uint16_t* h, hipStream_t stream) {
+    Dims d;
+    int st = check_geometry(g, &d);
+    if (st) return st;
+    if (g->axis != 1) return TRELLIS_ERR_GEOMETRY;
+    if (M < 0 || M > TRELLIS_MAX_M) return TRELLIS_ERR_GEOMETRY;
+    if ((st = check_operands(codes_g, scales_g, lut_g)) ||
+        (st = check_operands(codes_u, scales_u, lut_u)) || (st = check_io(x, h)))
+        return st;
+    if (M == 0) return TRELLIS_OK;
+    // One row whose activations fit the GEMV's staging: the GEMV mapping;
+    // otherwise the 16-row-group kernel (any row length, 1..32 rows).
+    if (M == 1 && d.nb <= trellis::gemv_max_blocks(g->k))
+        return status_of(trellis::launch_gemv_swiglu(x, codes_g, scales_g, lut_g, codes_u, scales_u,
+                                                     lut_u, h, d.lay, d.rows, d.nb, g->k, stream));
+    return status_of(trellis::launch_axis1_swiglu(x, M, codes_g, scales_g, lut_g, codes_u, scales_u,
+                                                  lut_u, h, d.lay, d.rows, d.nb, g->k, stream));
+}
+
 size_t trellis_workspace_bytes(const trellis_geometry* g, int32_t M, int32_t op) {
     Dims d;
     if (check_geometry(g, &d)) return static_cast<size_t>(-1);

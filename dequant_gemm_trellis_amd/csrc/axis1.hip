@@ -338,12 +338,21 @@ __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& 
     });
 }
 
+// silu(v) = v / (1 + e^-v) in float32: the gate nonlinearity of SwiGLU.
+__device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)); }
+
 // Two projections of the same geometry over the same activation rows (an
-// MLP's gate and up) can share one launch: workgroups below G0 compute y_a
-// from (codes_a, scales_a, lut_a), the others y_b from the b operands, each
-// half splitting its rows as one launch of its own would. A single
-// projection passes G0 = gridDim.x.
-template <int K, int MT, bool DIRECT, bool PAIRS, int KG>
+// MLP's gate and up) can share one launch.
+//   Without SWIGLU, workgroups below G0 compute y_a from (codes_a, scales_a,
+//   lut_a), the others y_b from the b operands, each half splitting its rows
+//   as one launch of its own would; a single projection passes G0 = gridDim.x.
+//   With SWIGLU (G0 = gridDim.x) every workgroup owns a row range of both: it
+//   runs its tasks on the gate (a operands), reduces the waves' tiles and keeps
+//   each output's gate sum in the register of the thread that reduced it,
+//   restages the table from the up codebook, runs the same tasks on the up
+//   projection (b operands) and writes y_a[m][n] = bf16(silu(g) * u), the same
+//   thread reducing the same output in both phases.
+template <int K, int MT, bool DIRECT, bool PAIRS, int KG, bool SWIGLU>
 __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes_a,
     const float* __restrict__ scales_a, const float* __restrict__ lut_a,
@@ -355,7 +364,7 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     __shared__ __attribute__((aligned(16))) float lds[Lds::floats];
     float* const tab = lds;
 
-    const bool second = static_cast<int>(blockIdx.x) >= G0;
+    const bool second = !SWIGLU && static_cast<int>(blockIdx.x) >= G0;
     const uint32_t* const codes = second ? codes_b : codes_a;
     const float* const scales = second ? scales_b : scales_a;
     const float* const lut = second ? lut_b : lut_a;
@@ -420,34 +429,76 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     // loads would be sunk into it, behind the barrier.)
     XFrags<MT> xf;
     int xb = -1;  // block whose fragments xf holds
-    for (int t0 = tau0; t0 < tau1; t0 += 3) {
-        load_task<K, PAIRS>(tc, cx, t0 + 2, tau1);
-        run_task<K, MT, DIRECT, KG>(ta, xf, xn, xb, xs, acc, tab, lane, j, c);
-        load_task<K, PAIRS>(ta, cx, t0 + 3, tau1);
-        if (t0 + 1 < tau1) run_task<K, MT, DIRECT, KG>(tb, xf, xn, xb, xs, acc, tab, lane, j, c);
-        load_task<K, PAIRS>(tb, cx, t0 + 4, tau1);
-        if (t0 + 2 < tau1) run_task<K, MT, DIRECT, KG>(tc, xf, xn, xb, xs, acc, tab, lane, j, c);
-    }
+    auto run_tasks = [&]() {
+        for (int t0 = tau0; t0 < tau1; t0 += 3) {
+            load_task<K, PAIRS>(tc, cx, t0 + 2, tau1);
+            run_task<K, MT, DIRECT, KG>(ta, xf, xn, xb, xs, acc, tab, lane, j, c);
+            load_task<K, PAIRS>(ta, cx, t0 + 3, tau1);
+            if (t0 + 1 < tau1) run_task<K, MT, DIRECT, KG>(tb, xf, xn, xb, xs, acc, tab, lane, j, c);
+            load_task<K, PAIRS>(tb, cx, t0 + 4, tau1);
+            if (t0 + 2 < tau1) run_task<K, MT, DIRECT, KG>(tc, xf, xn, xb, xs, acc, tab, lane, j, c);
+        }
+    };
+    run_tasks();
     __syncthreads();  // the table is dead from here on; its space takes the partials
 
-    // part[wave][group][m][j]: D[m = 4c + v][j] of each tile; untouched groups add zeros.
+    // part[wave][group][m][j]: D[m = 4c + v][j] of each tile; untouched groups
+    // add zeros. Output (16 mt + m, row) is reduced by thread idx % 512 in
+    // pass idx / 512, idx = (group * 16 + m) * 16 + j, the waves added in order.
     float* const part = lds;
+    constexpr int kPasses = (KG * 256 + kThreadsP - 1) / kThreadsP;
+    auto reduce = [&](auto&& sink) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int g = 0; g < KG; ++g)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    part[((wave * KG + g) * 16 + 4 * c + v) * 16 + j] = acc[g][mt][v];
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < kPasses; ++it) {
+                const int idx = tid + it * kThreadsP;
+                if (idx < gc * 256) {
+                    const int g = idx >> 8, m = (idx >> 4) & 15, jj = idx & 15;
+                    float s = 0.f;
+                    for (int w = 0; w < kWaves; ++w) s += part[((w * KG + g) * 16 + m) * 16 + jj];
+                    sink(mt, it, 16 * mt + m, r0 + 16 * g + jj, s);
+                }
+            }
+            __syncthreads();
+        }
+    };
+    if constexpr (SWIGLU) {
+        float gsum[MT][kPasses];
+        reduce([&](int mt, int it, int, int, float s) { gsum[mt][it] = s; });
+        // The up projection: its codebook and first tasks, as in the prologue.
+        cx.codes = codes_b;
+        cx.scales = scales_b;
+        typename Lds::Table::Src ts;
+        Lds::Table::fetch(ts, lut_b);
+        asm volatile("" ::: "memory");
+        load_task_opaque<K, PAIRS>(ta, cx, tau0, tau1 > 1 ? tau1 : 1);
+        load_task_opaque<K, PAIRS>(tb, cx, tau0 + 1, tau1 > 1 ? tau1 : 1);
+        if constexpr (DIRECT) load_x_frags_opaque<MT>(xn, xs.xa, ta.b);
+        asm volatile("" ::: "memory");
+        Lds::Table::store(ts, tab);
 #pragma unroll
         for (int g = 0; g < KG; ++g)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                part[((wave * KG + g) * 16 + 4 * c + v) * 16 + j] = acc[g][mt][v];
+            for (int mt = 0; mt < MT; ++mt) acc[g][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        xb = -1;
         __syncthreads();
-        for (int idx = tid; idx < gc * 256; idx += kThreadsP) {
-            const int g = idx >> 8, m = (idx >> 4) & 15, jj = idx & 15;
-            float s = 0.f;
-            for (int w = 0; w < kWaves; ++w) s += part[((w * KG + g) * 16 + m) * 16 + jj];
-            const int row = r0 + 16 * g + jj, mm = 16 * mt + m;
+        run_tasks();
+        __syncthreads();
+        reduce([&](int mt, int it, int mm, int row, float s) {
+            if (mm < M && row < r1)
+                y[static_cast<size_t>(mm) * N + row] = round_bf16(silu_f32(gsum[mt][it]) * s);
+        });
+    } else {
+        reduce([&](int, int, int mm, int row, float s) {
             if (mm < M && row < r1) y[static_cast<size_t>(mm) * N + row] = round_bf16(s);
-        }
-        __syncthreads();
+        });
     }
 }
 
@@ -476,24 +527,47 @@ __global__ __launch_bounds__(kThreads) void expand_kernel(
     });
 }
 
+// One workgroup per compute unit while that leaves at most kGroups groups
+// each; beyond that, as many workgroups as needed, run in rounds.
+int axis1_grid(int N) {
+    const int groups = (N + 15) / 16;
+    int G = groups < cu_count() ? groups : cu_count();
+    if ((N + G - 1) / G > 16 * kGroups) G = (N + 16 * kGroups - 1) / (16 * kGroups);
+    return G;
+}
+
 template <int K, int MT, bool DIRECT>
 hipError_t launch_axis1_k(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                           const float* scales, const float* lut, uint16_t* y, int N, int nb,
                           hipStream_t st) {
-    // One workgroup per compute unit while that leaves at most kGroups groups
-    // each; beyond that, as many workgroups as needed, run in rounds.
-    const int groups = (N + 15) / 16;
-    int G = groups < cu_count() ? groups : cu_count();
-    if ((N + G - 1) / G > 16 * kGroups) G = (N + 16 * kGroups - 1) / (16 * kGroups);
+    const int G = axis1_grid(N);
     // Row-major iff a row's blocks are contiguous (with two blocks per row the
     // two layouts coincide).
     if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
-        return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, false, kGroups>, dim3(G),
+        return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, false, kGroups, false>, dim3(G),
                              dim3(PrefillShape<MT>::threads), st, x, codes, scales, lut, y, codes,
                              scales, lut, y, G, lay, N, nb, M);
-    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, true, kGroups>, dim3(G),
+    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, true, kGroups, false>, dim3(G),
                          dim3(PrefillShape<MT>::threads), st, x, codes, scales, lut, y, codes,
                          scales, lut, y, G, lay, N, nb, M);
+}
+
+// Gate and up with the SwiGLU epilogue: the single launch's grid, every
+// workgroup decoding its rows of both projections.
+template <int K, int MT, bool DIRECT>
+hipError_t launch_axis1_swiglu_k(const uint16_t* x, int M, const uint32_t* codes_g,
+                                 const float* scales_g, const float* lut_g,
+                                 const uint32_t* codes_u, const float* scales_u,
+                                 const float* lut_u, uint16_t* h, CodeLayout lay, int N, int nb,
+                                 hipStream_t st) {
+    const int G = axis1_grid(N);
+    if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
+        return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, false, kGroups, true>, dim3(G),
+                             dim3(PrefillShape<MT>::threads), st, x, codes_g, scales_g, lut_g, h,
+                             codes_u, scales_u, lut_u, h, G, lay, N, nb, M);
+    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, true, kGroups, true>, dim3(G),
+                         dim3(PrefillShape<MT>::threads), st, x, codes_g, scales_g, lut_g, h,
+                         codes_u, scales_u, lut_u, h, G, lay, N, nb, M);
 }
 
 // Workgroups per projection of the two-projection launch: half the compute
@@ -513,10 +587,10 @@ hipError_t launch_axis1_dual_k(const uint16_t* x, int M, const uint32_t* codes_a
     const int G0 = axis1_dual_groups(N);
     if ((N + G0 - 1) / G0 > 16 * kDualGroups) return hipErrorInvalidValue;  // checked by the caller
     if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
-        return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, false, kDualGroups>, dim3(2 * G0),
+        return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, false, kDualGroups, false>, dim3(2 * G0),
                              dim3(PrefillShape<MT>::threads), st, x, codes_a, scales_a, lut_a, y_a,
                              codes_b, scales_b, lut_b, y_b, G0, lay, N, nb, M);
-    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, true, kDualGroups>, dim3(2 * G0),
+    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, true, kDualGroups, false>, dim3(2 * G0),
                          dim3(PrefillShape<MT>::threads), st, x, codes_a, scales_a, lut_a, y_a,
                          codes_b, scales_b, lut_b, y_b, G0, lay, N, nb, M);
 }
@@ -544,10 +618,8 @@ hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLay
     case 9: return launch_axis1_k<2, 1, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
     case 10: return launch_axis1_k<2, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
     case 12: return launch_axis1_k<3, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
-    case 13: return launch_axis1_k<3, 1, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
     case 14: return launch_axis1_k<3, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
     case 16: return launch_axis1_k<4, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
-    case 17: return launch_axis1_k<4, 1, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
     case 18: return launch_axis1_k<4, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
     default: return hipErrorInvalidValue;
     }
@@ -576,6 +648,25 @@ hipError_t launch_axis1_dual(const uint16_t* x, int M, const uint32_t* codes_a,
     case 14: return launch_axis1_dual_k<3, 2, false>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
     case 16: return launch_axis1_dual_k<4, 1, true>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
     case 18: return launch_axis1_dual_k<4, 2, false>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_axis1_swiglu(const uint16_t* x, int M, const uint32_t* codes_g,
+                               const float* scales_g, const float* lut_g, const uint32_t* codes_u,
+                               const float* scales_u, const float* lut_u, uint16_t* h,
+                               CodeLayout lay, int N, int nb, int k, hipStream_t st) {
+    // M tiles and activation loads as for the single launch
+    const int dmax = k == 2 ? kDirectMaxM : 16;
+    const int shape = M > 16 ? 2 : M > dmax ? 1 : 0;
+    switch (k * 4 + shape) {
+    case 8: return launch_axis1_swiglu_k<2, 1, true>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
+    case 9: return launch_axis1_swiglu_k<2, 1, false>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
+    case 10: return launch_axis1_swiglu_k<2, 2, false>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
+    case 12: return launch_axis1_swiglu_k<3, 1, true>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
+    case 14: return launch_axis1_swiglu_k<3, 2, false>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
+    case 16: return launch_axis1_swiglu_k<4, 1, true>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
+    case 18: return launch_axis1_swiglu_k<4, 2, false>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
     default: return hipErrorInvalidValue;
     }
 }

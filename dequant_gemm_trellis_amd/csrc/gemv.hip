@@ -59,11 +59,13 @@ constexpr int kXStride = 528;        // bytes per staged activation block (512 +
 
 // Decode table: the k = 2 pair table, or for k = 3, 4 the codebook in
 // bank-partitioned copies (kRepCopies, 128 KB); both leave 32 KB of LDS.
-template <int K>
+// SINGLE: the plain 16 KB codebook, for launches whose workgroups decode too
+// few units to repay building a 128 KB table (kSmallUnits).
+template <int K, bool SINGLE = false>
 struct GemvLds {
-    static constexpr bool pair = K == 2;
-    static constexpr bool rep = !pair;
-    static constexpr int tab_floats = pair ? 2 * kPairEntries : kRepFloats;
+    static constexpr bool pair = K == 2 && !SINGLE;
+    static constexpr bool rep = K != 2 && !SINGLE;
+    static constexpr int tab_floats = pair ? 2 * kPairEntries : rep ? kRepFloats : kLutEntries;
     // activation bytes that fit beside the table and the partials in 160 KB
     static constexpr int x_bytes = 24576;
     static constexpr int max_blocks = x_bytes / kXStride;
@@ -72,15 +74,20 @@ struct GemvLds {
     static constexpr int depth = 2;
 };
 
+// Below this many units (row x block) per workgroup the GEMV stages the plain
+// codebook: writing a 128 KB table costs about as much LDS time as the faster
+// gathers save over some 75 units.
+constexpr int kSmallUnits = 64;
+
 // Fragment S's gathers from the kernel's decode table.
-template <int K, int S>
-__device__ __forceinline__ Gathered<GemvLds<K>::pair> gemv_gather(const uint32_t (&w)[2 * K + 1],
-                                                                  const float* __restrict__ tab) {
-    return gather_tab<K, S, GemvLds<K>::pair, GemvLds<K>::rep>(w, tab);
+template <int K, int S, bool SINGLE>
+__device__ __forceinline__ Gathered<GemvLds<K, SINGLE>::pair> gemv_gather(
+    const uint32_t (&w)[2 * K + 1], const float* __restrict__ tab) {
+    return gather_tab<K, S, GemvLds<K, SINGLE>::pair, GemvLds<K, SINGLE>::rep>(w, tab);
 }
 
-template <int K>
-using GemvTable = DecodeTable<kThreads, GemvLds<K>::pair, GemvLds<K>::rep>;
+template <int K, bool SINGLE>
+using GemvTable = DecodeTable<kThreads, GemvLds<K, SINGLE>::pair, GemvLds<K, SINGLE>::rep>;
 
 // Code words of one step for one lane, plus the unit's block and the
 // row-major index (row * nb + block) of its partial.
@@ -146,12 +153,12 @@ __device__ __forceinline__ XFrag load_x(const char* __restrict__ xs, uint32_t b,
 // The A fragments stay in registers while the lane's unit stays in the same
 // block (xb), which with contiguous unit ranges per wave is all but one or two
 // steps; re-reading them every step would cost about a quarter of the LDS time.
-template <int K>
+template <int K, bool SINGLE>
 __device__ __forceinline__ void run_step(Step<K> st, XFrag& xf, uint32_t& xb,
                                          const char* __restrict__ xs,
                                          const float* __restrict__ tab, float* __restrict__ part,
                                          int u, int u_end, int j, int c) {
-    constexpr bool P = GemvLds<K>::pair;
+    constexpr bool P = GemvLds<K, SINGLE>::pair;
     st.w[2 * K] = next_run_word(st.w[0]);
     if (st.b != xb) {
         xb = st.b;
@@ -165,7 +172,7 @@ __device__ __forceinline__ void run_step(Step<K> st, XFrag& xf, uint32_t& xb,
     Gathered<P> g[8];
     static_for<0, D>([&](auto ic) {
         constexpr int S = 7 - decltype(ic)::value;
-        g[S] = gemv_gather<K, S>(st.w, tab);
+        g[S] = gemv_gather<K, S, SINGLE>(st.w, tab);
     });
     static_for<0, 8>([&](auto ic) {
         constexpr int S = 7 - decltype(ic)::value;
@@ -174,7 +181,7 @@ __device__ __forceinline__ void run_step(Step<K> st, XFrag& xf, uint32_t& xb,
         // the LDS queue stays fed (1-2% faster; around the packing instead,
         // no faster).
         __builtin_amdgcn_s_setprio(2);
-        if constexpr (S >= D) g[S - D] = gemv_gather<K, S - D>(st.w, tab);
+        if constexpr (S >= D) g[S - D] = gemv_gather<K, S - D, SINGLE>(st.w, tab);
         __builtin_amdgcn_s_setprio(0);
         const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g[S], st.scale));
         acc = mfma16x16x32(as_bf16x8(xf.v[S]), bfrag, acc);
@@ -185,12 +192,20 @@ __device__ __forceinline__ void run_step(Step<K> st, XFrag& xf, uint32_t& xb,
     }
 }
 
+// silu(v) = v / (1 + e^-v) in float32: the gate nonlinearity of SwiGLU.
+__device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)); }
+
 // Two projections of the same shape and the same activations (the gate and
-// up projections of an MLP) can share one launch: workgroups below G0 compute
-// y_a from (codes_a, scales_a, lut_a), the others y_b from the b operands,
-// each set of workgroups splitting the N rows evenly. A single projection
-// passes G0 = gridDim.x.
-template <int K, bool PAIRS>
+// up projections of an MLP) can share one launch.
+//   Without SWIGLU, workgroups below G0 compute y_a from (codes_a, scales_a,
+//   lut_a), the others y_b from the b operands, each set of workgroups
+//   splitting the N rows evenly; a single projection passes G0 = gridDim.x.
+//   With SWIGLU (G0 = gridDim.x) every workgroup owns a row range of both: it
+//   decodes the range's gate rows (a operands) from the gate codebook, restages
+//   its table from the up codebook, decodes the same rows of the up projection
+//   (b operands), and writes y_a[n] = bf16(silu(g_n) * u_n) from the two row
+//   sums, float32 throughout. The unit partials of both phases stay in LDS.
+template <int K, bool PAIRS, bool SINGLE, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes_a,
     const float* __restrict__ scales_a, const float* __restrict__ lut_a,
@@ -202,13 +217,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     // VALU op per weight). The unit partials take what the nb staged
     // activation blocks leave of the rest.
     __shared__ __attribute__((aligned(16)))
-    float lds[GemvLds<K>::tab_floats + GemvLds<K>::x_bytes / 4 + kPartialCap];
+    float lds[GemvLds<K, SINGLE>::tab_floats + GemvLds<K>::x_bytes / 4 + kPartialCap];
     float* const tab = lds;
-    char* const xs = reinterpret_cast<char*>(lds + GemvLds<K>::tab_floats);
+    char* const xs = reinterpret_cast<char*>(lds + GemvLds<K, SINGLE>::tab_floats);
     float* const part = reinterpret_cast<float*>(xs + nb * kXStride);
     const int part_cap = (GemvLds<K>::x_bytes - nb * kXStride) / 4 + kPartialCap;
+    constexpr int kPhases = SWIGLU ? 2 : 1;
 
-    const bool second = static_cast<int>(blockIdx.x) >= G0;
+    const bool second = !SWIGLU && static_cast<int>(blockIdx.x) >= G0;
     const uint32_t* const codes = second ? codes_b : codes_a;
     const float* const scales = second ? scales_b : scales_a;
     const float* const lut = second ? lut_b : lut_a;
@@ -220,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, c = lane >> 4;
-    const int chunk_rows = part_cap / nb;
+    const int chunk_rows = part_cap / (kPhases * nb);
 
     Ctx cx{codes + static_cast<size_t>(r0) * lay.row_words, lay, scales + r0, nb, 1, 0u, 3 - c};
     Step<K> sa, sb, sc;
@@ -231,8 +247,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     // only for their own data (memory-counter waits retire in issue order),
     // while the code words are still on their way from HBM.
     constexpr int kXChunks = (GemvLds<K>::max_blocks * 32 + kThreads - 1) / kThreads;
-    typename GemvTable<K>::Src tsrc;
-    GemvTable<K>::fetch(tsrc, lut);
+    typename GemvTable<K, SINGLE>::Src tsrc;
+    GemvTable<K, SINGLE>::fetch(tsrc, lut);
     u32x4 xv[kXChunks];
 #pragma unroll
     for (int q = 0; q < kXChunks; ++q) {  // 16-byte chunks of x, 32 per block
@@ -251,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     cx.magic = div_magic(CR);
     load_step<K, PAIRS>(sa, cx, ub + j, ue > 1 ? ue : 1);
     load_step<K, PAIRS>(sb, cx, ub + 16 + j, ue > 1 ? ue : 1);
-    GemvTable<K>::store(tsrc, tab);
+    GemvTable<K, SINGLE>::store(tsrc, tab);
 #pragma unroll
     for (int q = 0; q < kXChunks; ++q) {
         const int i = tid + q * kThreads;
@@ -264,32 +280,55 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         U = CR * nb;
         ub = wave * U / kWaves;
         ue = (wave + 1) * U / kWaves;
-        if (cr0 != r0 && ue > ub) {
-            cx.codes = codes + static_cast<size_t>(cr0) * lay.row_words;
-            cx.scales = scales + cr0;
-            cx.cr = CR;
-            cx.magic = div_magic(CR);
-            load_step<K, PAIRS>(sa, cx, ub + j, ue);
-            load_step<K, PAIRS>(sb, cx, ub + 16 + j, ue);
-        }
-        // Three register sets rotate, so the code words of the next two steps
-        // are in flight while one step is decoded. Every load is
-        // unconditional (past the end it re-reads a valid unit) and only the
-        // decode steps are guarded: the memory-counter waits the compiler
-        // places must hold on every path, so a conditional load, or a loop
-        // exit between loads, makes it wait for the prefetch too.
-        for (int u0 = ub; u0 < ue; u0 += 48) {
-            const int ua = u0 + j;
-            load_step<K, PAIRS>(sc, cx, ua + 32, ue);
-            run_step<K>(sa, xf, xb, xs, tab, part, ua, ue, j, c);
-            load_step<K, PAIRS>(sa, cx, ua + 48, ue);
-            if (u0 + 16 < ue) run_step<K>(sb, xf, xb, xs, tab, part, ua + 16, ue, j, c);
-            load_step<K, PAIRS>(sb, cx, ua + 64, ue);
-            if (u0 + 32 < ue) run_step<K>(sc, xf, xb, xs, tab, part, ua + 32, ue, j, c);
+        for (int ph = 0; ph < kPhases; ++ph) {
+            if constexpr (SWIGLU) {
+                // Every phase but the first of the launch switches projection:
+                // the other codebook is fetched and the phase's first two steps
+                // loaded while the waves finish with the old table, which is
+                // then rewritten.
+                if (cr0 != r0 || ph != 0) {
+                    cx.codes = (ph ? codes_b : codes_a) + static_cast<size_t>(cr0) * lay.row_words;
+                    cx.scales = (ph ? scales_b : scales_a) + cr0;
+                    cx.cr = CR;
+                    cx.magic = div_magic(CR);
+                    typename GemvTable<K, SINGLE>::Src ts;
+                    GemvTable<K, SINGLE>::fetch(ts, ph ? lut_b : lut_a);
+                    asm volatile("" ::: "memory");
+                    load_step<K, PAIRS>(sa, cx, ub + j, ue > 1 ? ue : 1);
+                    load_step<K, PAIRS>(sb, cx, ub + 16 + j, ue > 1 ? ue : 1);
+                    __syncthreads();
+                    GemvTable<K, SINGLE>::store(ts, tab);
+                    __syncthreads();
+                }
+            } else if (cr0 != r0 && ue > ub) {
+                cx.codes = codes + static_cast<size_t>(cr0) * lay.row_words;
+                cx.scales = scales + cr0;
+                cx.cr = CR;
+                cx.magic = div_magic(CR);
+                load_step<K, PAIRS>(sa, cx, ub + j, ue);
+                load_step<K, PAIRS>(sb, cx, ub + 16 + j, ue);
+            }
+            float* const pp = part + ph * U;  // this phase's unit partials
+            // Three register sets rotate, so the code words of the next two
+            // steps are in flight while one step is decoded. Every load is
+            // unconditional (past the end it re-reads a valid unit) and only
+            // the decode steps are guarded: the memory-counter waits the
+            // compiler places must hold on every path, so a conditional load,
+            // or a loop exit between loads, makes it wait for the prefetch too.
+            for (int u0 = ub; u0 < ue; u0 += 48) {
+                const int ua = u0 + j;
+                load_step<K, PAIRS>(sc, cx, ua + 32, ue);
+                run_step<K, SINGLE>(sa, xf, xb, xs, tab, pp, ua, ue, j, c);
+                load_step<K, PAIRS>(sa, cx, ua + 48, ue);
+                if (u0 + 16 < ue) run_step<K, SINGLE>(sb, xf, xb, xs, tab, pp, ua + 16, ue, j, c);
+                load_step<K, PAIRS>(sb, cx, ua + 64, ue);
+                if (u0 + 32 < ue) run_step<K, SINGLE>(sc, xf, xb, xs, tab, pp, ua + 32, ue, j, c);
+            }
         }
         __syncthreads();
-        for (int r = tid; r < CR; r += kThreads) {
-            const float* pr = part + r * nb;
+        // Each row: its block partials added in ascending block order (for
+        // SWIGLU once per projection).
+        auto row_sum = [&](const float* pr) {
             float s = 0.f;
             int q = 0;
             for (; q + 8 <= nb; q += 8) {  // reads issued together, added in order
@@ -300,7 +339,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
                 for (int i = 0; i < 8; ++i) s += v[i];
             }
             for (; q < nb; ++q) s += pr[q];
-            y[cr0 + r] = round_bf16(s);
+            return s;
+        };
+        for (int r = tid; r < CR; r += kThreads) {
+            const float s = row_sum(part + r * nb);
+            if constexpr (SWIGLU) y[cr0 + r] = round_bf16(silu_f32(s) * row_sum(part + U + r * nb));
+            else y[cr0 + r] = round_bf16(s);
         }
         __syncthreads();
     }
@@ -325,12 +369,31 @@ hipError_t launch_gemv_k(const uint16_t* x, const uint32_t* codes, const float* 
         y_b = y;
     }
     // Row-major iff a row's blocks are contiguous (with two blocks per row the
-    // two layouts coincide).
-    if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
-        return launch_kernel(gemv_kernel<K, false>, dim3(G), dim3(kThreads), st, x, codes, scales,
-                             lut, y, codes_b, scales_b, lut_b, y_b, G0, lay, N, nb);
-    return launch_kernel(gemv_kernel<K, true>, dim3(G), dim3(kThreads), st, x, codes, scales, lut,
-                         y, codes_b, scales_b, lut_b, y_b, G0, lay, N, nb);
+    // two layouts coincide). Workgroups own ceil(N / G0) rows at most.
+    const bool rowmajor = lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb;
+    const bool small = static_cast<long>((N + G0 - 1) / G0) * nb < kSmallUnits;
+    auto kern = small ? (rowmajor ? gemv_kernel<K, false, true, false> : gemv_kernel<K, true, true, false>)
+                      : (rowmajor ? gemv_kernel<K, false, false, false> : gemv_kernel<K, true, false, false>);
+    return launch_kernel(kern, dim3(G), dim3(kThreads), st, x, codes, scales, lut, y, codes_b,
+                         scales_b, lut_b, y_b, G0, lay, N, nb);
+}
+
+// Gate and up with the SwiGLU epilogue: min(N, CUs) workgroups, each owning a
+// row range of both projections.
+template <int K>
+hipError_t launch_gemv_swiglu_k(const uint16_t* x, const uint32_t* codes_g, const float* scales_g,
+                                const float* lut_g, const uint32_t* codes_u,
+                                const float* scales_u, const float* lut_u, uint16_t* h,
+                                CodeLayout lay, int N, int nb, hipStream_t st) {
+    int G = cu_count();
+    if (G > N) G = N;
+    if (G < 1) G = 1;
+    const bool rowmajor = lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb;
+    const bool small = 2l * ((N + G - 1) / G) * nb < kSmallUnits;
+    auto kern = small ? (rowmajor ? gemv_kernel<K, false, true, true> : gemv_kernel<K, true, true, true>)
+                      : (rowmajor ? gemv_kernel<K, false, false, true> : gemv_kernel<K, true, false, true>);
+    return launch_kernel(kern, dim3(G), dim3(kThreads), st, x, codes_g, scales_g, lut_g, h, codes_u,
+                         scales_u, lut_u, h, G, lay, N, nb);
 }
 
 // ---------------------------------------------------------------------------
@@ -626,6 +689,18 @@ hipError_t launch_gemv_dual(const uint16_t* x, const uint32_t* codes_a, const fl
     case 2: return launch_gemv_k<2>(x, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
     case 3: return launch_gemv_k<3>(x, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
     case 4: return launch_gemv_k<4>(x, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemv_swiglu(const uint16_t* x, const uint32_t* codes_g, const float* scales_g,
+                              const float* lut_g, const uint32_t* codes_u, const float* scales_u,
+                              const float* lut_u, uint16_t* h, CodeLayout lay, int N, int nb, int k,
+                              hipStream_t st) {
+    switch (k) {
+    case 2: return launch_gemv_swiglu_k<2>(x, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
+    case 3: return launch_gemv_swiglu_k<3>(x, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
+    case 4: return launch_gemv_swiglu_k<4>(x, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
     default: return hipErrorInvalidValue;
     }
 }

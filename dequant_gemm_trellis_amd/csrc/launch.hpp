@@ -52,6 +52,14 @@ hipError_t launch_gemv_dual(const uint16_t* x, const uint32_t* codes_a, const fl
                             const float* scales_b, const float* lut_b, uint16_t* y_b,
                             CodeLayout lay, int N, int nb, int k, hipStream_t st);
 
+// Gate and up (one activation row) with the SwiGLU epilogue in one launch:
+// h[n] = bf16(silu(g_n) * u_n) from the float32 row sums of both projections;
+// same conditions as launch_gemv.
+hipError_t launch_gemv_swiglu(const uint16_t* x, const uint32_t* codes_g, const float* scales_g,
+                              const float* lut_g, const uint32_t* codes_u, const float* scales_u,
+                              const float* lut_u, uint16_t* h, CodeLayout lay, int N, int nb, int k,
+                              hipStream_t st);
+
 // Axis 1, 1 <= M <= kGemvRowsMaxM, in the GEMV's unit mapping (one workgroup
 // per compute unit, at least 16 rows each); gemv_rows_supported says whether
 // the geometry fits it (at least 16 rows, 16 rows' unit partials fit in LDS)
@@ -78,6 +86,15 @@ hipError_t launch_axis1_dual(const uint16_t* x, int M, const uint32_t* codes_a,
                              const uint32_t* codes_b, const float* scales_b, const float* lut_b,
                              uint16_t* y_b, CodeLayout lay, int N, int nb, int k,
                              hipStream_t st);
+
+// Gate and up over the same x[M][nb*256], 1 <= M <= 32, with the SwiGLU
+// epilogue, in one launch of the 16-row-group kernel (the grid of
+// launch_axis1, every workgroup decoding its rows of both projections):
+// h[m][n] = bf16(silu(g[m][n]) * u[m][n]) from the float32 sums.
+hipError_t launch_axis1_swiglu(const uint16_t* x, int M, const uint32_t* codes_g,
+                               const float* scales_g, const float* lut_g, const uint32_t* codes_u,
+                               const float* scales_u, const float* lut_u, uint16_t* h,
+                               CodeLayout lay, int N, int nb, int k, hipStream_t st);
 
 // Axis 0, 1 <= M <= 32: per-part partials, then the ordered reduce over the
 // parts into y[M][C]. `partial` holds axis0_parts(R, C) * M * C floats.

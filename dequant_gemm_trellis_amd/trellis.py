@@ -35,10 +35,13 @@ OP_GEMV_SCATTER = 1
 OP_PREFILL = 2
 MAX_M = 32
 
-# Every function trellis.h declares, for the export check.
+# Every function the headers under include/ declare, for the export check.
 EXPORTED = ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_dual", "trellis_gemv_scatter",
-            "trellis_prefill", "trellis_prefill_dual", "trellis_workspace_bytes", "trellis_expand",
-            "trellis_repack", "trellis_strerror")
+            "trellis_prefill", "trellis_prefill_dual", "trellis_gate_up_swiglu",
+            "trellis_workspace_bytes", "trellis_expand", "trellis_repack", "trellis_strerror",
+            "trellis_gather_probe",
+            "trellis_gather_probe_values", "trellis_gather_probe_out_floats")
+PROBE_PAIR_B64, PROBE_COPIES8_B32, PROBE_SINGLE_B32 = 0, 1, 2
 
 
 class Geometry(C.Structure):
@@ -61,14 +64,23 @@ _lib.trellis_gemv_scatter.argtypes = [_vp, _vp, _vp, _vp, _GP, _vp, C.c_size_t, 
 _lib.trellis_prefill.argtypes = [_vp, C.c_int32, _vp, _vp, _vp, _GP, _vp, C.c_size_t, _vp, _vp]
 _lib.trellis_prefill_dual.argtypes = [_vp, C.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _GP,
                                       _vp]
+_lib.trellis_gate_up_swiglu.argtypes = [_vp, C.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _GP, _vp,
+                                        _vp]
 _lib.trellis_workspace_bytes.argtypes = [_GP, C.c_int32, C.c_int32]
 _lib.trellis_workspace_bytes.restype = C.c_size_t
 _lib.trellis_expand.argtypes = [_vp, _vp, _vp, _GP, _vp, _vp]
 _lib.trellis_repack.argtypes = [_vp, _vp, _GP, C.c_int32, _vp]
 _lib.trellis_strerror.argtypes = [C.c_int]
 _lib.trellis_strerror.restype = C.c_char_p
+_lib.trellis_gather_probe.argtypes = [C.c_int32, C.c_int32, _vp, C.c_size_t, _vp]
+_lib.trellis_gather_probe.restype = C.c_int
+_lib.trellis_gather_probe_values.argtypes = [C.c_int32, C.c_int32]
+_lib.trellis_gather_probe_values.restype = C.c_uint64
+_lib.trellis_gather_probe_out_floats.argtypes = []
+_lib.trellis_gather_probe_out_floats.restype = C.c_size_t
 for _f in ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_dual", "trellis_gemv_scatter",
-           "trellis_prefill", "trellis_prefill_dual", "trellis_expand", "trellis_repack"):
+           "trellis_prefill", "trellis_prefill_dual", "trellis_gate_up_swiglu", "trellis_expand",
+           "trellis_repack"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -196,6 +208,22 @@ def prefill_dual(x, a, b, g, y_a=None, y_b=None, stream=None) -> tuple[torch.Ten
     return y_a, y_b
 
 
+def gate_up_swiglu(x, gate, up, g, h=None, stream=None) -> torch.Tensor:
+    """h = bf16(silu(x Wg^T) * (x Wu^T)) for x [M][in] (or [in] for M = 1);
+    gate and up are (codes, scales, lut) triples of the same axis-1 geometry
+    g. Returns h, [M][out] (or [out] for a 1-D x)."""
+    geom = _geom(g)
+    M = x.shape[0] if x.dim() == 2 else 1
+    if h is None:
+        shape = (M, geom.out_features) if x.dim() == 2 else (geom.out_features,)
+        h = torch.empty(shape, dtype=torch.bfloat16, device=x.device)
+    (cg, sg, lg), (cu, su, lu) = gate, up
+    _check("trellis_gate_up_swiglu", _lib.trellis_gate_up_swiglu(
+        _dev(x), M, _dev(cg), _dev(sg), _dev(lg), _dev(cu), _dev(su), _dev(lu), C.byref(geom),
+        _dev(h), _stream(stream)))
+    return h
+
+
 def expand(codes, scales, lut, g, w=None, stream=None) -> torch.Tensor:
     geom = _geom(g)
     rows = geom.out_features if geom.axis == 1 else geom.in_features
@@ -216,3 +244,16 @@ def repack(codes, g, to_block_interleave: int, out=None, stream=None) -> torch.T
     _check("trellis_repack", _lib.trellis_repack(_dev(codes), _dev(out), C.byref(geom),
                                                  to_block_interleave, _stream(stream)))
     return out
+
+
+def gather_probe(kind: int, rounds: int, out: torch.Tensor, stream=None) -> int:
+    """Enqueue one launch of the LDS codebook-gather probe (trellis_probe.h);
+    returns the number of decoded-weight values its timed loop reads."""
+    status = _lib.trellis_gather_probe(kind, rounds, _dev(out), out.numel(), _stream(stream))
+    if status != OK:
+        raise RuntimeError(f"trellis_gather_probe: status {status}")
+    return int(_lib.trellis_gather_probe_values(kind, rounds))
+
+
+def gather_probe_out_floats() -> int:
+    return int(_lib.trellis_gather_probe_out_floats())

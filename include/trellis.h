@@ -197,8 +197,35 @@ int trellis_prefill_dual(const uint16_t *x, int32_t M, const uint32_t *codes_a,
                          uint16_t *y_b, const trellis_geometry *g, hipStream_t stream);
 
 /*
+ * The gate and up projections of a decoder MLP with their SwiGLU epilogue, in
+ * one launch, for 0 <= M <= 32 activation rows (M = 0 is a no-op):
+ *   h[m][n] = bf16( silu(g[m][n]) * u[m][n] ),   silu(v) = v / (1 + e^-v),
+ *   g[m][n] = sum_k x[m][k] * Wg[n][k],  u[m][n] = sum_k x[m][k] * Wu[n][k]
+ * with Wg from (codes_g, scales_g, lut_g) and Wu from (codes_u, scales_u,
+ * lut_u), each laid out as for trellis_prefill; g (axis 1) describes both;
+ * x: bf16 [M][in]; h: bf16 [M][out], which then feeds the down projection.
+ * g and u are the float32 sums (never rounded to bf16), silu is evaluated in
+ * float32, and only h is rounded. The pages tune their kernels for the Qwen
+ * MLP geometry (page 60 tiled-prefill.ts, its dispatch notes; page 60
+ * wide-prefill.ts takes that model's normalised activations) but print no
+ * activation function; SwiGLU is that MLP's, and the fused epilogue is this
+ * library's. Each workgroup decodes a row range of the gate, restages its
+ * codebook table from the up codebook and decodes the same rows of the up
+ * projection, so both sums of an output meet in one workgroup: no workspace,
+ * a fixed summation order (repeated calls give identical bits).
+ */
+int trellis_gate_up_swiglu(const uint16_t *x, int32_t M, const uint32_t *codes_g,
+                           const float *scales_g, const float *lut_g, const uint32_t *codes_u,
+                           const float *scales_u, const float *lut_u,
+                           const trellis_geometry *g, uint16_t *h, hipStream_t stream);
+
+/*
  * Workspace bytes an operation needs for geometry g and batch M (0 if it
- * needs none). Returns (size_t)-1 if g, M or op is not supported.
+ * needs none). Returns (size_t)-1 if g, M or op is not supported. The
+ * workspace holds the split-K float32 partials of the axis-0 operations
+ * (page 59 splitk-prefill.ts sizes its workspace as splits x M x N floats
+ * and keeps no dense weight buffer): P x M x out floats here, P as at
+ * trellis_gemv_scatter.
  */
 size_t trellis_workspace_bytes(const trellis_geometry *g, int32_t M, int32_t op);
 
@@ -223,7 +250,9 @@ int trellis_expand(const uint32_t *codes, const float *scales, const float *lut,
 int trellis_repack(const uint32_t *src, uint32_t *dst, const trellis_geometry *g,
                    int32_t to_block_interleave, hipStream_t stream);
 
-/* Static, human-readable text for a status code. */
+/* Static, human-readable text for a status code (the entry points reject
+ * unsupported input before any launch, as page 60 tiled-prefill.ts throws
+ * before dispatching; this names the reason). */
 const char *trellis_strerror(int status);
 
 #ifdef __cplusplus

@@ -72,3 +72,21 @@ def row_subset(p: synth.Problem, rows: np.ndarray) -> synth.Problem:
 
 SAMPLE_ROWS = np.concatenate([np.arange(0, 40), np.arange(8700, 8740),
                               np.arange(QWEN_OUT - 40, QWEN_OUT)])
+
+
+def oracle_columns(fn, n_out: int, workers: int = 16, chunk: int = 256):
+    """Run fn(n_begin, n_end) -> array [M, n_out] (zeros outside the range) over
+    column chunks on a thread pool and add the results: the oracle's C code
+    releases the GIL, so a full-size reference takes seconds instead of
+    minutes. Each column is still computed by the oracle alone."""
+    import concurrent.futures as cf
+
+    bounds = [(b, min(n_out, b + chunk)) for b in range(0, n_out, chunk)]
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        parts = list(ex.map(lambda be: (be, fn(*be)), bounds))
+    out = None
+    for (b, e), a in parts:
+        if out is None:
+            out = np.zeros_like(a)
+        out[:, b:e] = a[:, b:e]
+    return out
