@@ -145,6 +145,25 @@ int trellis_gemv_scatter(const uint16_t* x, const uint32_t* codes, const float* 
                                            d.cols, g->k, stream));
 }
 
+int trellis_gemv_scatter_static(const uint16_t* x, const uint32_t* codes, const float* scales,
+                                const float* lut, const trellis_geometry* g, uint16_t* y,
+                                hipStream_t stream) {
+    Dims d;
+    int st = check_geometry(g, &d);
+    if (st) return st;
+    if (g->axis != 0) return TRELLIS_ERR_GEOMETRY;
+    if ((st = check_operands(codes, scales, lut)) || (st = check_io(x, y))) return st;
+    if (axis0_workspace(d, 1) > trellis_static_scratch_bytes()) return TRELLIS_ERR_WORKSPACE;
+    float* partial = nullptr;
+    if (trellis::static_scratch(&partial) != hipSuccess) return TRELLIS_ERR_HIP;
+    return status_of(trellis::launch_axis0(x, 1, codes, d.lay, scales, lut, partial, y, d.rows,
+                                           d.cols, g->k, stream));
+}
+
+size_t trellis_static_scratch_bytes(void) {
+    return trellis::kStaticScratchFloats * sizeof(float);
+}
+
 int trellis_prefill(const uint16_t* x, int32_t M, const uint32_t* codes, const float* scales,
                     const float* lut, const trellis_geometry* g, float* workspace,
                     size_t workspace_bytes, uint16_t* y, hipStream_t stream) {

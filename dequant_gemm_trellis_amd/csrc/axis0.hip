@@ -33,12 +33,20 @@
 // step is decoded (the first-generation kernel, one wave per split, four per
 // workgroup, restaged the codebook in 1280 workgroups and waited on every
 // step's loads).
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace trellis {
+
+// Partials of the scatter variant that allocates nothing: one array per
+// device, held until the process ends. Host code never passes this name to a
+// kernel (on the host it is only a stand-in for the symbol); it uses the
+// device address static_scratch() looked up for the current device.
+__device__ __align__(256) float scratch[kStaticScratchFloats];
+
 namespace {
 
 constexpr int kThreads = 256;       // split reduce
@@ -409,6 +417,25 @@ hipError_t launch_axis0_v(const uint16_t* x, int M, const uint32_t* codes, CodeL
 }
 
 }  // namespace
+
+hipError_t static_scratch(float** ptr) {
+    static std::mutex mu;
+    static float* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = static_cast<float*>(p);
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 int axis0_parts(int R, int C) {
     const int tiles = C / kTileCols, steps = (R + 31) / 32;

@@ -103,6 +103,14 @@ hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, CodeLay
                         int C, int k, hipStream_t st);
 int axis0_parts(int R, int C);
 
+// The scatter variant that allocates nothing keeps its split-K partials in a
+// file-scope device array of kStaticScratchFloats floats (2 MB), one per
+// device. static_scratch returns the current device's address of it, looked
+// up with hipGetSymbolAddress on the first call on that device.
+constexpr size_t kStaticScratchFloats = size_t(1) << 19;
+constexpr int kMaxDevices = 64;
+hipError_t static_scratch(float** ptr);
+
 // Decoded weights w[rows][nb*256].
 hipError_t launch_expand(const uint32_t* codes, CodeLayout lay, const float* scales,
                          const float* lut, uint16_t* w, long rows, int nb, int k, hipStream_t st);

@@ -38,8 +38,8 @@ MAX_M = 32
 # Every function the headers under include/ declare, for the export check.
 EXPORTED = ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_dual", "trellis_gemv_scatter",
             "trellis_prefill", "trellis_prefill_dual", "trellis_gate_up_swiglu",
-            "trellis_workspace_bytes", "trellis_expand", "trellis_repack", "trellis_strerror",
-            "trellis_gather_probe",
+            "trellis_gemv_scatter_static", "trellis_static_scratch_bytes", "trellis_workspace_bytes",
+            "trellis_expand", "trellis_repack", "trellis_strerror", "trellis_gather_probe",
             "trellis_gather_probe_values", "trellis_gather_probe_out_floats")
 PROBE_PAIR_B64, PROBE_COPIES8_B32, PROBE_SINGLE_B32 = 0, 1, 2
 
@@ -66,6 +66,9 @@ _lib.trellis_prefill_dual.argtypes = [_vp, C.c_int32, _vp, _vp, _vp, _vp, _vp, _
                                       _vp]
 _lib.trellis_gate_up_swiglu.argtypes = [_vp, C.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _GP, _vp,
                                         _vp]
+_lib.trellis_gemv_scatter_static.argtypes = [_vp, _vp, _vp, _vp, _GP, _vp, _vp]
+_lib.trellis_static_scratch_bytes.argtypes = []
+_lib.trellis_static_scratch_bytes.restype = C.c_size_t
 _lib.trellis_workspace_bytes.argtypes = [_GP, C.c_int32, C.c_int32]
 _lib.trellis_workspace_bytes.restype = C.c_size_t
 _lib.trellis_expand.argtypes = [_vp, _vp, _vp, _GP, _vp, _vp]
@@ -80,7 +83,7 @@ _lib.trellis_gather_probe_out_floats.argtypes = []
 _lib.trellis_gather_probe_out_floats.restype = C.c_size_t
 for _f in ("trellis_lut_upload", "trellis_gemv", "trellis_gemv_dual", "trellis_gemv_scatter",
            "trellis_prefill", "trellis_prefill_dual", "trellis_gate_up_swiglu", "trellis_expand",
-           "trellis_repack"):
+           "trellis_repack", "trellis_gemv_scatter_static"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -175,6 +178,21 @@ def gemv_scatter(x, codes, scales, lut, g, workspace=None, y=None, stream=None) 
         _dev(x), _dev(codes), _dev(scales), _dev(lut), C.byref(geom), _dev(workspace),
         workspace.numel() * workspace.element_size(), _dev(y), _stream(stream)))
     return y
+
+
+def gemv_scatter_static(x, codes, scales, lut, g, y=None, stream=None) -> torch.Tensor:
+    """trellis_gemv_scatter with its partials in the library's static device
+    array (no workspace); calls overlapping on one device race."""
+    geom = _geom(g)
+    if y is None:
+        y = torch.empty(geom.out_features, dtype=torch.bfloat16, device=x.device)
+    _check("trellis_gemv_scatter_static", _lib.trellis_gemv_scatter_static(
+        _dev(x), _dev(codes), _dev(scales), _dev(lut), C.byref(geom), _dev(y), _stream(stream)))
+    return y
+
+
+def static_scratch_bytes() -> int:
+    return int(_lib.trellis_static_scratch_bytes())
 
 
 def prefill(x, codes, scales, lut, g, workspace=None, y=None, stream=None) -> torch.Tensor:

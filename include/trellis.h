@@ -161,6 +161,27 @@ int trellis_gemv_scatter(const uint16_t *x, const uint32_t *codes, const float *
                          size_t workspace_bytes, uint16_t *y, hipStream_t stream);
 
 /*
+ * trellis_gemv_scatter without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the float32 partials go to a static
+ * device array of trellis_static_scratch_bytes() bytes (2 MB; one per device,
+ * held until the process ends), which covers the scatter of every accepted
+ * geometry (P * out <= 2^19 floats); a geometry needing more returns
+ * TRELLIS_ERR_WORKSPACE. The call allocates nothing: the array's device
+ * address is looked up once per device on the first call there. Outputs are
+ * bit-identical to trellis_gemv_scatter's. Every call on a device shares that
+ * device's array, so calls that overlap on one device (concurrent streams,
+ * host threads) race and give undefined results; calls ordered on one stream
+ * are safe (each overwrites every partial it reads).
+ */
+int trellis_gemv_scatter_static(const uint16_t *x, const uint32_t *codes, const float *scales,
+                                const float *lut, const trellis_geometry *g, uint16_t *y,
+                                hipStream_t stream);
+
+/* Bytes of the static partials array of trellis_gemv_scatter_static. */
+size_t trellis_static_scratch_bytes(void);
+
+/*
  * Small-batch GEMM (prefill), M activation rows, 0 <= M <= 32 (M = 0 is a
  * no-op that returns TRELLIS_OK):
  *   axis 1: y[m][n] = bf16( sum_k x[m][k] * W[n][k] )   (page 60 tiled-prefill.ts)

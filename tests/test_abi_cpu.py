@@ -293,3 +293,22 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
 
+
+def test_static_scatter_validation(T):
+    """The no-allocation scatter checks its arguments like the regular one
+    (no workspace argument; the static array's size is fixed)."""
+    lib = T.raw()
+    assert T.static_scratch_bytes() == 2 << 20
+
+    def call(g, x=FAKE, codes=FAKE, scales=FAKE, lut=FAKE, y=FAKE):
+        return lib.trellis_gemv_scatter_static(C.c_void_p(x), C.c_void_p(codes),
+                                               C.c_void_p(scales), C.c_void_p(lut),
+                                               C.byref(g) if g is not None else None,
+                                               C.c_void_p(y), C.c_void_p(0))
+
+    assert call(None) == T.ERR_NULL
+    assert call(geom(T, axis=1)) == T.ERR_GEOMETRY
+    assert call(geom(T, axis=0, k=5)) == T.ERR_GEOMETRY
+    assert call(geom(T, axis=0), x=0) == T.ERR_NULL
+    assert call(geom(T, axis=0), y=FAKE + 2) == T.ERR_ALIGN
+    assert call(geom(T, axis=0), codes=FAKE + 4) == T.ERR_ALIGN
