@@ -70,9 +70,6 @@ def row_subset(p: synth.Problem, rows: np.ndarray) -> synth.Problem:
                          np.ascontiguousarray(p.scales[rows]), x)
 
 
-SAMPLE_ROWS = np.concatenate([np.arange(0, 40), np.arange(8700, 8740),
-                              np.arange(QWEN_OUT - 40, QWEN_OUT)])
-
 
 def oracle_columns(fn, n_out: int, workers: int = 16, chunk: int = 256):
     """Run fn(n_begin, n_end) -> array [M, n_out] (zeros outside the range) over
@@ -90,3 +87,36 @@ def oracle_columns(fn, n_out: int, workers: int = 16, chunk: int = 256):
             out = np.zeros_like(a)
         out[:, b:e] = a[:, b:e]
     return out
+
+
+def oracle_y_full(p: synth.Problem, workers: int = 16):
+    """The oracle's whole output for a problem ([M, out] float64), columns
+    computed in parallel chunks (oracle_columns)."""
+    import oracle
+
+    s = p.shape
+    return oracle_columns(
+        lambda b, e: oracle.fused_f64(p.x, p.codes, p.scales, p.lut, s.axis, s.T, s.L, s.k,
+                                      s.in_features, s.out_features, b, e,
+                                      block_interleave=s.block_interleave),
+        s.out_features, workers)
+
+
+def oracle_W_full(p: synth.Problem, workers: int = 16, chunk: int = 512) -> np.ndarray:
+    """The oracle's decoded weights [rows, cols] (bf16 bits), stored rows
+    expanded in parallel chunks."""
+    import concurrent.futures as cf
+
+    import oracle
+
+    s = p.shape
+    bounds = [(b, min(s.rows, b + chunk)) for b in range(0, s.rows, chunk)]
+
+    def part(be):
+        sub = row_subset(p, np.arange(*be))
+        t = sub.shape
+        return oracle.expand(sub.codes, sub.scales, sub.lut, t.axis, t.T, t.L, t.k,
+                             t.in_features, t.out_features)
+
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        return np.concatenate(list(ex.map(part, bounds)), axis=0)
