@@ -312,3 +312,49 @@ def test_static_scatter_validation(T):
     assert call(geom(T, axis=0), x=0) == T.ERR_NULL
     assert call(geom(T, axis=0), y=FAKE + 2) == T.ERR_ALIGN
     assert call(geom(T, axis=0), codes=FAKE + 4) == T.ERR_ALIGN
+
+
+def test_gate_up_swiglu_validation(T):
+    """The fused gate/up SwiGLU entry point checks geometry, batch size,
+    pointers and alignment on the host; M = 0 is a no-op."""
+    lib = T.raw()
+    g = geom(T)
+    far = FAKE + (1 << 20)
+
+    def call(g, M, x=FAKE, cg=FAKE, sg=FAKE, lg=FAKE, cu=FAKE, su=FAKE, lu=FAKE, h=far):
+        return lib.trellis_gate_up_swiglu(
+            C.c_void_p(x), M, C.c_void_p(cg), C.c_void_p(sg), C.c_void_p(lg), C.c_void_p(cu),
+            C.c_void_p(su), C.c_void_p(lu), C.byref(g) if g is not None else None, C.c_void_p(h),
+            C.c_void_p(0))
+
+    assert call(None, 4) == T.ERR_NULL
+    assert call(geom(T, axis=0, i=256, o=512), 4) == T.ERR_GEOMETRY
+    assert call(geom(T, k=5), 4) == T.ERR_GEOMETRY
+    assert call(g, -1) == T.ERR_GEOMETRY
+    assert call(g, 33) == T.ERR_GEOMETRY
+    for arg in ("x", "cg", "sg", "lg", "cu", "su", "lu", "h"):
+        assert call(g, 4, **{arg: 0}) == T.ERR_NULL, arg
+    for arg, addr in (("x", FAKE + 2), ("cg", FAKE + 4), ("lu", FAKE + 8), ("h", far + 2),
+                      ("su", FAKE + 2)):
+        assert call(g, 4, **{arg: addr}) == T.ERR_ALIGN, arg
+    assert call(g, 0) == T.OK
+
+
+def test_gather_probe_validation(T):
+    """The gather probe rejects a bad kind, round count or output buffer on the
+    host, and reports how many values a launch reads."""
+    lib = T.raw()
+    n = T.gather_probe_out_floats()
+    assert n > 0 and n % 512 == 0
+
+    def call(kind, rounds, out=FAKE, floats=n):
+        return lib.trellis_gather_probe(kind, rounds, C.c_void_p(out), floats, C.c_void_p(0))
+
+    assert call(3, 10) == -2 and call(-1, 10) == -2
+    assert call(0, -1) == -2 and call(0, (1 << 20) + 1) == -2
+    assert call(0, 10, out=0) == -2
+    assert call(1, 10, floats=n - 1) == -2
+    assert lib.trellis_gather_probe_values(0, 10) == n * 32 * 10 * 2
+    assert lib.trellis_gather_probe_values(1, 10) == n * 32 * 10
+    assert lib.trellis_gather_probe_values(2, 3) == n * 32 * 3
+    assert lib.trellis_gather_probe_values(5, 3) == 0

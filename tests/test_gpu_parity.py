@@ -512,28 +512,40 @@ def test_graph_capture_replays_match_eager(gpu_lib):
     y2 = torch.empty((5, 600), dtype=torch.bfloat16, device="cuda:0")
     y3 = torch.empty(768, dtype=torch.bfloat16, device="cuda:0")
 
+    y4 = torch.empty((5, 600), dtype=torch.bfloat16, device="cuda:0")
+    y5 = torch.empty(768, dtype=torch.bfloat16, device="cuda:0")
+    y6 = torch.empty(600, dtype=torch.bfloat16, device="cuda:0")
+
     def step(stream):
         T.gemv(du.x.reshape(-1), du.codes, du.scales, du.lut, up, y=y1, stream=stream)
         T.prefill(dp.x, dp.codes, dp.scales, dp.lut, up, y=y2, stream=stream)
         T.gemv_scatter(dd.x.reshape(-1), dd.codes, dd.scales, dd.lut, down, workspace=ws,
                        y=y3, stream=stream)
+        T.gate_up_swiglu(dp.x, (dp.codes, dp.scales, dp.lut), (du.codes, du.scales, du.lut), up,
+                         h=y4, stream=stream)
+        T.gemv_scatter_static(dd.x.reshape(-1), dd.codes, dd.scales, dd.lut, down, y=y5,
+                              stream=stream)
+        T.gate_up_swiglu(du.x, (du.codes, du.scales, du.lut), (dp.codes, dp.scales, dp.lut), up,
+                         h=y6, stream=stream)
 
-    say("graph capture: gemv + prefill + scatter")
+    say("graph capture: gemv + prefill + scatter + swiglu + static scatter")
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         step(s)
     torch.cuda.synchronize()
-    ref = [bf16_bits(y.clone()) for y in (y1, y2, y3)]
+    ys = (y1, y2, y3, y4, y5, y6)
+    ref = [bf16_bits(y.clone()) for y in ys]
+    assert np.array_equal(ref[4], ref[2])   # the static scatter matches the workspace one
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         step(s)
     for rep in range(4):
-        for y in (y1, y2, y3):
+        for y in ys:
             y.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for r, y in zip(ref, (y1, y2, y3)):
+        for r, y in zip(ref, ys):
             assert np.array_equal(bf16_bits(y), r), rep
     assert gate(bf16_to_f64(y1.reshape(1, -1)), oracle_y(pu)) <= TOL
 
