@@ -92,15 +92,40 @@ struct TaskCtx {
     CodeLayout lay;
     const float* scales;
     int nb, gc, r0, r1, j, cp;
+    // Mixed groups (MIXED): virtual row v < rm is row r0 + v of the first
+    // projection (codes, scales), v >= rm row r0 + v - rm of the second
+    // (codes_b, scales_b), whose codebook sits 16 KB above the first in LDS.
+    const uint32_t* codes_b;
+    const float* scales_b;
+    int rm;
 };
 
 template <int K>
 struct Task {
     uint32_t w[2 * K + 1];
     float scale;
-    int b, g;    // block and row group: uniform across the wave
-    bool valid;  // this lane's row lies in the workgroup's range
+    int b, g;      // block and row group: uniform across the wave
+    bool valid;    // this lane's row lies in the workgroup's range
+    uint32_t sel;  // MIXED: byte offset of this lane's codebook in LDS
 };
+
+// The stored row, code array and scales of lane row 16 g + j of a task, and
+// whether it is a real row (rows past the range re-read the last real one).
+template <bool MIXED>
+__device__ __forceinline__ int task_row(const TaskCtx& cx, int g, bool& valid, bool& second) {
+    const int v = 16 * g + cx.j;
+    if constexpr (MIXED) {
+        valid = v < 2 * cx.rm;
+        const int vc = valid ? v : 2 * cx.rm - 1;
+        second = vc >= cx.rm;
+        return cx.r0 + (second ? vc - cx.rm : vc);
+    } else {
+        const int row = cx.r0 + v;
+        valid = row < cx.r1;
+        second = false;
+        return valid ? row : cx.r1 - 1;
+    }
+}
 
 // Word offset of block b of row rc. Row-major codes (PAIRS false) keep the
 // plain row-major product; the general layout form measured 1% slower there
@@ -114,40 +139,46 @@ __device__ __forceinline__ uint64_t task_word(const TaskCtx& cx, int rc, int b) 
 // Load task tau's code words (2k per lane) and scale. Past the wave's last
 // task it re-reads that task: every load is unconditional, so the compiler's
 // memory-counter waits never have to cover a skipped load.
-template <int K, bool PAIRS>
+template <int K, bool PAIRS, bool MIXED = false>
 __device__ __forceinline__ void load_task(Task<K>& t, const TaskCtx& cx, int tau, int tau_end) {
     const int tc = tau < tau_end ? tau : tau_end - 1;
     const int b = tc / cx.gc;
     const int g = tc - b * cx.gc;
-    const int row = cx.r0 + 16 * g + cx.j;
-    t.valid = row < cx.r1;
-    const int rc = t.valid ? row : cx.r1 - 1;
+    bool second;
+    const int rc = task_row<MIXED>(cx, g, t.valid, second);
     t.b = b;
     t.g = g;
-    load_run64_words<K>(cx.codes + task_word<K, PAIRS>(cx, rc, b), cx.cp, t.w);
-    t.scale = cx.scales[rc];
+    t.sel = second ? kLutEntries * 4 : 0;
+    const uint32_t* codes = second ? cx.codes_b : cx.codes;
+    const float* scales = second ? cx.scales_b : cx.scales;
+    load_run64_words<K>(codes + task_word<K, PAIRS>(cx, rc, b), cx.cp, t.w);
+    t.scale = scales[rc];
 }
 
 // load_task through opaque global-address-space pointers, for the prologue:
 // through the restrict kernel pointers the loads count as invariant and the
 // compiler sinks them past the table stores and the barrier to their first
 // use, so the table stores and the code words no longer overlap.
-template <int K, bool PAIRS>
+template <int K, bool PAIRS, bool MIXED = false>
 __device__ __forceinline__ void load_task_opaque(Task<K>& t, const TaskCtx& cx, int tau, int tau_end) {
     using gu32 = const __attribute__((address_space(1))) uint32_t*;
     using gu32x4 = const __attribute__((address_space(1))) u32x4*;
     using gf32 = const __attribute__((address_space(1))) float*;
-    gu32 codes = (gu32)cx.codes;  // generic to global: an address-space cast
-    gf32 scales = (gf32)cx.scales;
-    asm volatile("" : "+s"(codes), "+s"(scales));
+    gu32 codes_a = (gu32)cx.codes;  // generic to global: an address-space cast
+    gf32 scales_a = (gf32)cx.scales;
+    gu32 codes_b = (gu32)cx.codes_b;
+    gf32 scales_b = (gf32)cx.scales_b;
+    asm volatile("" : "+s"(codes_a), "+s"(scales_a), "+s"(codes_b), "+s"(scales_b));
     const int tc = tau < tau_end ? tau : tau_end - 1;
     const int b = tc / cx.gc;
     const int g = tc - b * cx.gc;
-    const int row = cx.r0 + 16 * g + cx.j;
-    t.valid = row < cx.r1;
-    const int rc = t.valid ? row : cx.r1 - 1;
+    bool second;
+    const int rc = task_row<MIXED>(cx, g, t.valid, second);
     t.b = b;
     t.g = g;
+    t.sel = second ? kLutEntries * 4 : 0;
+    const gu32 codes = second ? codes_b : codes_a;
+    const gf32 scales = second ? scales_b : scales_a;
     const gu32 p = codes + task_word<K, PAIRS>(cx, rc, b) + 2 * K * cx.cp;
     if constexpr (K == 2) {
         const u32x4 v = *reinterpret_cast<gu32x4>(p);
@@ -280,19 +311,24 @@ struct XSource {
 // block change earlier (or in the prologue), which then fetches the next
 // block's; on the staged path through the LDS slot, the one memory wait that
 // covers the prefetched code words.
-template <int K, int MT, bool DIRECT, int KG>
+// MIXED (staged activations, k = 3, 4): each lane reads the plain codebook of
+// its row's projection (Task::sel), and the activation slot holds all four
+// lines.
+template <int K, int MT, bool DIRECT, int KG, bool MIXED = false>
 __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& xn, int& xb,
                                          const XSource<MT>& xs, floatx4 (&acc)[KG][MT],
                                          const float* __restrict__ tab, int lane, int j, int c) {
+    static_assert(!MIXED || (K != 2 && !DIRECT), "mixed groups read two plain codebooks");
     constexpr bool P = PrefillLds<K, MT, DIRECT>::pair;
     constexpr bool REP = PrefillLds<K, MT, DIRECT>::rep;
+    constexpr int kLines = MIXED ? 4 : PrefillLds<K, MT, DIRECT>::lines;
     if (t.b != xb) {
         xb = t.b;
         if constexpr (DIRECT) {
             xf = xn;
             load_x_frags<MT>(xn, xs.xa, t.b + 1 < xs.nb ? t.b + 1 : xs.nb - 1);
         } else {
-            load_x_block<MT, PrefillLds<K, MT, DIRECT>::lines>(xf, xs.slot, xs.xrows, t.b, lane, j, c);
+            load_x_block<MT, kLines>(xf, xs.slot, xs.xrows, t.b, lane, j, c);
         }
     }
     if (!t.valid) {
@@ -313,13 +349,18 @@ __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& 
     });
     // Fragments 7 .. 0: only fragment 0 reads the word from the neighbouring
     // lane, which thus has the whole task to arrive.
-    Gathered<P> g0 = gather_tab<K, 7, P, REP>(t.w, tab);
-    Gathered<P> g1 = gather_tab<K, 6, P, REP>(t.w, tab);
+    auto gather = [&](auto sc) {
+        constexpr int S = decltype(sc)::value;
+        if constexpr (MIXED) return gather_run64_sel<K, S>(t.w, tab, t.sel);
+        else return gather_tab<K, S, P, REP>(t.w, tab);
+    };
+    Gathered<P> g0 = gather(std::integral_constant<int, 7>{});
+    Gathered<P> g1 = gather(std::integral_constant<int, 6>{});
     static_for<0, 8>([&](auto ic) {
         constexpr int S = 7 - decltype(ic)::value;
         Gathered<P> g2;
         __builtin_amdgcn_s_setprio(2);  // the gathers issue at raised priority
-        if constexpr (S >= 2) g2 = gather_tab<K, S - 2, P, REP>(t.w, tab);
+        if constexpr (S >= 2) g2 = gather(std::integral_constant<int, S - 2>{});
         __builtin_amdgcn_s_setprio(0);
         const bf16x8 bfrag = as_bf16x8(pack_fragment<P>(g0, t.scale));
 #pragma unroll
@@ -401,7 +442,7 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     xs.slot = reinterpret_cast<u32x4*>(lds + Lds::tab_floats) + wave * Lds::slot_chunks;
     xs.nb = nb;
 
-    TaskCtx cx{codes, lay, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp};
+    TaskCtx cx{codes, lay, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp, codes, scales, 0};
     floatx4 acc[KG][MT];
 #pragma unroll
     for (int g = 0; g < KG; ++g)
@@ -499,6 +540,134 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
         reduce([&](int, int, int mm, int row, float s) {
             if (mm < M && row < r1) y[static_cast<size_t>(mm) * N + row] = round_bf16(s);
         });
+    }
+}
+
+// Gate and up with the SwiGLU epilogue at k = 3, 4 and two M tiles (M = 17..32),
+// in mixed groups. Both projections read the same activations, so a 16-row
+// MFMA group may hold rows of either as long as each lane reads its own row's
+// codebook: the two plain 16 KB codebooks sit one after the other in LDS and a
+// lane's gather offset carries its projection (Task::sel). A workgroup owns
+// rows [r0, r1) of both, rm <= 72 of them, i.e. 2 rm virtual rows in at most
+// kDualGroups groups -- the slot count of the dual launch, where the two-phase
+// kernel runs two rounds of five -- with the four-line activation slots beside
+// the two codebooks (160 KB). The waves' tiles are reduced as in the prefill
+// epilogue; output (m, i) is bf16(silu(g) * u) with g the sum of virtual row
+// i and u that of virtual row rm + i.
+constexpr int kMixedRows = 16 * kDualGroups / 2;  // rows of each projection per workgroup
+
+struct MixedLds {
+    static constexpr int threads = 512, waves = threads / kWave, MT = 2;
+    static constexpr int tab_floats = 2 * kLutEntries;
+    static constexpr int slot_chunks = MT * 4 * 16 * 8;
+    static constexpr int decode_floats = tab_floats + waves * slot_chunks * 4;
+    static constexpr int part_floats = waves * kDualGroups * 256;
+    static constexpr int floats = decode_floats > part_floats ? decode_floats : part_floats;
+    static_assert(floats * 4 <= 160 * 1024, "fits the CU's LDS");
+};
+
+template <int K, bool PAIRS>
+__global__ __launch_bounds__(MixedLds::threads) void axis1_swiglu_mixed_kernel(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes_g,
+    const float* __restrict__ scales_g, const float* __restrict__ lut_g,
+    const uint32_t* __restrict__ codes_u, const float* __restrict__ scales_u,
+    const float* __restrict__ lut_u, uint16_t* __restrict__ h, CodeLayout lay, int N, int nb,
+    int M) {
+    constexpr int MT = 2, KG = kDualGroups, kWaves = MixedLds::waves;
+    constexpr int kThreadsP = MixedLds::threads;
+    __shared__ __attribute__((aligned(16))) float lds[MixedLds::floats];
+    float* const tab = lds;
+
+    const int G = static_cast<int>(gridDim.x), wg = static_cast<int>(blockIdx.x);
+    const int r0 = static_cast<int>(static_cast<long>(wg) * N / G);
+    const int r1 = static_cast<int>(static_cast<long>(wg + 1) * N / G);
+    const int rm = r1 - r0;  // 1 <= rm <= kMixedRows (the launcher's grid)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, c = lane >> 4, cp = 3 - c;
+    const int gc = (2 * rm + 15) >> 4;
+    const int tasks = gc * nb;
+    const int tau0 = static_cast<int>(static_cast<long>(wave) * tasks / kWaves);
+    const int tau1 = static_cast<int>(static_cast<long>(wave + 1) * tasks / kWaves);
+    const long in = static_cast<long>(nb) * kT;
+
+    XSource<MT> xs;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int m = 16 * mt + 8 * hh + (lane >> 3);
+            xs.xrows[mt][hh] = x + (m < M ? m : M - 1) * in + 8 * (lane & 7);
+        }
+        const int m = 16 * mt + j;
+        xs.xa[mt] = x + (m < M ? m : M - 1) * in + 64 * c;
+    }
+    xs.slot = reinterpret_cast<u32x4*>(lds + MixedLds::tab_floats) + wave * MixedLds::slot_chunks;
+    xs.nb = nb;
+
+    TaskCtx cx{codes_g, lay, scales_g, nb, gc, r0, r1, j, cp, codes_u, scales_u, rm};
+    floatx4 acc[KG][MT];
+#pragma unroll
+    for (int g = 0; g < KG; ++g)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[g][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // Prologue: both codebooks, then the first two tasks' code words; the
+    // codebook stores wait only for their own data.
+    RepSrc<kThreadsP> src_g, src_u;  // 8 entries of each codebook per thread
+    fetch_rep<kThreadsP>(src_g, lut_g);
+    fetch_rep<kThreadsP>(src_u, lut_u);
+    asm volatile("" ::: "memory");
+    Task<K> ta, tb, tc;
+    load_task_opaque<K, PAIRS, true>(ta, cx, tau0, tau1 > 1 ? tau1 : 1);
+    load_task_opaque<K, PAIRS, true>(tb, cx, tau0 + 1, tau1 > 1 ? tau1 : 1);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < RepSrc<kThreadsP>::n; ++i) {
+        tab[tid + kThreadsP * i] = src_g.a[i];
+        tab[kLutEntries + tid + kThreadsP * i] = src_u.a[i];
+    }
+    __syncthreads();
+
+    XFrags<MT> xf, xn;
+    int xb = -1;
+    for (int t0 = tau0; t0 < tau1; t0 += 3) {
+        load_task<K, PAIRS, true>(tc, cx, t0 + 2, tau1);
+        run_task<K, MT, false, KG, true>(ta, xf, xn, xb, xs, acc, tab, lane, j, c);
+        load_task<K, PAIRS, true>(ta, cx, t0 + 3, tau1);
+        if (t0 + 1 < tau1) run_task<K, MT, false, KG, true>(tb, xf, xn, xb, xs, acc, tab, lane, j, c);
+        load_task<K, PAIRS, true>(tb, cx, t0 + 4, tau1);
+        if (t0 + 2 < tau1) run_task<K, MT, false, KG, true>(tc, xf, xn, xb, xs, acc, tab, lane, j, c);
+    }
+    __syncthreads();  // the tables and slots are dead from here on
+
+    // part[wave][group][m][j] as in the prefill epilogue; then the thread of
+    // output (16 mt + m, i) sums the waves' tiles of gate virtual row i and up
+    // virtual row rm + i and writes h.
+    float* const part = lds;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int g = 0; g < KG; ++g)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                part[((wave * KG + g) * 16 + 4 * c + v) * 16 + j] = acc[g][mt][v];
+        __syncthreads();
+        for (int o = tid; o < 16 * rm; o += kThreadsP) {
+            const int m = o / rm, i = o - m * rm;
+            const int u = rm + i;
+            const float* pg = part + ((i >> 4) * 16 + m) * 16 + (i & 15);
+            const float* pu = part + ((u >> 4) * 16 + m) * 16 + (u & 15);
+            float sg = 0.f, su = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                sg += pg[w * KG * 256];
+                su += pu[w * KG * 256];
+            }
+            if (16 * mt + m < M)
+                h[static_cast<size_t>(16 * mt + m) * N + r0 + i] = round_bf16(silu_f32(sg) * su);
+        }
+        __syncthreads();
     }
 }
 
@@ -656,6 +825,20 @@ hipError_t launch_axis1_swiglu(const uint16_t* x, int M, const uint32_t* codes_g
                                const float* scales_g, const float* lut_g, const uint32_t* codes_u,
                                const float* scales_u, const float* lut_u, uint16_t* h,
                                CodeLayout lay, int N, int nb, int k, hipStream_t st) {
+    // k = 3, 4 with two M tiles: mixed gate/up groups; at most kMixedRows rows
+    // of each projection per workgroup.
+    if (k != 2 && M > 16) {
+        int G = cu_count() < N ? cu_count() : N;
+        if ((N + G - 1) / G > kMixedRows) G = (N + kMixedRows - 1) / kMixedRows;
+        const bool rowmajor = lay.row_words == static_cast<uint64_t>(nb) * 8 * k;
+        if (k == 3)
+            return launch_kernel(rowmajor ? axis1_swiglu_mixed_kernel<3, false> : axis1_swiglu_mixed_kernel<3, true>,
+                                 dim3(G), dim3(MixedLds::threads), st, x, codes_g, scales_g, lut_g,
+                                 codes_u, scales_u, lut_u, h, lay, N, nb, M);
+        return launch_kernel(rowmajor ? axis1_swiglu_mixed_kernel<4, false> : axis1_swiglu_mixed_kernel<4, true>,
+                             dim3(G), dim3(MixedLds::threads), st, x, codes_g, scales_g, lut_g,
+                             codes_u, scales_u, lut_u, h, lay, N, nb, M);
+    }
     // M tiles and activation loads as for the single launch
     const int dmax = k == 2 ? kDirectMaxM : 16;
     const int shape = M > 16 ? 2 : M > dmax ? 1 : 0;

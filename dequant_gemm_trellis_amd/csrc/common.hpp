@@ -60,21 +60,37 @@ __device__ __forceinline__ void static_for(F&& f) {
 // ((bits >> O) & (2^WIDTH - 1)) << SHIFT, formed as one shift or funnel shift
 // plus one mask. O is a template constant, so every word index is known at
 // compile time and the array stays in registers.
+// field_raw: the same before the mask, i.e. the field at bits [SHIFT, SHIFT +
+// WIDTH) of the result with whatever bits surround it.
 template <int O, int WIDTH, int SHIFT, int N>
-__device__ __forceinline__ uint32_t field_offset(const uint32_t (&w)[N]) {
-    constexpr uint32_t mask = ((1u << WIDTH) - 1u) << SHIFT;
+__device__ __forceinline__ uint32_t field_raw(const uint32_t (&w)[N]) {
     if constexpr (O < SHIFT) {
         static_assert(O + WIDTH <= 32, "field must sit in word 0");
-        return (w[0] << (SHIFT - O)) & mask;
+        return w[0] << (SHIFT - O);
     } else {
         constexpr int s = O - SHIFT, wi = s >> 5, sh = s & 31;
         if constexpr (sh + WIDTH + SHIFT <= 32) {
-            return (w[wi] >> sh) & mask;
+            return w[wi] >> sh;
         } else {
             static_assert(wi + 1 < N, "field runs past the loaded words");
-            return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh) & mask;
+            return __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh);
         }
     }
+}
+
+template <int O, int WIDTH, int SHIFT, int N>
+__device__ __forceinline__ uint32_t field_offset(const uint32_t (&w)[N]) {
+    constexpr uint32_t mask = ((1u << WIDTH) - 1u) << SHIFT;
+    return field_raw<O, WIDTH, SHIFT>(w) & mask;
+}
+
+// (a & mask) | b in one VALU op (v_and_or_b32). Written out because the
+// compiler turns an OR of disjoint bits into an add and then re-associates it
+// with the LDS base, which costs a separate AND and ADD per gather.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(b));
+    return r;
 }
 
 // Byte offset into the LDS codebook (4-byte entries) of the 12-bit window
@@ -236,6 +252,24 @@ __device__ __forceinline__ Gathered<false> gather_run64_rep(const uint32_t (&w)[
         constexpr int q0 = 63 - 8 * S - 2 * d;
         g.v[d].x = lds_lut(tab, field_offset<q0 * K, kL, 5>(w) | cofs);
         g.v[d].y = lds_lut(tab, field_offset<(q0 - 1) * K, kL, 5>(w) | cofs);
+    });
+    return g;
+}
+
+// Gathers of fragment S from one of several plain codebooks laid out one after
+// another in LDS: `sel` is the byte offset of this lane's codebook (a multiple
+// of 16 KB), OR-ed into the window's offset as the copy offset is above.
+template <int K, int S>
+__device__ __forceinline__ Gathered<false> gather_run64_sel(const uint32_t (&w)[2 * K + 1],
+                                                            const float* __restrict__ tab,
+                                                            uint32_t sel) {
+    Gathered<false> g;
+    static_for<0, 4>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        constexpr int q0 = 63 - 8 * S - 2 * d;
+        constexpr uint32_t mask = (kLutEntries - 1u) << 2;
+        g.v[d].x = lds_lut(tab, and_or(field_raw<q0 * K, kL, 2>(w), mask, sel));
+        g.v[d].y = lds_lut(tab, and_or(field_raw<(q0 - 1) * K, kL, 2>(w), mask, sel));
     });
     return g;
 }

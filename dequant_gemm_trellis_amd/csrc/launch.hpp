@@ -88,8 +88,9 @@ hipError_t launch_axis1_dual(const uint16_t* x, int M, const uint32_t* codes_a,
                              hipStream_t st);
 
 // Gate and up over the same x[M][nb*256], 1 <= M <= 32, with the SwiGLU
-// epilogue, in one launch of the 16-row-group kernel (the grid of
-// launch_axis1, every workgroup decoding its rows of both projections):
+// epilogue, in one launch of a 16-row-group kernel, every workgroup decoding
+// its rows of both projections (k = 3, 4 at M > 16: side by side in shared
+// groups; otherwise gate, then up, on the grid of launch_axis1):
 // h[m][n] = bf16(silu(g[m][n]) * u[m][n]) from the float32 sums.
 hipError_t launch_axis1_swiglu(const uint16_t* x, int M, const uint32_t* codes_g,
                                const float* scales_g, const float* lut_g, const uint32_t* codes_u,

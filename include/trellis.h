@@ -230,10 +230,11 @@ int trellis_prefill_dual(const uint16_t *x, int32_t M, const uint32_t *codes_a,
  * MLP geometry (page 60 tiled-prefill.ts, its dispatch notes; page 60
  * wide-prefill.ts takes that model's normalised activations) but print no
  * activation function; SwiGLU is that MLP's, and the fused epilogue is this
- * library's. Each workgroup decodes a row range of the gate, restages its
- * codebook table from the up codebook and decodes the same rows of the up
- * projection, so both sums of an output meet in one workgroup: no workspace,
- * a fixed summation order (repeated calls give identical bits).
+ * library's. Each workgroup decodes the same row range of both projections
+ * (either the gate rows, then the up rows after restaging its codebook table,
+ * or, at k = 3, 4 with 17 <= M <= 32, gate and up rows side by side in shared
+ * 16-row groups), so both sums of an output meet in one workgroup: no
+ * workspace, a fixed summation order (repeated calls give identical bits).
  */
 int trellis_gate_up_swiglu(const uint16_t *x, int32_t M, const uint32_t *codes_g,
                            const float *scales_g, const float *lut_g, const uint32_t *codes_u,
