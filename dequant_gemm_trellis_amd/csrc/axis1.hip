@@ -98,6 +98,9 @@ struct TaskCtx {
     const uint32_t* codes_b;
     const float* scales_b;
     int rm;
+    // Folded last group (gf >= 1; see task_place): the number of full groups
+    // before it. -1: no folding.
+    int gf = -1;
 };
 
 template <int K>
@@ -106,8 +109,75 @@ struct Task {
     float scale;
     int b, g;      // block and row group: uniform across the wave
     bool valid;    // this lane's row lies in the workgroup's range
+    bool fold;     // a folded task (uniform)
     uint32_t sel;  // MIXED: byte offset of this lane's codebook in LDS
 };
+
+// Where task tc sits. Without folding, block-major: tc = b gc + g. Folding
+// serves a last group of at most 8 rows with one M tile of at most 8
+// activation rows: A and B then have 8 spare rows and columns, so a task can
+// hold that group's rows for two blocks side by side -- lanes j < 8 block b,
+// j >= 8 block b + 1, A rows 0-7 block b's activations, rows 8-15 block
+// b + 1's -- and the two diagonal 8x8 quarters of D are the two blocks'
+// partials (the other two quarters are ignored). Each pair of blocks (2P,
+// 2P + 1) runs the gf full groups of block 2P, the folded task, then the full
+// groups of block 2P + 1 (an odd last block: its full groups and a folded task
+// with an empty second half), so blocks still change one at a time and the
+// last group costs half a task per block instead of a whole one.
+//
+// A wave loads its tasks in order (tau0, tau0 + 1, ...; past its last task it
+// re-reads that one), so a cursor walks the sequence with compares: one
+// division when it is set, none per task.
+struct TaskCursor {
+    int tau;  // the task the next load reads
+    int b0;   // its block (no folding) or the pair's first block (folding)
+    int rem;  // its position within the block's gc or the pair's 2 gf + 1 tasks
+};
+
+template <bool FOLD>
+__device__ __forceinline__ TaskCursor task_cursor(const TaskCtx& cx, int tau0, int tau_end) {
+    const int tau = tau0 < tau_end ? tau0 : tau_end - 1;
+    const bool fold = FOLD && cx.gf >= 0;
+    const int per = fold ? 2 * cx.gf + 1 : cx.gc;
+    const int q = tau / per;
+    return {tau, fold ? 2 * q : q, tau - q * per};
+}
+
+// The cursor's task (block, group, folded?), then the cursor moves on unless
+// that was the last task before tau_end.
+template <bool FOLD>
+__device__ __forceinline__ void task_place(const TaskCtx& cx, TaskCursor& k, int tau_end, int& b,
+                                           int& g, bool& fold) {
+    const bool folding = FOLD && cx.gf >= 0;
+    if (!folding) {
+        b = k.b0;
+        g = k.rem;
+        fold = false;
+    } else {
+        fold = k.rem == cx.gf;
+        b = k.b0 + (k.rem > cx.gf ? 1 : 0);
+        g = k.rem < cx.gf ? k.rem : k.rem > cx.gf ? k.rem - cx.gf - 1 : cx.gf;
+    }
+    if (k.tau + 1 < tau_end) {
+        ++k.tau;
+        if (++k.rem == (folding ? 2 * cx.gf + 1 : cx.gc)) {
+            k.rem = 0;
+            k.b0 += folding ? 2 : 1;
+        }
+    }
+}
+
+// A folded task's lane: row r0 + 16 g + (j & 7) of block b + (j >> 3). Lanes
+// past the rows or past the last block re-read a valid row and block; their
+// scale is zeroed, since their D columns are added into stored rows.
+__device__ __forceinline__ void fold_lane(const TaskCtx& cx, int g, int b, int& rc, int& bl,
+                                          bool& valid) {
+    const int row = cx.r0 + 16 * g + (cx.j & 7);
+    const int blk = b + (cx.j >> 3);
+    valid = row < cx.r1 && blk < cx.nb;
+    rc = row < cx.r1 ? row : cx.r1 - 1;
+    bl = blk < cx.nb ? blk : cx.nb - 1;
+}
 
 // The stored row, code array and scales of lane row 16 g + j of a task, and
 // whether it is a real row (rows past the range re-read the last real one).
@@ -136,31 +206,34 @@ __device__ __forceinline__ uint64_t task_word(const TaskCtx& cx, int rc, int b) 
     else return (static_cast<size_t>(rc) * cx.nb + b) * Bits<K>::wpb;
 }
 
-// Load task tau's code words (2k per lane) and scale. Past the wave's last
-// task it re-reads that task: every load is unconditional, so the compiler's
-// memory-counter waits never have to cover a skipped load.
-template <int K, bool PAIRS, bool MIXED = false>
-__device__ __forceinline__ void load_task(Task<K>& t, const TaskCtx& cx, int tau, int tau_end) {
-    const int tc = tau < tau_end ? tau : tau_end - 1;
-    const int b = tc / cx.gc;
-    const int g = tc - b * cx.gc;
+// Load the cursor's task: its code words (2k per lane) and scale. Past the
+// wave's last task it re-reads that task: every load is unconditional, so the
+// compiler's memory-counter waits never have to cover a skipped load.
+template <int K, bool PAIRS, bool MIXED = false, bool FOLD = false>
+__device__ __forceinline__ void load_task(Task<K>& t, const TaskCtx& cx, TaskCursor& k, int tau_end) {
+    int b, g;
+    task_place<FOLD>(cx, k, tau_end, b, g, t.fold);
     bool second;
-    const int rc = task_row<MIXED>(cx, g, t.valid, second);
+    int rc = task_row<MIXED>(cx, g, t.valid, second);
+    int bl = b;
+    if (FOLD && t.fold) fold_lane(cx, g, b, rc, bl, t.valid);
     t.b = b;
     t.g = g;
     t.sel = second ? kLutEntries * 4 : 0;
     const uint32_t* codes = second ? cx.codes_b : cx.codes;
     const float* scales = second ? cx.scales_b : cx.scales;
-    load_run64_words<K>(codes + task_word<K, PAIRS>(cx, rc, b), cx.cp, t.w);
+    load_run64_words<K>(codes + task_word<K, PAIRS>(cx, rc, bl), cx.cp, t.w);
     t.scale = scales[rc];
+    if (FOLD && t.fold && !t.valid) t.scale = 0.f;
 }
 
 // load_task through opaque global-address-space pointers, for the prologue:
 // through the restrict kernel pointers the loads count as invariant and the
 // compiler sinks them past the table stores and the barrier to their first
 // use, so the table stores and the code words no longer overlap.
-template <int K, bool PAIRS, bool MIXED = false>
-__device__ __forceinline__ void load_task_opaque(Task<K>& t, const TaskCtx& cx, int tau, int tau_end) {
+template <int K, bool PAIRS, bool MIXED = false, bool FOLD = false>
+__device__ __forceinline__ void load_task_opaque(Task<K>& t, const TaskCtx& cx, TaskCursor& k,
+                                                 int tau_end) {
     using gu32 = const __attribute__((address_space(1))) uint32_t*;
     using gu32x4 = const __attribute__((address_space(1))) u32x4*;
     using gf32 = const __attribute__((address_space(1))) float*;
@@ -169,17 +242,18 @@ __device__ __forceinline__ void load_task_opaque(Task<K>& t, const TaskCtx& cx, 
     gu32 codes_b = (gu32)cx.codes_b;
     gf32 scales_b = (gf32)cx.scales_b;
     asm volatile("" : "+s"(codes_a), "+s"(scales_a), "+s"(codes_b), "+s"(scales_b));
-    const int tc = tau < tau_end ? tau : tau_end - 1;
-    const int b = tc / cx.gc;
-    const int g = tc - b * cx.gc;
+    int b, g;
+    task_place<FOLD>(cx, k, tau_end, b, g, t.fold);
     bool second;
-    const int rc = task_row<MIXED>(cx, g, t.valid, second);
+    int rc = task_row<MIXED>(cx, g, t.valid, second);
+    int bl = b;
+    if (FOLD && t.fold) fold_lane(cx, g, b, rc, bl, t.valid);
     t.b = b;
     t.g = g;
     t.sel = second ? kLutEntries * 4 : 0;
     const gu32 codes = second ? codes_b : codes_a;
     const gf32 scales = second ? scales_b : scales_a;
-    const gu32 p = codes + task_word<K, PAIRS>(cx, rc, b) + 2 * K * cx.cp;
+    const gu32 p = codes + task_word<K, PAIRS>(cx, rc, bl) + 2 * K * cx.cp;
     if constexpr (K == 2) {
         const u32x4 v = *reinterpret_cast<gu32x4>(p);
         t.w[0] = v.x; t.w[1] = v.y; t.w[2] = v.z; t.w[3] = v.w;
@@ -188,6 +262,7 @@ __device__ __forceinline__ void load_task_opaque(Task<K>& t, const TaskCtx& cx, 
         for (int i = 0; i < 2 * K; ++i) t.w[i] = p[i];
     }
     t.scale = scales[rc];
+    if (FOLD && t.fold && !t.valid) t.scale = 0.f;
 }
 
 template <int MT>
@@ -296,6 +371,21 @@ __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__
     }
 }
 
+// A folded task's A operand from the direct path's fragments: rows 0-7 stay
+// block b's (xf), rows 8-15 become block b + 1's, i.e. lane j >= 8 takes xn
+// of lane j - 8 (DPP row_shr:8 within each 16-lane row, written to banks 2
+// and 3 only, lanes 8-15). Done in place: the folded task is the last of its
+// block in every wave's sequence, and the next block change reloads xf.
+__device__ __forceinline__ void fold_frags(XFrags<1>& xf, const XFrags<1>& xn) {
+#pragma unroll
+    for (int S = 0; S < 8; ++S)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            xf.v[0][S][q] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+                static_cast<int>(xf.v[0][S][q]), static_cast<int>(xn.v[0][S][q]),
+                0x118 /* row_shr:8 */, 0xF, 0xC, false));
+}
+
 // Where a wave's activation fragments come from (see the two paths above).
 template <int MT>
 struct XSource {
@@ -314,7 +404,7 @@ struct XSource {
 // MIXED (staged activations, k = 3, 4): each lane reads the plain codebook of
 // its row's projection (Task::sel), and the activation slot holds all four
 // lines.
-template <int K, int MT, bool DIRECT, int KG, bool MIXED = false>
+template <int K, int MT, bool DIRECT, int KG, bool MIXED = false, bool FOLD = false>
 __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& xn, int& xb,
                                          const XSource<MT>& xs, floatx4 (&acc)[KG][MT],
                                          const float* __restrict__ tab, int lane, int j, int c) {
@@ -330,6 +420,10 @@ __device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& 
         } else {
             load_x_block<MT, kLines>(xf, xs.slot, xs.xrows, t.b, lane, j, c);
         }
+    }
+    if constexpr (FOLD) {
+        static_assert(DIRECT && MT == 1, "folding pairs two blocks' 8 rows in one M tile");
+        if (t.fold) fold_frags(xf, xn);
     }
     if (!t.valid) {
 #pragma unroll
@@ -393,7 +487,7 @@ __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)
 //   restages the table from the up codebook, runs the same tasks on the up
 //   projection (b operands) and writes y_a[m][n] = bf16(silu(g) * u), the same
 //   thread reducing the same output in both phases.
-template <int K, int MT, bool DIRECT, bool PAIRS, int KG, bool SWIGLU>
+template <int K, int MT, bool DIRECT, bool PAIRS, int KG, bool SWIGLU, bool FOLD>
 __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes_a,
     const float* __restrict__ scales_a, const float* __restrict__ lut_a,
@@ -418,7 +512,10 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, c = lane >> 4, cp = 3 - c;
     const int gc = (r1 - r0 + 15) >> 4;  // groups in this workgroup, <= KG
-    const int tasks = gc * nb;
+    // Folding (task_place): direct fragments, one M tile, M <= 8, a last group
+    // of at most 8 rows after at least one full group.
+    const bool fold = FOLD && M <= 8 && gc >= 2 && r1 - r0 - 16 * (gc - 1) <= 8;
+    const int tasks = fold ? (nb >> 1) * (2 * gc - 1) + (nb & 1) * gc : gc * nb;
     const int tau0 = static_cast<int>(static_cast<long>(wave) * tasks / kWaves);
     const int tau1 = static_cast<int>(static_cast<long>(wave + 1) * tasks / kWaves);
     const long in = static_cast<long>(nb) * kT;
@@ -442,7 +539,8 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     xs.slot = reinterpret_cast<u32x4*>(lds + Lds::tab_floats) + wave * Lds::slot_chunks;
     xs.nb = nb;
 
-    TaskCtx cx{codes, lay, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp, codes, scales, 0};
+    TaskCtx cx{codes, lay, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp, codes, scales, 0,
+               fold ? gc - 1 : -1};
     floatx4 acc[KG][MT];
 #pragma unroll
     for (int g = 0; g < KG; ++g)
@@ -457,8 +555,10 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     Lds::Table::fetch(tsrc, lut);
     asm volatile("" ::: "memory");
     Task<K> ta, tb, tc;
-    load_task_opaque<K, PAIRS>(ta, cx, tau0, tau1 > 1 ? tau1 : 1);
-    load_task_opaque<K, PAIRS>(tb, cx, tau0 + 1, tau1 > 1 ? tau1 : 1);
+    const int tend = tau1 > 1 ? tau1 : 1;  // a wave without tasks re-reads a valid one
+    TaskCursor cur = task_cursor<FOLD>(cx, tau0, tend);
+    load_task_opaque<K, PAIRS, false, FOLD>(ta, cx, cur, tend);
+    load_task_opaque<K, PAIRS, false, FOLD>(tb, cx, cur, tend);
     XFrags<MT> xn;
     if constexpr (DIRECT) load_x_frags_opaque<MT>(xn, xs.xa, ta.b);
     asm volatile("" ::: "memory");
@@ -472,12 +572,14 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     int xb = -1;  // block whose fragments xf holds
     auto run_tasks = [&]() {
         for (int t0 = tau0; t0 < tau1; t0 += 3) {
-            load_task<K, PAIRS>(tc, cx, t0 + 2, tau1);
-            run_task<K, MT, DIRECT, KG>(ta, xf, xn, xb, xs, acc, tab, lane, j, c);
-            load_task<K, PAIRS>(ta, cx, t0 + 3, tau1);
-            if (t0 + 1 < tau1) run_task<K, MT, DIRECT, KG>(tb, xf, xn, xb, xs, acc, tab, lane, j, c);
-            load_task<K, PAIRS>(tb, cx, t0 + 4, tau1);
-            if (t0 + 2 < tau1) run_task<K, MT, DIRECT, KG>(tc, xf, xn, xb, xs, acc, tab, lane, j, c);
+            load_task<K, PAIRS, false, FOLD>(tc, cx, cur, tend);
+            run_task<K, MT, DIRECT, KG, false, FOLD>(ta, xf, xn, xb, xs, acc, tab, lane, j, c);
+            load_task<K, PAIRS, false, FOLD>(ta, cx, cur, tend);
+            if (t0 + 1 < tau1)
+                run_task<K, MT, DIRECT, KG, false, FOLD>(tb, xf, xn, xb, xs, acc, tab, lane, j, c);
+            load_task<K, PAIRS, false, FOLD>(tb, cx, cur, tend);
+            if (t0 + 2 < tau1)
+                run_task<K, MT, DIRECT, KG, false, FOLD>(tc, xf, xn, xb, xs, acc, tab, lane, j, c);
         }
     };
     run_tasks();
@@ -485,7 +587,8 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
 
     // part[wave][group][m][j]: D[m = 4c + v][j] of each tile; untouched groups
     // add zeros. Output (16 mt + m, row) is reduced by thread idx % 512 in
-    // pass idx / 512, idx = (group * 16 + m) * 16 + j, the waves added in order.
+    // pass idx / 512, idx = (group * 16 + m) * 16 + j, the waves added in order
+    // (for a folded group, then the waves' second-block quarter).
     float* const part = lds;
     constexpr int kPasses = (KG * 256 + kThreadsP - 1) / kThreadsP;
     auto reduce = [&](auto&& sink) {
@@ -504,6 +607,10 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
                     const int g = idx >> 8, m = (idx >> 4) & 15, jj = idx & 15;
                     float s = 0.f;
                     for (int w = 0; w < kWaves; ++w) s += part[((w * KG + g) * 16 + m) * 16 + jj];
+                    // a folded group: block b + 1's quarter of D for the same row
+                    if (fold && g == gc - 1 && m < 8 && jj < 8)
+                        for (int w = 0; w < kWaves; ++w)
+                            s += part[((w * KG + g) * 16 + 8 + m) * 16 + 8 + jj];
                     sink(mt, it, 16 * mt + m, r0 + 16 * g + jj, s);
                 }
             }
@@ -519,8 +626,9 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
         typename Lds::Table::Src ts;
         Lds::Table::fetch(ts, lut_b);
         asm volatile("" ::: "memory");
-        load_task_opaque<K, PAIRS>(ta, cx, tau0, tau1 > 1 ? tau1 : 1);
-        load_task_opaque<K, PAIRS>(tb, cx, tau0 + 1, tau1 > 1 ? tau1 : 1);
+        cur = task_cursor<FOLD>(cx, tau0, tend);
+        load_task_opaque<K, PAIRS, false, FOLD>(ta, cx, cur, tend);
+        load_task_opaque<K, PAIRS, false, FOLD>(tb, cx, cur, tend);
         if constexpr (DIRECT) load_x_frags_opaque<MT>(xn, xs.xa, ta.b);
         asm volatile("" ::: "memory");
         Lds::Table::store(ts, tab);
@@ -619,8 +727,10 @@ __global__ __launch_bounds__(MixedLds::threads) void axis1_swiglu_mixed_kernel(
     fetch_rep<kThreadsP>(src_u, lut_u);
     asm volatile("" ::: "memory");
     Task<K> ta, tb, tc;
-    load_task_opaque<K, PAIRS, true>(ta, cx, tau0, tau1 > 1 ? tau1 : 1);
-    load_task_opaque<K, PAIRS, true>(tb, cx, tau0 + 1, tau1 > 1 ? tau1 : 1);
+    const int tend = tau1 > 1 ? tau1 : 1;
+    TaskCursor cur = task_cursor<false>(cx, tau0, tend);
+    load_task_opaque<K, PAIRS, true>(ta, cx, cur, tend);
+    load_task_opaque<K, PAIRS, true>(tb, cx, cur, tend);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < RepSrc<kThreadsP>::n; ++i) {
@@ -632,11 +742,11 @@ __global__ __launch_bounds__(MixedLds::threads) void axis1_swiglu_mixed_kernel(
     XFrags<MT> xf, xn;
     int xb = -1;
     for (int t0 = tau0; t0 < tau1; t0 += 3) {
-        load_task<K, PAIRS, true>(tc, cx, t0 + 2, tau1);
+        load_task<K, PAIRS, true>(tc, cx, cur, tend);
         run_task<K, MT, false, KG, true>(ta, xf, xn, xb, xs, acc, tab, lane, j, c);
-        load_task<K, PAIRS, true>(ta, cx, t0 + 3, tau1);
+        load_task<K, PAIRS, true>(ta, cx, cur, tend);
         if (t0 + 1 < tau1) run_task<K, MT, false, KG, true>(tb, xf, xn, xb, xs, acc, tab, lane, j, c);
-        load_task<K, PAIRS, true>(tb, cx, t0 + 4, tau1);
+        load_task<K, PAIRS, true>(tb, cx, cur, tend);
         if (t0 + 2 < tau1) run_task<K, MT, false, KG, true>(tc, xf, xn, xb, xs, acc, tab, lane, j, c);
     }
     __syncthreads();  // the tables and slots are dead from here on
@@ -705,20 +815,48 @@ int axis1_grid(int N) {
     return G;
 }
 
+// Whether a workgroup of G over N rows ends in a group of at most 8 rows after
+// a full one, where folding pays (the row counts differ by at most one).
+bool fold_pays(int N, int G) {
+    for (int rows = N / G; rows <= (N + G - 1) / G; ++rows) {
+        const int gc = (rows + 15) >> 4;
+        if (gc >= 2 && rows - 16 * (gc - 1) <= 8) return true;
+    }
+    return false;
+}
+
+// One launch of the 16-row-group kernel: the folding variant when asked for
+// (one M tile of directly loaded activations, M <= 8), row-major or
+// block-interleaved codes.
+template <int K, int MT, bool DIRECT, int KG, bool SWIGLU>
+hipError_t launch_prefill(bool fold, int G, int G0, hipStream_t st, const uint16_t* x,
+                          const uint32_t* codes_a, const float* scales_a, const float* lut_a,
+                          uint16_t* y_a, const uint32_t* codes_b, const float* scales_b,
+                          const float* lut_b, uint16_t* y_b, CodeLayout lay, int N, int nb, int M) {
+    auto go = [&](auto kernel) {
+        return launch_kernel(kernel, dim3(G), dim3(PrefillShape<MT>::threads), st, x, codes_a,
+                             scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, G0, lay, N, nb, M);
+    };
+    // Row-major iff a row's blocks are contiguous (with two blocks per row the
+    // two layouts coincide).
+    const bool rowmajor = lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb;
+    if constexpr (DIRECT && MT == 1) {
+        if (fold && M <= 8)
+            return rowmajor ? go(axis1_prefill_kernel<K, MT, DIRECT, false, KG, SWIGLU, true>)
+                            : go(axis1_prefill_kernel<K, MT, DIRECT, true, KG, SWIGLU, true>);
+    }
+    return rowmajor ? go(axis1_prefill_kernel<K, MT, DIRECT, false, KG, SWIGLU, false>)
+                    : go(axis1_prefill_kernel<K, MT, DIRECT, true, KG, SWIGLU, false>);
+}
+
 template <int K, int MT, bool DIRECT>
 hipError_t launch_axis1_k(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                           const float* scales, const float* lut, uint16_t* y, int N, int nb,
                           hipStream_t st) {
     const int G = axis1_grid(N);
-    // Row-major iff a row's blocks are contiguous (with two blocks per row the
-    // two layouts coincide).
-    if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
-        return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, false, kGroups, false>, dim3(G),
-                             dim3(PrefillShape<MT>::threads), st, x, codes, scales, lut, y, codes,
-                             scales, lut, y, G, lay, N, nb, M);
-    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, true, kGroups, false>, dim3(G),
-                         dim3(PrefillShape<MT>::threads), st, x, codes, scales, lut, y, codes,
-                         scales, lut, y, G, lay, N, nb, M);
+    return launch_prefill<K, MT, DIRECT, kGroups, false>(fold_pays(N, G), G, G, st, x, codes,
+                                                         scales, lut, y, codes, scales, lut, y,
+                                                         lay, N, nb, M);
 }
 
 // Gate and up with the SwiGLU epilogue: the single launch's grid, every
@@ -730,13 +868,9 @@ hipError_t launch_axis1_swiglu_k(const uint16_t* x, int M, const uint32_t* codes
                                  const float* lut_u, uint16_t* h, CodeLayout lay, int N, int nb,
                                  hipStream_t st) {
     const int G = axis1_grid(N);
-    if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
-        return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, false, kGroups, true>, dim3(G),
-                             dim3(PrefillShape<MT>::threads), st, x, codes_g, scales_g, lut_g, h,
-                             codes_u, scales_u, lut_u, h, G, lay, N, nb, M);
-    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, true, kGroups, true>, dim3(G),
-                         dim3(PrefillShape<MT>::threads), st, x, codes_g, scales_g, lut_g, h,
-                         codes_u, scales_u, lut_u, h, G, lay, N, nb, M);
+    return launch_prefill<K, MT, DIRECT, kGroups, true>(fold_pays(N, G), G, G, st, x, codes_g,
+                                                        scales_g, lut_g, h, codes_u, scales_u,
+                                                        lut_u, h, lay, N, nb, M);
 }
 
 // Workgroups per projection of the two-projection launch: half the compute
@@ -755,13 +889,9 @@ hipError_t launch_axis1_dual_k(const uint16_t* x, int M, const uint32_t* codes_a
                                hipStream_t st) {
     const int G0 = axis1_dual_groups(N);
     if ((N + G0 - 1) / G0 > 16 * kDualGroups) return hipErrorInvalidValue;  // checked by the caller
-    if (lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb)
-        return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, false, kDualGroups, false>, dim3(2 * G0),
-                             dim3(PrefillShape<MT>::threads), st, x, codes_a, scales_a, lut_a, y_a,
-                             codes_b, scales_b, lut_b, y_b, G0, lay, N, nb, M);
-    return launch_kernel(axis1_prefill_kernel<K, MT, DIRECT, true, kDualGroups, false>, dim3(2 * G0),
-                         dim3(PrefillShape<MT>::threads), st, x, codes_a, scales_a, lut_a, y_a,
-                         codes_b, scales_b, lut_b, y_b, G0, lay, N, nb, M);
+    return launch_prefill<K, MT, DIRECT, kDualGroups, false>(fold_pays(N, G0), 2 * G0, G0, st, x,
+                                                             codes_a, scales_a, lut_a, y_a, codes_b,
+                                                             scales_b, lut_b, y_b, lay, N, nb, M);
 }
 
 template <int K>

@@ -306,6 +306,50 @@ def test_rows_kernel_ragged(gpu_lib, N, M, k):
     assert gate(y, oracle_y(p)) <= TOL
 
 
+# ------------------------------------- axis 1, folded last group (M <= 8)
+FOLD_CASES = [(768, 5000, 2, 5, 0),    # 19-20 rows per workgroup: 3-4 rows folded; 3 blocks
+              (1024, 5000, 3, 8, 0),   # 4 blocks
+              (2048, 4500, 4, 7, 2),   # 17-18 rows: 1-2 rows folded; interleaved codes
+              (1280, 17000, 2, 6, 0),  # 66-67 rows: four full groups and 2-3 rows; 5 blocks
+              (256, 4400, 3, 8, 0),    # one block: the folded task's second half is empty
+              (512, 6000, 4, 5, 2),    # 23-24 rows: 7-8 rows folded
+              (768, 6200, 2, 8, 0)]    # 24-25 rows: a last group of 8 rows folds, of 9 does not
+
+
+@pytest.mark.parametrize("i,o,k,M,il", FOLD_CASES)
+def test_prefill_folded_last_group(gpu_lib, i, o, k, M, il):
+    """With directly loaded activations and M <= 8, a last 16-row group of at
+    most 8 rows decodes two blocks per task (A and B each hold two blocks'
+    8 rows): odd and even block counts, one block, 1 to 8 folded rows, and
+    workgroups on both sides of the 8-row limit."""
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, k, i, o, il)
+    p = synth.make_problem(shape, M, CFG["test"], proj=1700 + M + k)
+    say(f"prefill folded in={i} out={o} k={k} M={M} interleave={il}")
+    y = bf16_to_f64(run(T, Dev(p, T)))
+    assert gate(y, oracle_y(p)) <= TOL
+
+
+@pytest.mark.parametrize("i,o,k,M", [(768, 5000, 2, 6), (256, 4400, 3, 8), (1280, 17000, 4, 5)])
+def test_prefill_folded_integer_codebook_bit_exact(gpu_lib, i, o, k, M):
+    """The folded group with an integer codebook and integer activations: both
+    blocks' quarters of every tile are exact, so each output is the unique
+    bf16 of the exact sum; a lane past the last block must add zero."""
+    T = gpu_lib
+    shape = synth.Shape(1, 256, L, k, i, o)
+    g = np.random.default_rng(90 + M + k)
+    p0 = synth.make_problem(shape, M, CFG["test"], proj=1750 + M)
+    xi = g.integers(-3, 4, (M, shape.in_features)).astype(np.float32)
+    p = synth.Problem(shape, M, p0.codes, synth.integer_lut(),
+                      g.choice(np.array([0.5, 1.0, 2.0], np.float32), shape.rows),
+                      synth.to_bf16_bits(xi))
+    say(f"prefill folded integer codebook in={i} out={o} k={k} M={M}")
+    y = bf16_bits(run(T, Dev(p, T)))
+    exact = oracle_y(p)
+    assert np.all(np.abs(exact) < 2**24)
+    assert np.array_equal(y, synth.to_bf16_bits(exact.astype(np.float32)))
+
+
 @pytest.mark.parametrize("i", [256, 512])
 @pytest.mark.parametrize("M", [3, 7])
 def test_rows_kernel_one_or_two_blocks_per_row(gpu_lib, i, M):
@@ -667,11 +711,12 @@ def prefill_dual_case(T, shape, M, proj):
                                         (256, 1, 2, 7, 0), (512, 300, 3, 3, 0),
                                         (1024, 4111, 2, 2, 0), (512, 300, 4, 20, 0),
                                         (1024, 1000, 2, 32, 0), (2048, 4111, 3, 17, 2),
-                                        (768, 300, 2, 1, 0)])
+                                        (768, 300, 2, 1, 0), (1024, 5000, 2, 8, 0),
+                                        (1024, 4800, 3, 5, 2)])
 def test_prefill_dual_small(gpu_lib, i, o, k, M, il):
     """One shared launch for 2..32 rows (direct and staged activations, one
-    and two M tiles, ragged and single-row groups, interleaved codes); the
-    dual GEMV at one row."""
+    and two M tiles, ragged and single-row groups, interleaved codes, a folded
+    last group at 5000 and 4800 rows); the dual GEMV at one row."""
     T = gpu_lib
     say(f"prefill_dual in={i} out={o} k={k} M={M} interleave={il}")
     pa, pb, ya, yb = prefill_dual_case(T, synth.Shape(1, 256, L, k, i, o, il), M, 1300 + M + k)

@@ -74,7 +74,8 @@ def test_swiglu_small(gpu_lib, M, k):
                                         (32768, 40, 4, 1, 0), (256, 21000, 3, 6, 0),
                                         (512, 16, 3, 20, 2), (256, 21000, 4, 24, 0),
                                         (1024, 1, 3, 32, 0), (2048, 4111, 4, 17, 2),
-                                        (768, 37, 4, 31, 0), (4096, 18500, 3, 32, 2)])
+                                        (768, 37, 4, 31, 0), (4096, 18500, 3, 32, 2),
+                                        (768, 5000, 2, 5, 0), (1024, 5000, 4, 8, 2)])
 def test_swiglu_shapes(gpu_lib, i, o, k, M, il):
     """Ragged row counts, one row, one block per row, block interleave 2, rows
     longer than the GEMV stages (12288 inputs at k = 2, 32768 at k = 4: the
@@ -82,7 +83,8 @@ def test_swiglu_shapes(gpu_lib, i, o, k, M, il):
     persistent round holds (21000). At k = 3, 4 and M > 16 gate and up rows
     share 16-row groups: one row of each per workgroup (16, 1 rows), an odd
     count per workgroup (37, 4111), and more workgroups than compute units
-    (21000 and 18500 rows, more than 72 per compute unit)."""
+    (21000 and 18500 rows, more than 72 per compute unit). At 5000 rows and
+    M <= 8 the last group of each workgroup is folded (two blocks per task)."""
     T = gpu_lib
     shape = synth.Shape(1, 256, L, k, i, o, il)
     pg, pu = problems(shape, M, CFG["test"], 1100 + i % 97 + o % 89)
