@@ -64,7 +64,7 @@ REPS = 5
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_qwen_up_k2.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "dequant_gemm_trellis_amd", "csrc", f)
                   for f in ("gemv.hip", "common.hpp")]
-HEADLINE_KERNEL = "gemv_kernel<2, false, false>"
+HEADLINE_KERNEL = "gemv_kernel<2, false, false, false>"
 METRIC = "µs/call and effective HBM GB/s, trellis GEMV 5120→17408 k=2/3/4, M=1"
 # probe table kind whose gather rate bounds a kernel's decode: the k = 2 pair
 # table, or the eight bank-partitioned codebook copies for k = 3, 4
