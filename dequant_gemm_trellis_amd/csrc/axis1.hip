@@ -371,20 +371,12 @@ __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__
     }
 }
 
-// A folded task's A operand from the direct path's fragments: rows 0-7 stay
-// block b's (xf), rows 8-15 become block b + 1's, i.e. lane j >= 8 takes xn
-// of lane j - 8 (DPP row_shr:8 within each 16-lane row, written to banks 2
-// and 3 only, lanes 8-15). Done in place: the folded task is the last of its
-// block in every wave's sequence, and the next block change reloads xf.
-__device__ __forceinline__ void fold_frags(XFrags<1>& xf, const XFrags<1>& xn) {
-#pragma unroll
-    for (int S = 0; S < 8; ++S)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            xf.v[0][S][q] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-                static_cast<int>(xf.v[0][S][q]), static_cast<int>(xn.v[0][S][q]),
-                0x118 /* row_shr:8 */, 0xF, 0xC, false));
-}
+// Which blocks a wave's fragment sets hold: xf block b, xn block lb (direct
+// path).
+struct XCursor {
+    int b = -1;
+    int lb = -1;
+};
 
 // Where a wave's activation fragments come from (see the two paths above).
 template <int MT>
@@ -393,37 +385,69 @@ struct XSource {
     const uint16_t* xa[MT];        // direct: A-layout row pointers
     u32x4* slot;                   // staged: this wave's LDS slot
     int nb;
+    bool hi;                       // folding kernel, lanes j >= 8 (see lane_block)
 };
+
+// The block whose activations a lane's direct fragments for block b hold. In
+// the folding kernel lanes j >= 8 (A rows 8-15) hold rows 0-7 of block b + 1
+// (of b itself at the last block), so a folded task multiplies the fragments
+// as they are; every other task leaves D rows 8-15 unused (M <= 8).
+template <int MT>
+__device__ __forceinline__ int lane_block(const XSource<MT>& xs, int b) {
+    return b + (xs.hi && b + 1 < xs.nb ? 1 : 0);
+}
 
 // One task: eight fragments, the gathers of the next two in flight while one is
 // packed and multiplied against the MT activation tiles. A new block first
-// refreshes the activation fragments: on the direct path from xn, loaded one
-// block change earlier (or in the prologue), which then fetches the next
-// block's; on the staged path through the LDS slot, the one memory wait that
-// covers the prefetched code words.
+// refreshes the activation fragments. Direct path: xf takes xn; xn is fetched
+// one task ahead, by the task before one that enters a new block (tn is the
+// wave's next task), so the loads have a whole task to arrive. (Fetching the
+// next block at the block change itself, the compiler issued the loads ahead
+// of the move into temporaries and copied those into xn at once, i.e. waited
+// for the loads it had just issued: 6-10% of the kernel.) A block a wave enters
+// unannounced (its first) is fetched at once. Staged path: through the LDS
+// slot, the one memory wait that covers the prefetched code words.
 // MIXED (staged activations, k = 3, 4): each lane reads the plain codebook of
 // its row's projection (Task::sel), and the activation slot holds all four
 // lines.
 template <int K, int MT, bool DIRECT, int KG, bool MIXED = false, bool FOLD = false>
-__device__ __forceinline__ void run_task(Task<K> t, XFrags<MT>& xf, XFrags<MT>& xn, int& xb,
+__device__ __forceinline__ void run_task(Task<K> t, const Task<K>& tn, XFrags<MT>& xf,
+                                         XFrags<MT>& xn, XCursor& xc,
                                          const XSource<MT>& xs, floatx4 (&acc)[KG][MT],
                                          const float* __restrict__ tab, int lane, int j, int c) {
     static_assert(!MIXED || (K != 2 && !DIRECT), "mixed groups read two plain codebooks");
     constexpr bool P = PrefillLds<K, MT, DIRECT>::pair;
     constexpr bool REP = PrefillLds<K, MT, DIRECT>::rep;
     constexpr int kLines = MIXED ? 4 : PrefillLds<K, MT, DIRECT>::lines;
-    if (t.b != xb) {
-        xb = t.b;
+    // (Distinct empty asm statements open and close each fetch, so that the
+    // compiler neither hoists its loads above the branch nor merges fetches
+    // into one through a selected address.)
+    if (t.b != xc.b) {
         if constexpr (DIRECT) {
-            xf = xn;
-            load_x_frags<MT>(xn, xs.xa, t.b + 1 < xs.nb ? t.b + 1 : xs.nb - 1);
+            if (xc.lb == t.b) {
+                xf = xn;
+            } else {
+                asm volatile("; x fetch now");
+                load_x_frags<MT>(xf, xs.xa, lane_block(xs, t.b));
+                // wait here, on this path only: after the branches the
+                // compiler's wait for xf would also cover a fetch ahead
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int S = 0; S < 8; ++S) asm volatile("; x fetch now done" : : "v"(xf.v[mt][S]));
+            }
         } else {
             load_x_block<MT, kLines>(xf, xs.slot, xs.xrows, t.b, lane, j, c);
         }
+        xc.b = t.b;
     }
-    if constexpr (FOLD) {
-        static_assert(DIRECT && MT == 1, "folding pairs two blocks' 8 rows in one M tile");
-        if (t.fold) fold_frags(xf, xn);
+    if constexpr (DIRECT) {
+        if (tn.b != t.b && tn.b != xc.lb) {
+            asm volatile("; x fetch ahead");
+            load_x_frags<MT>(xn, xs.xa, lane_block(xs, tn.b));
+            asm volatile("; x fetch ahead done");
+            xc.lb = tn.b;
+        }
     }
     if (!t.valid) {
 #pragma unroll
@@ -533,11 +557,13 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
             const int m = 16 * mt + 8 * h + (lane >> 3);
             xs.xrows[mt][h] = x + (m < M ? m : M - 1) * in + 8 * (lane & 7);
         }
-        const int m = 16 * mt + j;
+        // (folding kernel: row j & 7 in both halves of A, see lane_block)
+        const int m = FOLD ? (j & 7) : 16 * mt + j;
         xs.xa[mt] = x + (m < M ? m : M - 1) * in + 64 * c;
     }
     xs.slot = reinterpret_cast<u32x4*>(lds + Lds::tab_floats) + wave * Lds::slot_chunks;
     xs.nb = nb;
+    xs.hi = FOLD && j >= 8;
 
     TaskCtx cx{codes, lay, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp, codes, scales, 0,
                fold ? gc - 1 : -1};
@@ -560,7 +586,7 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     load_task_opaque<K, PAIRS, false, FOLD>(ta, cx, cur, tend);
     load_task_opaque<K, PAIRS, false, FOLD>(tb, cx, cur, tend);
     XFrags<MT> xn;
-    if constexpr (DIRECT) load_x_frags_opaque<MT>(xn, xs.xa, ta.b);
+    if constexpr (DIRECT) load_x_frags_opaque<MT>(xn, xs.xa, lane_block(xs, ta.b));
     asm volatile("" ::: "memory");
     Lds::Table::store(tsrc, tab);
     __syncthreads();
@@ -569,17 +595,18 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     // flight while one is decoded. (No branch around the loop: the prologue's
     // loads would be sunk into it, behind the barrier.)
     XFrags<MT> xf;
-    int xb = -1;  // block whose fragments xf holds
+    XCursor xc;
+    xc.lb = ta.b;  // the prologue's fetch
     auto run_tasks = [&]() {
         for (int t0 = tau0; t0 < tau1; t0 += 3) {
             load_task<K, PAIRS, false, FOLD>(tc, cx, cur, tend);
-            run_task<K, MT, DIRECT, KG, false, FOLD>(ta, xf, xn, xb, xs, acc, tab, lane, j, c);
+            run_task<K, MT, DIRECT, KG, false, FOLD>(ta, tb, xf, xn, xc, xs, acc, tab, lane, j, c);
             load_task<K, PAIRS, false, FOLD>(ta, cx, cur, tend);
             if (t0 + 1 < tau1)
-                run_task<K, MT, DIRECT, KG, false, FOLD>(tb, xf, xn, xb, xs, acc, tab, lane, j, c);
+                run_task<K, MT, DIRECT, KG, false, FOLD>(tb, tc, xf, xn, xc, xs, acc, tab, lane, j, c);
             load_task<K, PAIRS, false, FOLD>(tb, cx, cur, tend);
             if (t0 + 2 < tau1)
-                run_task<K, MT, DIRECT, KG, false, FOLD>(tc, xf, xn, xb, xs, acc, tab, lane, j, c);
+                run_task<K, MT, DIRECT, KG, false, FOLD>(tc, ta, xf, xn, xc, xs, acc, tab, lane, j, c);
         }
     };
     run_tasks();
@@ -629,14 +656,15 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
         cur = task_cursor<FOLD>(cx, tau0, tend);
         load_task_opaque<K, PAIRS, false, FOLD>(ta, cx, cur, tend);
         load_task_opaque<K, PAIRS, false, FOLD>(tb, cx, cur, tend);
-        if constexpr (DIRECT) load_x_frags_opaque<MT>(xn, xs.xa, ta.b);
+        if constexpr (DIRECT) load_x_frags_opaque<MT>(xn, xs.xa, lane_block(xs, ta.b));
         asm volatile("" ::: "memory");
         Lds::Table::store(ts, tab);
 #pragma unroll
         for (int g = 0; g < KG; ++g)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[g][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        xb = -1;
+        xc = XCursor{};
+        xc.lb = ta.b;
         __syncthreads();
         run_tasks();
         __syncthreads();
@@ -712,6 +740,7 @@ __global__ __launch_bounds__(MixedLds::threads) void axis1_swiglu_mixed_kernel(
     }
     xs.slot = reinterpret_cast<u32x4*>(lds + MixedLds::tab_floats) + wave * MixedLds::slot_chunks;
     xs.nb = nb;
+    xs.hi = false;
 
     TaskCtx cx{codes_g, lay, scales_g, nb, gc, r0, r1, j, cp, codes_u, scales_u, rm};
     floatx4 acc[KG][MT];
@@ -740,14 +769,14 @@ __global__ __launch_bounds__(MixedLds::threads) void axis1_swiglu_mixed_kernel(
     __syncthreads();
 
     XFrags<MT> xf, xn;
-    int xb = -1;
+    XCursor xc;
     for (int t0 = tau0; t0 < tau1; t0 += 3) {
         load_task<K, PAIRS, true>(tc, cx, cur, tend);
-        run_task<K, MT, false, KG, true>(ta, xf, xn, xb, xs, acc, tab, lane, j, c);
+        run_task<K, MT, false, KG, true>(ta, tb, xf, xn, xc, xs, acc, tab, lane, j, c);
         load_task<K, PAIRS, true>(ta, cx, cur, tend);
-        if (t0 + 1 < tau1) run_task<K, MT, false, KG, true>(tb, xf, xn, xb, xs, acc, tab, lane, j, c);
+        if (t0 + 1 < tau1) run_task<K, MT, false, KG, true>(tb, tc, xf, xn, xc, xs, acc, tab, lane, j, c);
         load_task<K, PAIRS, true>(tb, cx, cur, tend);
-        if (t0 + 2 < tau1) run_task<K, MT, false, KG, true>(tc, xf, xn, xb, xs, acc, tab, lane, j, c);
+        if (t0 + 2 < tau1) run_task<K, MT, false, KG, true>(tc, ta, xf, xn, xc, xs, acc, tab, lane, j, c);
     }
     __syncthreads();  // the tables and slots are dead from here on
 

@@ -461,8 +461,7 @@ __device__ __forceinline__ void load_xa_opaque(XFrag& xn, const uint16_t* xa, ui
 template <int K, bool REP, bool STRAD>
 __device__ __forceinline__ void run_rows_step(Step<K> st, const XFrag& xf, const XFrag& xn,
                                               uint32_t blo, const float* __restrict__ tab,
-                                              float* __restrict__ part, int u, int u_end, int c,
-                                              int m4) {
+                                              float* __restrict__ part, int u, int u_end, int c) {
     constexpr bool P = RowsLds<K, REP>::pair;
     constexpr int D = GemvLds<K>::depth;
     st.w[2 * K] = next_run_word(st.w[0]);
@@ -484,7 +483,8 @@ __device__ __forceinline__ void run_rows_step(Step<K> st, const XFrag& xf, const
     if constexpr (STRAD) {
         if (st.b != blo) d1 = d2;
     }
-    if (4 * c < m4 && u < u_end) *reinterpret_cast<floatx4*>(part + u * m4 + 4 * c) = d1;
+    // D rows 4c + v: only c = 0 holds activation rows (M <= kGemvRowsMaxM = 4)
+    if (c == 0 && u < u_end) *reinterpret_cast<floatx4*>(part + u * 4) = d1;
 }
 
 template <int K, bool PAIRS, bool REP>
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, c = lane >> 4;
-    const int m4 = M > 4 ? 8 : 4;
+    constexpr int m4 = 4;  // partial floats per unit (M <= kGemvRowsMaxM = 4)
     // Balanced row chunks whose unit partials fit; chunk q is rows
     // [r0 + q rows / n, r0 + (q + 1) rows / n). The launcher guarantees at
     // least 16 rows per chunk (rows_chunks).
@@ -568,11 +568,11 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(
             // and waits for all of them at it); k = 2: the branch.
             if constexpr (K != 2) {
                 (void)strad;
-                run_rows_step<K, REP, true>(st, xf, xn, blo, tab, part, u0 + j, ue, c, m4);
+                run_rows_step<K, REP, true>(st, xf, xn, blo, tab, part, u0 + j, ue, c);
             } else if (strad) {
-                run_rows_step<K, REP, true>(st, xf, xn, blo, tab, part, u0 + j, ue, c, m4);
+                run_rows_step<K, REP, true>(st, xf, xn, blo, tab, part, u0 + j, ue, c);
             } else {
-                run_rows_step<K, REP, false>(st, xf, xn, blo, tab, part, u0 + j, ue, c, m4);
+                run_rows_step<K, REP, false>(st, xf, xn, blo, tab, part, u0 + j, ue, c);
             }
         };
         // Three register sets rotate as in gemv_kernel; every load is
@@ -629,8 +629,7 @@ hipError_t launch_gemv_rows_kr(const uint16_t* x, int M, const uint32_t* codes, 
 // Every workgroup's partials fit in one chunk beside a RowsLds<K, REP> table.
 template <int K, bool REP>
 bool rows_one_chunk(int M, int N, int nb) {
-    const int m4 = M > 4 ? 8 : 4;
-    const int max_rows = RowsLds<K, REP>::part_floats / (m4 * nb);
+    const int max_rows = RowsLds<K, REP>::part_floats / (4 * nb);
     const int G = rows_grid(N);
     // workgroups own floor(N / G) or ceil(N / G) rows
     return rows_chunks(N / G, max_rows) == 1 && rows_chunks((N + G - 1) / G, max_rows) == 1;
@@ -707,17 +706,8 @@ hipError_t launch_gemv_swiglu(const uint16_t* x, const uint32_t* codes_g, const 
 
 bool gemv_rows_supported(int M, int N, int nb, int k) {
     if (M < 1 || M > kGemvRowsMaxM || N < 16 || nb < 1) return false;
-    // Beyond 4 rows the 16-row-group kernel measured faster: at k = 2 only
-    // about 49 rows' partials of 8 floats fit beside the 128 KB pair table at
-    // 5120 inputs, and the second chunk (pipeline restart, a second epilogue,
-    // a block edge every other step) was 14-21% slower; at k = 3, 4 the
-    // 16-row-group kernel with directly loaded activations reads the
-    // codebook copies and was 0.5-4% faster than this kernel on one codebook
-    // (M = 5, 8).
-    if (M > 4) return false;
-    const int m4 = M > 4 ? 8 : 4;
     const int max_rows =
-        (k == 2 ? RowsLds<2, false>::part_floats : RowsLds<4, false>::part_floats) / (m4 * nb);
+        (k == 2 ? RowsLds<2, false>::part_floats : RowsLds<4, false>::part_floats) / (4 * nb);
     const int G = rows_grid(N);
     // workgroups own floor(N / G) or ceil(N / G) rows
     return rows_chunks(N / G, max_rows) > 0 && rows_chunks((N + G - 1) / G, max_rows) > 0;

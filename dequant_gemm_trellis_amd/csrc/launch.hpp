@@ -62,9 +62,14 @@ hipError_t launch_gemv_swiglu(const uint16_t* x, const uint32_t* codes_g, const 
 
 // Axis 1, 1 <= M <= kGemvRowsMaxM, in the GEMV's unit mapping (one workgroup
 // per compute unit, at least 16 rows each); gemv_rows_supported says whether
-// the geometry fits it (at least 16 rows, 16 rows' unit partials fit in LDS)
-// and it measured faster than launch_axis1 there (up to M = 4).
-constexpr int kGemvRowsMaxM = 8;
+// the geometry fits it (at least 16 rows, 16 rows' unit partials fit in LDS).
+// Beyond 4 rows the 16-row-group kernel measured faster: at k = 2 only about
+// 49 rows' partials of 8 floats fit beside the 128 KB pair table at 5120
+// inputs, and a second chunk (pipeline restart, a second epilogue, a block
+// edge every other step) was 14-21% slower; at k = 3, 4 the 16-row-group
+// kernel with directly loaded activations reads the codebook copies and was
+// 0.5-4% faster than this kernel on one codebook (M = 5, 8).
+constexpr int kGemvRowsMaxM = 4;
 bool gemv_rows_supported(int M, int N, int nb, int k);
 hipError_t launch_gemv_rows(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                             const float* scales, const float* lut, uint16_t* y, int N, int nb,
