@@ -33,18 +33,16 @@
 // reusing the table's space. Lanes of rows past the workgroup's range decode
 // all-zero words, so their gathers all hit one LDS address.
 //
-// Activation fragments reach the lanes one of two ways, chosen by M and k:
-//   - direct (M <= kDirectMaxM at k = 2, one M tile at k = 3, 4): each lane
-//     loads its own fragments from global memory in A layout, one block
-//     ahead of use. Lanes of rows m >= M read row M - 1, so an instruction
-//     touches only M x 4 distinct cache lines, and nothing goes through the
-//     LDS, which the codebook gathers keep busy. At k = 3, 4 this path also
-//     leaves room for the bank-partitioned codebook copies;
-//   - staged (larger M): coalesced loads of 16 rows, transposed through a
-//     per-wave LDS slot when the block changes. With the single table,
-//     direct loads of 16 rows (64 lines per instruction) measured slower;
-//     at k = 3, 4 the copies they make room for more than make up for it
-//     (M = 16: 0.4-1.6% faster).
+// Activation fragments reach the lanes one of two ways, chosen by M:
+//   - direct (one M tile, M <= 16): each lane loads its own fragments from
+//     global memory in A layout, a task ahead of use. Lanes of rows m >= M
+//     read row M - 1, so an instruction touches only M x 4 distinct cache
+//     lines, and nothing goes through the LDS, which the codebook gathers
+//     keep busy. At k = 3, 4 this path also leaves room for the
+//     bank-partitioned codebook copies;
+//   - staged (two M tiles): coalesced loads of 16 rows, transposed through a
+//     per-wave LDS slot when the block changes (the two tiles' direct
+//     fragments, twice over for the fetch ahead, do not fit in registers).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -54,7 +52,6 @@ namespace {
 constexpr int kThreads = 256;    // expand kernel
 constexpr int kGroups = 5;       // 16-row groups per prefill workgroup (80 rows)
 constexpr int kDualGroups = 9;   // the same for the two-projection launch (144 rows)
-constexpr int kDirectMaxM = 8;   // largest M whose activation fragments are loaded directly
 
 // Prefill workgroup size: 8 waves, two per SIMD. For one M tile this
 // measured 2-7% faster than 16 waves (less contention in the LDS queue); two
@@ -937,13 +934,10 @@ hipError_t launch_expand_k(const uint32_t* codes, CodeLayout lay, const float* s
 hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                         const float* scales, const float* lut, uint16_t* y, int N, int nb, int k,
                         hipStream_t st) {
-    // One M tile up to M = 16, two above; direct activation fragments up to
-    // kDirectMaxM at k = 2, for one M tile at k = 3, 4.
-    const int dmax = k == 2 ? kDirectMaxM : 16;
-    const int shape = M > 16 ? 2 : M > dmax ? 1 : 0;
+    // One M tile (direct activation fragments) up to M = 16, two (staged) above.
+    const int shape = M > 16 ? 2 : 0;
     switch (k * 4 + shape) {
     case 8: return launch_axis1_k<2, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
-    case 9: return launch_axis1_k<2, 1, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
     case 10: return launch_axis1_k<2, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
     case 12: return launch_axis1_k<3, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
     case 14: return launch_axis1_k<3, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
@@ -966,11 +960,9 @@ hipError_t launch_axis1_dual(const uint16_t* x, int M, const uint32_t* codes_a,
                              hipStream_t st) {
     if (!axis1_dual_supported(M, N, k)) return hipErrorInvalidValue;
     // M tiles and activation loads as for the single launch
-    const int dmax = k == 2 ? kDirectMaxM : 16;
-    const int shape = M > 16 ? 2 : M > dmax ? 1 : 0;
+    const int shape = M > 16 ? 2 : 0;
     switch (k * 4 + shape) {
     case 8: return launch_axis1_dual_k<2, 1, true>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
-    case 9: return launch_axis1_dual_k<2, 1, false>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
     case 10: return launch_axis1_dual_k<2, 2, false>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
     case 12: return launch_axis1_dual_k<3, 1, true>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
     case 14: return launch_axis1_dual_k<3, 2, false>(x, M, codes_a, scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, lay, N, nb, st);
@@ -999,16 +991,12 @@ hipError_t launch_axis1_swiglu(const uint16_t* x, int M, const uint32_t* codes_g
                              codes_u, scales_u, lut_u, h, lay, N, nb, M);
     }
     // M tiles and activation loads as for the single launch
-    const int dmax = k == 2 ? kDirectMaxM : 16;
-    const int shape = M > 16 ? 2 : M > dmax ? 1 : 0;
+    const int shape = M > 16 ? 2 : 0;
     switch (k * 4 + shape) {
     case 8: return launch_axis1_swiglu_k<2, 1, true>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
-    case 9: return launch_axis1_swiglu_k<2, 1, false>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
     case 10: return launch_axis1_swiglu_k<2, 2, false>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
     case 12: return launch_axis1_swiglu_k<3, 1, true>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
-    case 14: return launch_axis1_swiglu_k<3, 2, false>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
     case 16: return launch_axis1_swiglu_k<4, 1, true>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
-    case 18: return launch_axis1_swiglu_k<4, 2, false>(x, M, codes_g, scales_g, lut_g, codes_u, scales_u, lut_u, h, lay, N, nb, st);
     default: return hipErrorInvalidValue;
     }
 }
