@@ -451,17 +451,27 @@ __device__ __forceinline__ void run_task(Task<K> t, const Task<K>& tn, XFrags<MT
         for (int i = 0; i < 2 * K; ++i) t.w[i] = 0u;
     }
     t.w[2 * K] = next_run_word(t.w[0]);
-    // The group's accumulators move in and out under uniform branches (the
-    // empty asm keeps each a branch: as selects they cost 36 VALU per task).
+    // The group's accumulators move into cur and back. Up to five tiles, by a
+    // uniform register index (s_set_gpr_idx moves); more tiles the compiler
+    // would keep in scratch memory that way, so they move under uniform
+    // branches (the empty asm keeps each a branch: as selects they cost 36
+    // VALU per task). With five one-tile groups the branches (ten per task)
+    // measured 2-5% slower than the indexed moves.
+    constexpr bool kIndexed = KG * MT <= kGroups;
     floatx4 cur[MT];
-    static_for<0, KG>([&](auto gc) {
-        constexpr int G = decltype(gc)::value;
-        if (t.g == G) {
-            asm volatile("");
+    if constexpr (kIndexed) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) cur[mt] = acc[G][mt];
-        }
-    });
+        for (int mt = 0; mt < MT; ++mt) cur[mt] = acc[t.g][mt];
+    } else {
+        static_for<0, KG>([&](auto gc) {
+            constexpr int G = decltype(gc)::value;
+            if (t.g == G) {
+                asm volatile("");
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) cur[mt] = acc[G][mt];
+            }
+        });
+    }
     // Fragments 7 .. 0: only fragment 0 reads the word from the neighbouring
     // lane, which thus has the whole task to arrive.
     auto gather = [&](auto sc) {
@@ -484,14 +494,19 @@ __device__ __forceinline__ void run_task(Task<K> t, const Task<K>& tn, XFrags<MT
         g0 = g1;
         if constexpr (S >= 2) g1 = g2;
     });
-    static_for<0, KG>([&](auto gc) {
-        constexpr int G = decltype(gc)::value;
-        if (t.g == G) {
-            asm volatile("");
+    if constexpr (kIndexed) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[G][mt] = cur[mt];
-        }
-    });
+        for (int mt = 0; mt < MT; ++mt) acc[t.g][mt] = cur[mt];
+    } else {
+        static_for<0, KG>([&](auto gc) {
+            constexpr int G = decltype(gc)::value;
+            if (t.g == G) {
+                asm volatile("");
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[G][mt] = cur[mt];
+            }
+        });
+    }
 }
 
 // silu(v) = v / (1 + e^-v) in float32: the gate nonlinearity of SwiGLU.
