@@ -368,11 +368,23 @@ __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__
     }
 }
 
-// A wave's accumulator tiles: one array per M tile (acc1 unused with one),
-// so that a uniform dynamic group index into either stays in registers.
+// A wave's accumulator tiles: per M tile, groups [0, 5) in one array and the
+// rest (the nine-group launches) in another, so that a uniform dynamic group
+// index into any of them stays in registers (a larger indexed array the
+// compiler keeps in scratch memory). Tile 1's arrays are unused with one tile.
 template <int KG>
-__device__ __forceinline__ floatx4& acc_at(floatx4 (&acc0)[KG], floatx4 (&acc1)[KG], int g, int mt) {
-    return mt == 0 ? acc0[g] : acc1[g];
+struct AccShape {
+    static constexpr int lo = KG < kGroups ? KG : kGroups;
+    static constexpr int hi = KG - lo > 0 ? KG - lo : 1;
+};
+#define TRELLIS_ACC_PARAMS(KG)                                                      \
+    floatx4 (&al0)[AccShape<KG>::lo], floatx4 (&al1)[AccShape<KG>::lo],            \
+        floatx4 (&ah0)[AccShape<KG>::hi], floatx4 (&ah1)[AccShape<KG>::hi]
+// Group g (known at compile time once loops unroll), tile mt.
+template <int KG>
+__device__ __forceinline__ floatx4& acc_at(TRELLIS_ACC_PARAMS(KG), int g, int mt) {
+    constexpr int lo = AccShape<KG>::lo;
+    return g < lo ? (mt == 0 ? al0[g] : al1[g]) : (mt == 0 ? ah0[g - lo] : ah1[g - lo]);
 }
 
 // Which blocks a wave's fragment sets hold: xf block b, xn block lb (direct
@@ -417,8 +429,7 @@ __device__ __forceinline__ int lane_block(const XSource<MT>& xs, int b) {
 template <int K, int MT, bool DIRECT, int KG, bool MIXED = false, bool FOLD = false>
 __device__ __forceinline__ void run_task(Task<K> t, const Task<K>& tn, XFrags<MT>& xf,
                                          XFrags<MT>& xn, XCursor& xc,
-                                         const XSource<MT>& xs, floatx4 (&acc0)[KG],
-                                         floatx4 (&acc1)[KG],
+                                         const XSource<MT>& xs, TRELLIS_ACC_PARAMS(KG),
                                          const float* __restrict__ tab, int lane, int j, int c) {
     static_assert(!MIXED || (K != 2 && !DIRECT), "mixed groups read two plain codebooks");
     constexpr bool P = PrefillLds<K, MT, DIRECT>::pair;
@@ -459,26 +470,36 @@ __device__ __forceinline__ void run_task(Task<K> t, const Task<K>& tn, XFrags<MT
         for (int i = 0; i < 2 * K; ++i) t.w[i] = 0u;
     }
     t.w[2 * K] = next_run_word(t.w[0]);
-    // The group's accumulators move into cur and back. With five groups, by a
-    // uniform register index into each M tile's array (s_set_gpr_idx moves);
-    // with nine the compiler would keep the arrays in scratch memory that way,
-    // so they move under uniform branches (the empty asm keeps each a branch:
-    // as selects they cost 36 VALU per task). The branches (ten per task with
-    // five groups) measured 1-5% slower than the indexed moves.
-    constexpr bool kIndexed = KG <= kGroups;
+    // The group's accumulators move into cur and back by a uniform register
+    // index (s_set_gpr_idx moves) into its array; nine groups pick the array
+    // under one uniform branch (distinct asm markers keep the two sides from
+    // merging into a selected address). One uniform branch per group and
+    // direction instead measured 1-5% slower; it remains for nine groups of two
+    // M tiles, whose indexed arrays the compiler partly keeps in scratch memory
+    // (the empty asm keeps each a branch: as selects they cost 36 VALU per
+    // task).
+    constexpr int kLo = AccShape<KG>::lo;
+    constexpr bool kIndexed = !(MT == 2 && KG > kGroups);
     floatx4 cur[MT];
-    if constexpr (kIndexed) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) cur[mt] = acc_at<KG>(acc0, acc1, t.g, mt);
-    } else {
+    if constexpr (!kIndexed) {
         static_for<0, KG>([&](auto gc) {
             constexpr int G = decltype(gc)::value;
             if (t.g == G) {
                 asm volatile("");
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) cur[mt] = acc_at<KG>(acc0, acc1, G, mt);
+                for (int mt = 0; mt < MT; ++mt) cur[mt] = acc_at<KG>(al0, al1, ah0, ah1, G, mt);
             }
         });
+    } else if (KG <= kLo || t.g < kLo) {
+        asm volatile("; acc lo in");
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) cur[mt] = mt == 0 ? al0[t.g] : al1[t.g];
+        asm volatile("; acc lo in done");
+    } else {
+        asm volatile("; acc hi in");
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) cur[mt] = mt == 0 ? ah0[t.g - kLo] : ah1[t.g - kLo];
+        asm volatile("; acc hi in done");
     }
     // Fragments 7 .. 0: only fragment 0 reads the word from the neighbouring
     // lane, which thus has the whole task to arrive.
@@ -502,18 +523,25 @@ __device__ __forceinline__ void run_task(Task<K> t, const Task<K>& tn, XFrags<MT
         g0 = g1;
         if constexpr (S >= 2) g1 = g2;
     });
-    if constexpr (kIndexed) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc_at<KG>(acc0, acc1, t.g, mt) = cur[mt];
-    } else {
+    if constexpr (!kIndexed) {
         static_for<0, KG>([&](auto gc) {
             constexpr int G = decltype(gc)::value;
             if (t.g == G) {
                 asm volatile("");
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc_at<KG>(acc0, acc1, G, mt) = cur[mt];
+                for (int mt = 0; mt < MT; ++mt) acc_at<KG>(al0, al1, ah0, ah1, G, mt) = cur[mt];
             }
         });
+    } else if (KG <= kLo || t.g < kLo) {
+        asm volatile("; acc lo out");
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) (mt == 0 ? al0[t.g] : al1[t.g]) = cur[mt];
+        asm volatile("; acc lo out done");
+    } else {
+        asm volatile("; acc hi out");
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) (mt == 0 ? ah0[t.g - kLo] : ah1[t.g - kLo]) = cur[mt];
+        asm volatile("; acc hi out done");
     }
 }
 
@@ -587,11 +615,11 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
 
     TaskCtx cx{codes, lay, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp, codes, scales, 0,
                fold ? gc - 1 : -1};
-    floatx4 acc0[KG], acc1[KG];  // M tiles 0 and 1
+    floatx4 al0[AccShape<KG>::lo], al1[AccShape<KG>::lo], ah0[AccShape<KG>::hi], ah1[AccShape<KG>::hi];
 #pragma unroll
     for (int g = 0; g < KG; ++g)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc_at<KG>(acc0, acc1, g, mt) = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) acc_at<KG>(al0, al1, ah0, ah1, g, mt) = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // Prologue: the codebook first, then the first two tasks' code words and,
     // on the direct path, the first block's activation fragments
@@ -620,13 +648,13 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     auto run_tasks = [&]() {
         for (int t0 = tau0; t0 < tau1; t0 += 3) {
             load_task<K, PAIRS, false, FOLD>(tc, cx, cur, tend);
-            run_task<K, MT, DIRECT, KG, false, FOLD>(ta, tb, xf, xn, xc, xs, acc0, acc1, tab, lane, j, c);
+            run_task<K, MT, DIRECT, KG, false, FOLD>(ta, tb, xf, xn, xc, xs, al0, al1, ah0, ah1, tab, lane, j, c);
             load_task<K, PAIRS, false, FOLD>(ta, cx, cur, tend);
             if (t0 + 1 < tau1)
-                run_task<K, MT, DIRECT, KG, false, FOLD>(tb, tc, xf, xn, xc, xs, acc0, acc1, tab, lane, j, c);
+                run_task<K, MT, DIRECT, KG, false, FOLD>(tb, tc, xf, xn, xc, xs, al0, al1, ah0, ah1, tab, lane, j, c);
             load_task<K, PAIRS, false, FOLD>(tb, cx, cur, tend);
             if (t0 + 2 < tau1)
-                run_task<K, MT, DIRECT, KG, false, FOLD>(tc, ta, xf, xn, xc, xs, acc0, acc1, tab, lane, j, c);
+                run_task<K, MT, DIRECT, KG, false, FOLD>(tc, ta, xf, xn, xc, xs, al0, al1, ah0, ah1, tab, lane, j, c);
         }
     };
     run_tasks();
@@ -645,7 +673,7 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
             for (int g = 0; g < KG; ++g)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    part[((wave * KG + g) * 16 + 4 * c + v) * 16 + j] = acc_at<KG>(acc0, acc1, g, mt)[v];
+                    part[((wave * KG + g) * 16 + 4 * c + v) * 16 + j] = acc_at<KG>(al0, al1, ah0, ah1, g, mt)[v];
             __syncthreads();
 #pragma unroll
             for (int it = 0; it < kPasses; ++it) {
@@ -682,7 +710,7 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
 #pragma unroll
         for (int g = 0; g < KG; ++g)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc_at<KG>(acc0, acc1, g, mt) = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < MT; ++mt) acc_at<KG>(al0, al1, ah0, ah1, g, mt) = floatx4{0.f, 0.f, 0.f, 0.f};
         xc = XCursor{};
         xc.lb = ta.b;
         __syncthreads();
@@ -763,11 +791,11 @@ __global__ __launch_bounds__(MixedLds::threads) void axis1_swiglu_mixed_kernel(
     xs.hi = false;
 
     TaskCtx cx{codes_g, lay, scales_g, nb, gc, r0, r1, j, cp, codes_u, scales_u, rm};
-    floatx4 acc0[KG], acc1[KG];  // M tiles 0 and 1
+    floatx4 al0[AccShape<KG>::lo], al1[AccShape<KG>::lo], ah0[AccShape<KG>::hi], ah1[AccShape<KG>::hi];
 #pragma unroll
     for (int g = 0; g < KG; ++g)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc_at<KG>(acc0, acc1, g, mt) = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) acc_at<KG>(al0, al1, ah0, ah1, g, mt) = floatx4{0.f, 0.f, 0.f, 0.f};
 
     // Prologue: both codebooks, then the first two tasks' code words; the
     // codebook stores wait only for their own data.
@@ -792,11 +820,11 @@ __global__ __launch_bounds__(MixedLds::threads) void axis1_swiglu_mixed_kernel(
     XCursor xc;
     for (int t0 = tau0; t0 < tau1; t0 += 3) {
         load_task<K, PAIRS, true>(tc, cx, cur, tend);
-        run_task<K, MT, false, KG, true>(ta, tb, xf, xn, xc, xs, acc0, acc1, tab, lane, j, c);
+        run_task<K, MT, false, KG, true>(ta, tb, xf, xn, xc, xs, al0, al1, ah0, ah1, tab, lane, j, c);
         load_task<K, PAIRS, true>(ta, cx, cur, tend);
-        if (t0 + 1 < tau1) run_task<K, MT, false, KG, true>(tb, tc, xf, xn, xc, xs, acc0, acc1, tab, lane, j, c);
+        if (t0 + 1 < tau1) run_task<K, MT, false, KG, true>(tb, tc, xf, xn, xc, xs, al0, al1, ah0, ah1, tab, lane, j, c);
         load_task<K, PAIRS, true>(tb, cx, cur, tend);
-        if (t0 + 2 < tau1) run_task<K, MT, false, KG, true>(tc, ta, xf, xn, xc, xs, acc0, acc1, tab, lane, j, c);
+        if (t0 + 2 < tau1) run_task<K, MT, false, KG, true>(tc, ta, xf, xn, xc, xs, al0, al1, ah0, ah1, tab, lane, j, c);
     }
     __syncthreads();  // the tables and slots are dead from here on
 
@@ -810,7 +838,7 @@ __global__ __launch_bounds__(MixedLds::threads) void axis1_swiglu_mixed_kernel(
         for (int g = 0; g < KG; ++g)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                part[((wave * KG + g) * 16 + 4 * c + v) * 16 + j] = acc_at<KG>(acc0, acc1, g, mt)[v];
+                part[((wave * KG + g) * 16 + 4 * c + v) * 16 + j] = acc_at<KG>(al0, al1, ah0, ah1, g, mt)[v];
         __syncthreads();
         for (int o = tid; o < 16 * rm; o += kThreadsP) {
             const int m = o / rm, i = o - m * rm;
