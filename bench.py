@@ -351,7 +351,7 @@ def bench_all(T, torch, dev, timer: Timer, ceiling: dict | None, only=None, extr
         nbytes = T.workspace_bytes(g0, 1, T.OP_GEMV_SCATTER)
         ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
         record("c3_scatter_k3", lambda i: T.gemv_scatter(x, *pl.set(i), g0, workspace=ws, y=y),
-               pl.code_bytes, W, 3, rotation_sets=pl.n, split_parts=nbytes // (4 * QWEN_IN))
+               pl.code_bytes, W, 3, rotation_sets=pl.n, workspace_bytes=nbytes)
 
     # C4: prefill, k = 2, 3, 4 x M = 5, 8, 16, 32
     for k in (2, 3, 4):

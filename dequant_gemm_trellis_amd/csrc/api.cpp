@@ -57,11 +57,10 @@ int check_io(const void* x, const void* y) {
     return TRELLIS_OK;
 }
 
-// Axis-0 workspace: the float32 partials of the row ranges ("parts") the
-// kernel splits the contraction into, P * M * cols floats.
+// Axis-0 workspace: the float32 partials of the split contraction, one
+// M x 128 block per (workgroup, column tile) share.
 size_t axis0_workspace(const Dims& d, int M) {
-    return static_cast<size_t>(trellis::axis0_parts(d.rows, d.cols)) * static_cast<size_t>(M) *
-           static_cast<size_t>(d.cols) * sizeof(float);
+    return trellis::axis0_partial_floats(d.rows, d.cols, M) * sizeof(float);
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? TRELLIS_OK : TRELLIS_ERR_HIP; }

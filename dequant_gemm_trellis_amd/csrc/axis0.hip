@@ -18,14 +18,23 @@
 // rows is the B fragment of MFMA number e, whose accumulator collects output
 // column 8j + e. The A fragment is x[m][the same 8 rows].
 //
-// Mapping: a workgroup of 8 waves owns one 128-column tile and one of P
-// contiguous row ranges of it ("parts"; P = 256 / tiles, at least 1, a fixed
-// count so that results do not depend on the device). Each wave takes a
-// contiguous share of the part's 32-row steps (lane j = l % 16 -> columns
-// 8j..8j+7, c = l / 16 -> rows 8c..8c+7 of a step) and accumulates in
-// registers; the waves' tiles are summed in LDS in wave order, one partial per
-// part, and the reduce kernel sums the parts in a fixed order. Every order is
-// fixed, so repeated calls give identical bits.
+// Mapping: the 32-row steps of every 128-column tile are cut into the same nr
+// contiguous ranges, one per wave (a lane j = l % 16 takes columns 8j..8j+7,
+// c = l / 16 rows 8c..8c+7 of a step), and the wave accumulates its range in
+// registers. Waves are numbered band-major: band b holds ranges nv b .. nv b +
+// nv - 1 of tile 0, then of tile 1, and so on, and workgroup L takes waves nv
+// L .. nv L + nv - 1. Usually nr = 8 P with P = 256 / tiles bands (at most the
+// step count) and nv = 8, so a workgroup owns one band of one tile. Where that
+// leaves a quarter or more of the compute units idle (e.g. 136 tiles: 136
+// workgroups), nr = 2048 / tiles (256 compute units x 8 waves), nv = 8 (fewer
+// when there are fewer than 2048 ranges), and the last band's nr mod nv ranges
+// of several tiles share workgroups, a tile's spanning at most two. The plan
+// depends on R and C only, not on the device. All tiles have the same ranges,
+// so neighbouring tiles, whose code rows share cache lines, read the same rows
+// at the same time. A workgroup sums its waves' tiles in LDS in wave order, one
+// partial per run of waves on one tile, and the reduce kernel sums a tile's
+// partials in range order. Every order is fixed, so repeated calls give
+// identical bits.
 //
 // The decode table (the k = 2 pair table, or eight bank-partitioned copies of
 // the codebook for k = 3, 4) is staged once per workgroup, and the next
@@ -248,11 +257,33 @@ __device__ __forceinline__ void a0_decode(const A0Step<MT>& st, const A0Ctx& cx,
     }
 }
 
-template <int K, int MT, bool VEC, bool BUF>
+// The wave plan: nr ranges per tile, nv waves used per workgroup, nf = nr / nv
+// whole bands first (nf nv tiles waves), then the partial band of rr = nr -
+// nf nv waves per tile. Partial slots: one per whole-band workgroup
+// (band-major), then tw per tile for its partial-band run: with rr > 1 a run
+// can be cut by a workgroup end, and its second piece takes the tile's
+// second slot (a run that is not cut writes zeros there).
+struct A0Bands {
+    int nr, nv, nf, tiles;
+    int rr, full, tw;
+    __host__ __device__ A0Bands(int nr_, int nv_, int nf_, int tiles_)
+        : nr(nr_), nv(nv_), nf(nf_), tiles(tiles_) {
+        rr = nr - nf * nv;
+        full = nf * nv * tiles;
+        tw = rr > 1 ? 2 : 1;
+    }
+    __host__ __device__ int slots() const { return nf * tiles + (rr ? tw * tiles : 0); }
+    __host__ __device__ int band_slot(int kb, int t) const { return kb * tiles + t; }
+    __host__ __device__ int tail_slot(int t) const { return nf * tiles + tw * t; }
+};
+
+// TAIL: the plan has a partial band (nr % nv != 0); without it every
+// workgroup is a whole band's.
+template <int K, int MT, bool VEC, bool BUF, bool TAIL>
 __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
     const float* __restrict__ scales, const float* __restrict__ lut,
-    float* __restrict__ partial, CodeLayout lay, int R, int C, int M, int P) {
+    float* __restrict__ partial, CodeLayout lay, int R, int C, int M, int nr, int nv, int nf) {
     constexpr int wpb = Bits<K>::wpb;
     __shared__ __attribute__((aligned(16))) float lds[A0Lds<K>::floats];
     float* const tab = lds;
@@ -260,15 +291,29 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, c = lane >> 4;
-    // Workgroup b runs on XCD b % 8 (round-robin dispatch). The (part, tile)
-    // pairs are numbered part-major and each XCD takes a contiguous range of
-    // them, so that neighbouring tiles of a part, whose code rows share cache
-    // lines (a k = 3 tile reads 48 bytes of each row), meet in one L2.
-    const int G = static_cast<int>(gridDim.x), tiles = G / P;
+    // Workgroup b runs on XCD b % 8 (round-robin dispatch), and each XCD
+    // takes a contiguous range of the workgroups: a band's neighbouring tiles,
+    // whose code rows share cache lines (a k = 3 tile reads 48 bytes of each
+    // row), meet in one L2.
+    const int G = static_cast<int>(gridDim.x), tiles = C / kTileCols, RS = (R + 31) / 32;
     const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
     const int L = xcd * (G / kXcds) + min(xcd, G % kXcds) + slot;
-    const int part = L / tiles;
-    const int tile = L - part * tiles;
+    const A0Bands bd(nr, nv, nf, tiles);
+    const int gw = L * nv + wave;                          // this wave's number
+    const bool live = wave < nv && gw < nr * tiles;
+    const bool band = !TAIL || L * nv < bd.full;           // a whole-band workgroup
+    const int kb = L / tiles;                              // its band
+    int tile = 0, k = 0;                                   // this wave's tile and range
+    if (live) {
+        if (band) {
+            tile = L - kb * tiles;
+            k = kb * nv + wave;
+        } else {
+            const int rem = gw - bd.full;
+            tile = rem / bd.rr;
+            k = nf * nv + (rem - tile * bd.rr);
+        }
+    }
     const int col0 = tile * kTileCols;
     const int blk = col0 / kT;
     const int t0 = (col0 % kT) + 8 * j;         // first weight of this lane's 8 columns
@@ -276,12 +321,10 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const int w0 = lo >> 5, sh = lo & 31;
     const int w1 = (w0 + 1 == wpb) ? 0 : w0 + 1;  // tail-biting wrap to word 0
 
-    // This part's 32-row steps, and this wave's contiguous share of them.
-    const int RS = (R + 31) / 32;
-    const int p0 = static_cast<int>(static_cast<long>(part) * RS / P);
-    const int p1 = static_cast<int>(static_cast<long>(part + 1) * RS / P);
-    const int s0 = p0 + wave * (p1 - p0) / kA0Waves;
-    const int s1 = p0 + (wave + 1) * (p1 - p0) / kA0Waves;
+    // This wave's 32-row steps (none for a wave past the last range; nr x RS
+    // fits in 31 bits: nr <= 2048, RS <= 2^14).
+    const int s0 = k * RS / nr;
+    const int s1 = live ? (k + 1) * RS / nr : s0;
 
     A0Ctx cx;
     cx.cbase = codes + block_word<K>(lay, 0, blk);
@@ -335,7 +378,37 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     if (s < s1) a0_decode<K, MT, VEC>(sa, cx, sh, tab, cofs, acc);
     __syncthreads();  // the table is dead from here on; its space takes the wave partials
 
-    // Sum the waves' tiles in wave order, one M tile at a time.
+    // Sum the waves' tiles in wave order, one M tile at a time: all of them
+    // into one partial in a whole-band workgroup, else one partial per run of
+    // waves on one tile (waves past the last range hold zeros and end no run,
+    // so adding them changes nothing). The slot each wave's run of a tile
+    // ends in (-1: its run goes on) is uniform and fixed before the sums, and
+    // each sum's LDS reads are all issued before its first add.
+    int end_slot[kA0Waves] = {-1, -1, -1, -1, -1, -1, -1, -1};
+    int zero_slot[kA0Waves] = {-1, -1, -1, -1, -1, -1, -1, -1};
+    const int bslot = bd.band_slot(kb, L - kb * tiles);  // a whole-band workgroup's slot
+    if (!band) {
+        const int nlive = min(nv, nr * tiles - L * nv);
+        const int rem = L * nv - bd.full;
+        int t = rem / bd.rr, in = rem - t * bd.rr;  // the first wave's tile and place in its run
+        bool second = in > 0;                       // the run began in the previous workgroup
+#pragma unroll
+        for (int w = 0; w < kA0Waves; ++w) {
+            if (w < nlive) {
+                const bool whole = in + 1 == bd.rr;  // the tile's last wave
+                if (whole || w + 1 == nlive) {
+                    end_slot[w] = bd.tail_slot(t) + (second ? 1 : 0);
+                    if (whole && !second && bd.tw == 2) zero_slot[w] = bd.tail_slot(t) + 1;
+                    ++t;
+                    in = 0;
+                    second = false;
+                } else {
+                    ++in;
+                }
+            }
+        }
+    }
+    const size_t mstride = static_cast<size_t>(M) * kTileCols;
     // D layout: lane holds D[m = 4c + v][n = j] of the tile of column 8j + e.
     float* const red = lds;
 #pragma unroll
@@ -348,72 +421,96 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
         __syncthreads();
         for (int idx = tid; idx < 16 * kTileCols; idx += kA0Threads) {
             const int m = idx / kTileCols, col = idx % kTileCols;
-            float sum = 0.f;
-#pragma unroll
-            for (int w = 0; w < kA0Waves; ++w) sum += red[(w * 16 + m) * kTileCols + col];
             const int mm = 16 * mt + m;
-            if (mm < M) partial[(static_cast<size_t>(part) * M + mm) * C + col0 + col] = sum;
+            float* const dst = partial + static_cast<size_t>(mm) * kTileCols + col;
+            float pv[kA0Waves];  // all reads issued before the first add
+#pragma unroll
+            for (int w = 0; w < kA0Waves; ++w) pv[w] = red[(w * 16 + m) * kTileCols + col];
+            float sum = 0.f;
+            if (band) {
+#pragma unroll
+                for (int w = 0; w < kA0Waves; ++w) sum += pv[w];
+                if (mm < M) dst[static_cast<size_t>(bslot) * mstride] = sum;
+            } else {
+#pragma unroll
+                for (int w = 0; w < kA0Waves; ++w) {
+                    sum += pv[w];
+                    if (end_slot[w] >= 0) {
+                        if (mm < M) {
+                            dst[static_cast<size_t>(end_slot[w]) * mstride] = sum;
+                            if (zero_slot[w] >= 0) dst[static_cast<size_t>(zero_slot[w]) * mstride] = 0.f;
+                        }
+                        sum = 0.f;
+                    }
+                }
+            }
         }
         __syncthreads();
     }
 }
 
-// y[i] = bf16( sum over parts g ascending of partial[g][i] ), i < M*C.
-// Four waves each sum a contiguous quarter of the parts; the quarters are
-// then added in order.
+// y[m][col] = bf16( the partials of col's tile t summed in range order: the
+// whole bands' slots b tiles + t, b ascending, then the tile's partial-band
+// slots ). A block takes 64 outputs of one row m and one tile; four waves
+// each sum a contiguous quarter of the bands (the last also the partial
+// band), then the quarters are added in order.
 __global__ __launch_bounds__(kThreads) void split_reduce_kernel(
-    const float* __restrict__ partial, uint16_t* __restrict__ y, int MC, int G) {
+    const float* __restrict__ partial, uint16_t* __restrict__ y, int M, int C, int nr, int nv,
+    int nf) {
     __shared__ float red[4][64];
-    const int q = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int i = blockIdx.x * 64 + lane;
-    const int per = (G + 3) / 4;
-    const int g0 = q * per, g1 = min(G, g0 + per);
+    const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int i0 = blockIdx.x * 64;
+    const int m = i0 / C, col0 = i0 - m * C;
+    const int tiles = C / kTileCols, t = col0 / kTileCols;
+    const A0Bands bd(nr, nv, nf, tiles);
+    const size_t mstride = static_cast<size_t>(M) * kTileCols;
+    const float* const src = partial + static_cast<size_t>(m) * kTileCols + col0 % kTileCols + lane;
+    const int per = (bd.nf + 3) / 4;
+    const int b0 = q * per, b1 = min(bd.nf, b0 + per);
     float s = 0.f;
-    if (i < MC) {
-        int g = g0;
-        for (; g + 8 <= g1; g += 8) {  // loads issued together, added in order
-            float v[8];
+    int b = b0;
+    for (; b + 4 <= b1; b += 4) {  // loads issued together, added in order
+        float v[4];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) v[t] = partial[static_cast<size_t>(g + t) * MC + i];
+        for (int u = 0; u < 4; ++u) v[u] = src[static_cast<size_t>(bd.band_slot(b + u, t)) * mstride];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) s += v[t];
-        }
-        if (g + 4 <= g1) {
-            float v[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = partial[static_cast<size_t>(g + t) * MC + i];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) s += v[t];
-            g += 4;
-        }
-        for (; g < g1; ++g) s += partial[static_cast<size_t>(g) * MC + i];
+        for (int u = 0; u < 4; ++u) s += v[u];
+    }
+    for (; b < b1; ++b) s += src[static_cast<size_t>(bd.band_slot(b, t)) * mstride];
+    if (q == 3 && bd.rr) {
+        s += src[static_cast<size_t>(bd.tail_slot(t)) * mstride];
+        if (bd.tw == 2) s += src[static_cast<size_t>(bd.tail_slot(t) + 1) * mstride];
     }
     red[q][lane] = s;
     __syncthreads();
-    if (q == 0 && i < MC) y[i] = round_bf16(((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
+    if (q == 0) y[i0 + lane] = round_bf16(((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane]);
 }
 
 template <int K, int MT, bool VEC, bool BUF>
 hipError_t launch_axis0_k(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
-                          const float* scales, const float* lut, float* partial, int R, int C, int P,
-                          hipStream_t st) {
-    const dim3 grid(static_cast<unsigned>((C / kTileCols) * P));
-    return launch_kernel(axis0_mma_kernel<K, MT, VEC, BUF>, grid, dim3(kA0Threads), st, x, codes,
-                         scales, lut, partial, lay, R, C, M, P);
+                          const float* scales, const float* lut, float* partial, int R, int C,
+                          A0Plan pl, hipStream_t st) {
+    const dim3 grid(static_cast<unsigned>(pl.G)), block(kA0Threads);
+    const int nf = pl.ranges / pl.waves;
+    if (pl.ranges % pl.waves)
+        return launch_kernel(axis0_mma_kernel<K, MT, VEC, BUF, true>, grid, block, st, x, codes,
+                             scales, lut, partial, lay, R, C, M, pl.ranges, pl.waves, nf);
+    return launch_kernel(axis0_mma_kernel<K, MT, VEC, BUF, false>, grid, block, st, x, codes, scales,
+                         lut, partial, lay, R, C, M, pl.ranges, pl.waves, nf);
 }
 
 template <int K, int MT>
 hipError_t launch_axis0_v(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
-                          const float* scales, const float* lut, float* partial, int R, int C, int P,
-                          hipStream_t st) {
+                          const float* scales, const float* lut, float* partial, int R, int C,
+                          A0Plan pl, hipStream_t st) {
     if (R % 8 == 0 && reinterpret_cast<uintptr_t>(scales) % 16 == 0) {
         // buffer loads when every byte offset they form fits in 31 bits
         const uint64_t lim = 1ull << 31;
         if (static_cast<uint64_t>(R) * lay.row_words * 4 < lim)
-            return launch_axis0_k<K, MT, true, true>(x, M, codes, lay, scales, lut, partial, R, C, P, st);
-        return launch_axis0_k<K, MT, true, false>(x, M, codes, lay, scales, lut, partial, R, C, P, st);
+            return launch_axis0_k<K, MT, true, true>(x, M, codes, lay, scales, lut, partial, R, C, pl, st);
+        return launch_axis0_k<K, MT, true, false>(x, M, codes, lay, scales, lut, partial, R, C, pl, st);
     }
-    return launch_axis0_k<K, MT, false, false>(x, M, codes, lay, scales, lut, partial, R, C, P, st);
+    return launch_axis0_k<K, MT, false, false>(x, M, codes, lay, scales, lut, partial, R, C, pl, st);
 }
 
 }  // namespace
@@ -437,32 +534,54 @@ hipError_t static_scratch(float** ptr) {
     return hipSuccess;
 }
 
-int axis0_parts(int R, int C) {
-    const int tiles = C / kTileCols, steps = (R + 31) / 32;
+A0Plan axis0_plan(int R, int C) {
+    const int tiles = C / kTileCols, RS = (R + 31) / 32;
+    // Whole bands only: P = 256 / tiles bands (at most the step count) of 8
+    // ranges per tile (some empty when a band has fewer than 8 steps), one
+    // workgroup per (band, tile).
     int P = kA0TargetGroups / tiles;
-    if (P > steps) P = steps;
-    return P > 1 ? P : 1;
+    if (P > RS) P = RS;
+    if (P < 1) P = 1;
+    const int groups = P * tiles;
+    const int rounds = (groups + kA0TargetGroups - 1) / kA0TargetGroups;
+    if (4 * groups >= 3 * rounds * kA0TargetGroups)  // fills at least 3/4 of its rounds
+        return A0Plan{groups, kA0Waves * P, kA0Waves};
+    // Otherwise the finer plan: 2048 / tiles ranges per tile (the chip's 256
+    // compute units x 8 waves), at most the step count, with a partial band.
+    int nr = kA0Waves * kA0TargetGroups / tiles;
+    if (nr > RS) nr = RS;
+    if (nr < 1) nr = 1;
+    const int waves = nr * tiles;  // at most max(2048, tiles)
+    int v = (waves + kA0TargetGroups - 1) / kA0TargetGroups;
+    if (v > kA0Waves) v = kA0Waves;
+    return A0Plan{(waves + v - 1) / v, nr, v};
+}
+
+size_t axis0_partial_floats(int R, int C, int M) {
+    const A0Plan pl = axis0_plan(R, C);
+    const A0Bands bd(pl.ranges, pl.waves, pl.ranges / pl.waves, C / kTileCols);
+    return static_cast<size_t>(bd.slots()) * static_cast<size_t>(M) * kTileCols;
 }
 
 hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                         const float* scales, const float* lut, float* partial, uint16_t* y, int R,
                         int C, int k, hipStream_t st) {
     const bool two = M > 16;
-    const int P = axis0_parts(R, C);
+    const A0Plan pl = axis0_plan(R, C);
     hipError_t e;
     switch (k) {
-    case 2: e = two ? launch_axis0_v<2, 2>(x, M, codes, lay, scales, lut, partial, R, C, P, st)
-                    : launch_axis0_v<2, 1>(x, M, codes, lay, scales, lut, partial, R, C, P, st); break;
-    case 3: e = two ? launch_axis0_v<3, 2>(x, M, codes, lay, scales, lut, partial, R, C, P, st)
-                    : launch_axis0_v<3, 1>(x, M, codes, lay, scales, lut, partial, R, C, P, st); break;
-    case 4: e = two ? launch_axis0_v<4, 2>(x, M, codes, lay, scales, lut, partial, R, C, P, st)
-                    : launch_axis0_v<4, 1>(x, M, codes, lay, scales, lut, partial, R, C, P, st); break;
+    case 2: e = two ? launch_axis0_v<2, 2>(x, M, codes, lay, scales, lut, partial, R, C, pl, st)
+                    : launch_axis0_v<2, 1>(x, M, codes, lay, scales, lut, partial, R, C, pl, st); break;
+    case 3: e = two ? launch_axis0_v<3, 2>(x, M, codes, lay, scales, lut, partial, R, C, pl, st)
+                    : launch_axis0_v<3, 1>(x, M, codes, lay, scales, lut, partial, R, C, pl, st); break;
+    case 4: e = two ? launch_axis0_v<4, 2>(x, M, codes, lay, scales, lut, partial, R, C, pl, st)
+                    : launch_axis0_v<4, 1>(x, M, codes, lay, scales, lut, partial, R, C, pl, st); break;
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    const int MC = M * C;
-    return launch_kernel(split_reduce_kernel, dim3((MC + 63) / 64), dim3(kThreads), st, partial, y,
-                         MC, P);
+    const int MC = M * C;  // a multiple of 128
+    return launch_kernel(split_reduce_kernel, dim3(MC / 64), dim3(kThreads), st, partial, y, M, C,
+                         pl.ranges, pl.waves, pl.ranges / pl.waves);
 }
 
 }  // namespace trellis

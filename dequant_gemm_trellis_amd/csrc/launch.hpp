@@ -102,12 +102,23 @@ hipError_t launch_axis1_swiglu(const uint16_t* x, int M, const uint32_t* codes_g
                                const float* scales_u, const float* lut_u, uint16_t* h,
                                CodeLayout lay, int N, int nb, int k, hipStream_t st);
 
-// Axis 0, 1 <= M <= 32: per-part partials, then the ordered reduce over the
-// parts into y[M][C]. `partial` holds axis0_parts(R, C) * M * C floats.
+// Axis 0, 1 <= M <= 32: split-K partials of 128-column tiles over ranges of
+// the stored rows, then the ordered reduce over them into y[M][C]. `partial`
+// holds axis0_partial_floats(R, C, M) floats.
 hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                         const float* scales, const float* lut, float* partial, uint16_t* y, int R,
                         int C, int k, hipStream_t st);
-int axis0_parts(int R, int C);
+
+// The axis-0 split: every 128-column tile's rows cut into `ranges` ranges,
+// one per wave, `waves` waves per workgroup, G workgroups. It depends on R
+// and C only (not on the device), so results do not either.
+struct A0Plan {
+    int G;       // workgroups
+    int ranges;  // row ranges per tile
+    int waves;   // waves used per workgroup
+};
+A0Plan axis0_plan(int R, int C);
+size_t axis0_partial_floats(int R, int C, int M);
 
 // The scatter variant that allocates nothing keeps its split-K partials in a
 // file-scope device array of kStaticScratchFloats floats (2 MB), one per

@@ -146,15 +146,19 @@ int trellis_gemv_dual(const uint16_t *x, const uint32_t *codes_a, const float *s
  * the stored rows, float32 partials per row range, then their sum and a cast):
  *   partial[s][n] = sum over stored rows r in range s of x[r] * W[r][n]
  *   y[n]          = bf16( sum over s of partial[s][n] ).
- * The stored rows of each 128-column tile are split into P contiguous ranges,
- * P = max(1, min(ceil(in / 32), 256 / (out / 128))); every sum runs in a fixed
- * order, so a geometry always gives the same bits. (The pages use 128 ranges;
- * the count only changes the float32 summation order, which is free.)
+ * The stored rows of each 128-column tile are split into the same contiguous
+ * ranges, nr of them: 8 P with P = max(1, min(ceil(in / 32), 256 / (out /
+ * 128))), or 2048 / (out / 128) (at most ceil(in / 32)) where 8 P ranges
+ * would leave a quarter or more of the GPU's 256 compute units idle. The
+ * count depends on the geometry only, and every sum runs in a fixed order,
+ * so a geometry always gives the same bits. (The pages use 128 ranges; the
+ * count only changes the float32 summation order, which is free.)
  * x: bf16 [in]; codes: uint32 [in][out*k/32]; scales: float32 [in];
  * lut: float32 [4096]; y: bf16 [out]. g->axis must be 0.
  * workspace: float32 scratch of at least
- * trellis_workspace_bytes(g, 1, TRELLIS_OP_GEMV_SCATTER) bytes (P * out
- * floats); its contents on entry do not matter and are overwritten.
+ * trellis_workspace_bytes(g, 1, TRELLIS_OP_GEMV_SCATTER) bytes (one 128-float
+ * partial per workgroup and column tile it sums, at most 4096 of them); its
+ * contents on entry do not matter and are overwritten.
  */
 int trellis_gemv_scatter(const uint16_t *x, const uint32_t *codes, const float *scales,
                          const float *lut, const trellis_geometry *g, float *workspace,
@@ -166,8 +170,8 @@ int trellis_gemv_scatter(const uint16_t *x, const uint32_t *codes, const float *
  * harnesses that forbid allocation): the float32 partials go to a static
  * device array of trellis_static_scratch_bytes() bytes (2 MB; one per device,
  * held until the process ends), which covers the scatter of every accepted
- * geometry (P * out <= 2^19 floats); a geometry needing more returns
- * TRELLIS_ERR_WORKSPACE. The call allocates nothing: the array's device
+ * geometry (at most 4096 partials of 128 floats); a geometry needing more
+ * would return TRELLIS_ERR_WORKSPACE. The call allocates nothing: the array's device
  * address is looked up once per device on the first call there. Outputs are
  * bit-identical to trellis_gemv_scatter's. Every call on a device shares that
  * device's array, so calls that overlap on one device (concurrent streams,
@@ -246,8 +250,8 @@ int trellis_gate_up_swiglu(const uint16_t *x, int32_t M, const uint32_t *codes_g
  * needs none). Returns (size_t)-1 if g, M or op is not supported. The
  * workspace holds the split-K float32 partials of the axis-0 operations
  * (page 59 splitk-prefill.ts sizes its workspace as splits x M x N floats
- * and keeps no dense weight buffer): P x M x out floats here, P as at
- * trellis_gemv_scatter.
+ * and keeps no dense weight buffer): S x M x 128 floats here, S <= 4096 the
+ * (workgroup, column tile) partials of trellis_gemv_scatter's split.
  */
 size_t trellis_workspace_bytes(const trellis_geometry *g, int32_t M, int32_t op);
 

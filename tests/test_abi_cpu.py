@@ -198,13 +198,25 @@ def test_prefill_validation(T):
 
 def test_workspace_bytes(T):
     g0 = geom(T, axis=0, i=17408, o=5120, k=3)
-    # 40 tiles of 128 output columns, 256 / 40 = 6 row ranges each: 6 float32
-    # partial rows of 5120
-    assert T.workspace_bytes(g0, 1, T.OP_GEMV_SCATTER) == 6 * 5120 * 4
-    assert T.workspace_bytes(g0, 32, T.OP_PREFILL) == 6 * 32 * 5120 * 4
-    # 2 tiles: ranges capped by the 32-row steps (37 rows: 2 steps)
+    # 40 tiles of 128 output columns, each tile's 544 32-row steps cut into
+    # 256 // 40 = 6 bands of 8 ranges, one per wave: 240 workgroups of one
+    # (band, tile) each, one M x 128 float32 partial per workgroup
+    assert T.workspace_bytes(g0, 1, T.OP_GEMV_SCATTER) == 240 * 128 * 4
+    assert T.workspace_bytes(g0, 32, T.OP_PREFILL) == 240 * 32 * 128 * 4
+    # 136 tiles (5120 x 17408 stored): one band per tile would leave 120 of
+    # 256 compute units idle, so the finer plan: 15 ranges per tile, one whole
+    # band of 8 per tile, then 7 per tile packed 8 to a workgroup (a tile's 7
+    # may span two workgroups): 136 + 2 * 136 partials
+    up = geom(T, axis=0, i=5120, o=17408, k=3)
+    assert T.workspace_bytes(up, 1, T.OP_GEMV_SCATTER) == 3 * 136 * 128 * 4
+    # 2 tiles, ranges capped by the 32-row steps (37 rows: 2 steps): 4 ranges,
+    # one wave per workgroup
     small = geom(T, axis=0, i=37, o=256, k=3)
-    assert T.workspace_bytes(small, 1, T.OP_GEMV_SCATTER) == 2 * 256 * 4
+    assert T.workspace_bytes(small, 1, T.OP_GEMV_SCATTER) == 4 * 128 * 4
+    # the widest geometry still fits the no-allocation scatter's 2 MB: 4096
+    # tiles of one range each, 4096 partial rows of 128
+    wide = geom(T, axis=0, i=100, o=1 << 19, k=2)
+    assert T.workspace_bytes(wide, 1, T.OP_GEMV_SCATTER) == T.static_scratch_bytes()
     assert T.workspace_bytes(geom(T), 1, T.OP_GEMV) == 0
     with pytest.raises(T.TrellisError):
         T.workspace_bytes(geom(T), 2, T.OP_GEMV)

@@ -225,6 +225,26 @@ def test_axis0_fewer_rows_than_splits(gpu_lib, M):
     assert gate(bf16_to_f64(y), oracle_y(p)) <= TOL
 
 
+@pytest.mark.parametrize("i,o,M,k", [(5120, 17408, 1, 2), (5120, 17408, 32, 4), (2050, 17408, 20, 3),
+                                     (1000, 20480, 1, 4), (96, 17408, 3, 3), (4099, 1280, 1, 3)])
+def test_axis0_partial_band(gpu_lib, i, o, M, k):
+    """Shapes where one workgroup per (band of 8 row ranges, tile) would leave
+    a quarter or more of the compute units idle, so every tile's rows are cut
+    into more ranges and the last band's ranges of several tiles share
+    workgroups (a tile's may span two): 136 tiles in 15 ranges (M = 1, and 32
+    in two M tiles), 2050 ragged rows (element-wise activation loads) in 15,
+    160 tiles in 12, 96 rows = 3 ranges on 2 waves per workgroup (one range per
+    tile in the last band); and 4099 x 10 tiles, which keeps whole bands."""
+    T = gpu_lib
+    shape = synth.Shape(0, 256, L, k, i, o)
+    p = synth.make_problem(shape, M, CFG["test"], proj=950 + M + k)
+    say(f"axis0 partial band in={i} out={o} M={M} k={k}")
+    d = Dev(p, T)
+    y = run(T, d, op="scatter") if M == 1 else run(T, d)
+    ref = oracle_y_full(p) if o > 4096 else oracle_y(p)
+    assert gate(bf16_to_f64(y), ref) <= TOL
+
+
 def test_scatter_deterministic(gpu_lib):
     T = gpu_lib
     shape = synth.Shape(0, 256, L, 3, QWEN_OUT, QWEN_IN)

@@ -18,7 +18,11 @@ pytestmark = pytest.mark.gpu
 def test_static_scatter_matches_workspace_scatter(gpu_lib):
     T = gpu_lib
     assert T.static_scratch_bytes() == 2 << 20
+    # the down projection (whole bands), the up projection's shape stored on
+    # axis 0 (a partial band, whose zero-filled slots the static array keeps
+    # between calls), then a smaller problem
     cases = [(synth.Shape(0, 256, 12, 3, QWEN_OUT, QWEN_IN), synth.CONFIG_IDS["qwen_down_scatter"]),
+             (synth.Shape(0, 256, 12, 3, QWEN_IN, QWEN_OUT), synth.CONFIG_IDS["test"]),
              (synth.Shape(0, 256, 12, 2, 300, 512), synth.CONFIG_IDS["test"])]
     for shape, cfg in cases:
         p = synth.make_problem(shape, 1, cfg, proj=77)
