@@ -110,6 +110,8 @@ CASES = [
     ("prefill", 1, 1024, 300, 17),   # two M tiles
     ("prefill", 0, 300, 1024, 3),
     ("prefill", 0, 300, 1024, 20),
+    ("scatter", 0, 2050, 17408, 1),   # axis 0, a partial band (136 tiles)
+    ("prefill", 0, 2050, 17408, 20),
 ]
 
 
