@@ -226,7 +226,8 @@ def test_axis0_fewer_rows_than_splits(gpu_lib, M):
 
 
 @pytest.mark.parametrize("i,o,M,k", [(5120, 17408, 1, 2), (5120, 17408, 32, 4), (2050, 17408, 20, 3),
-                                     (1000, 20480, 1, 4), (96, 17408, 3, 3), (4099, 1280, 1, 3)])
+                                     (1000, 20480, 1, 4), (96, 17408, 3, 3), (4099, 1280, 1, 3),
+                                     (320, 17408, 1, 3), (640, 24320, 4, 2), (4096, 11520, 1, 4)])
 def test_axis0_partial_band(gpu_lib, i, o, M, k):
     """Shapes where one workgroup per (band of 8 row ranges, tile) would leave
     a quarter or more of the compute units idle, so every tile's rows are cut
@@ -234,7 +235,9 @@ def test_axis0_partial_band(gpu_lib, i, o, M, k):
     workgroups (a tile's may span two): 136 tiles in 15 ranges (M = 1, and 32
     in two M tiles), 2050 ragged rows (element-wise activation loads) in 15,
     160 tiles in 12, 96 rows = 3 ranges on 2 waves per workgroup (one range per
-    tile in the last band); and 4099 x 10 tiles, which keeps whole bands."""
+    tile in the last band), 320 rows = 10 ranges on 6 waves per workgroup, 190
+    tiles in 10 ranges (a last band of 2 per tile), 90 tiles in 22 (6 per
+    tile); and 4099 x 10 tiles, which keeps whole bands."""
     T = gpu_lib
     shape = synth.Shape(0, 256, L, k, i, o)
     p = synth.make_problem(shape, M, CFG["test"], proj=950 + M + k)
