@@ -2,11 +2,12 @@
 dual GEMV, scatter, prefill on both axes, dual prefill) at random k, block
 counts, row counts (including 1, 16, 17, 68 and counts that leave ragged row
 groups), activation batch sizes and code layouts, against the CPU oracle,
-with a second call checked bit-identical to the first.
+with a second call checked bit-identical to the first; and axis 0 at wide
+outputs, where the row split changes plan.
 
-The geometry of case c is drawn from its own generator (seed 20000 + c, or
-40000 + c for the dual-prefill cases), so a failing case is named by its
-index alone and reruns unchanged.
+The geometry of case c is drawn from its own generator (seed 20000 + c,
+40000 + c for the dual-prefill cases, 50000 + c for the wide axis-0 ones), so
+a failing case is named by its index alone and reruns unchanged.
 """
 import numpy as np
 import pytest
@@ -67,6 +68,26 @@ def draw_dual_prefill_case(c):
 @pytest.mark.parametrize("c", range(32))
 def test_random_geometry_dual_prefill(gpu_lib, c):
     run_case(gpu_lib, 1000 + c, *draw_dual_prefill_case(c))
+
+
+def draw_axis0_case(c):
+    """Axis 0 with wide outputs (up to 300 column tiles) and few to many stored
+    rows: both split plans (whole bands, and the finer one with a partial
+    band, one to eight waves per workgroup), at most 8M weights per case."""
+    rng = np.random.default_rng(50000 + c)
+    k = int(rng.integers(2, 5))
+    nb = int(rng.integers(1, 151))
+    cap = max(1, (8 << 20) // (256 * nb))
+    rows = int(min(cap, rng.choice([1, 9, 33, 96, 320, 1000, 2050, 4111])))
+    il = 2 if (nb % 2 == 0 and rng.random() < 0.3) else 0
+    op = str(rng.choice(["scatter", "prefill"]))
+    M = 1 if op == "scatter" else int(rng.integers(1, 33))
+    return synth.Shape(0, 256, 12, k, rows, 256 * nb, il), op, M
+
+
+@pytest.mark.parametrize("c", range(32))
+def test_random_geometry_axis0_splits(gpu_lib, c):
+    run_case(gpu_lib, 2000 + c, *draw_axis0_case(c))
 
 
 def run_case(gpu_lib, c, sh, op, M):
