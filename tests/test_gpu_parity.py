@@ -210,6 +210,27 @@ def test_scatter_integer_codebook_bit_exact(gpu_lib):
     assert np.array_equal(y, synth.to_bf16_bits(exact.astype(np.float32)))
 
 
+@pytest.mark.parametrize("i,o,M,k", [(2050, 17408, 1, 3), (2050, 17408, 20, 4), (320, 17408, 1, 2)])
+def test_axis0_partial_band_integer_codebook_bit_exact(gpu_lib, i, o, M, k):
+    """The finer axis-0 split (a partial band, a tile's last ranges in two
+    workgroups, zero-filled second slots) with an integer codebook, scales in
+    {0.5, 1, 2} and small-integer activations: every partial and sum is exact
+    in float32, so the output is the exact result rounded once to bf16."""
+    T = gpu_lib
+    shape = synth.Shape(0, 256, L, k, i, o)
+    g = np.random.default_rng(78 + M + k)
+    p0 = synth.make_problem(shape, M, CFG["test"], proj=401)
+    xi = g.integers(-3, 4, (M, shape.in_features)).astype(np.float32)
+    p = synth.Problem(shape, M, p0.codes, synth.integer_lut(),
+                      g.choice(np.array([0.5, 1.0, 2.0], np.float32), shape.rows),
+                      synth.to_bf16_bits(xi))
+    say(f"axis0 partial band integer codebook in={i} out={o} M={M} k={k}")
+    d = Dev(p, T)
+    y = bf16_bits(run(T, d, op="scatter") if M == 1 else run(T, d)).reshape(M, -1)
+    exact = oracle_y_full(p)
+    assert np.array_equal(y, synth.to_bf16_bits(exact.astype(np.float32)))
+
+
 @pytest.mark.parametrize("M", [1, 3, 20])
 def test_axis0_fewer_rows_than_splits(gpu_lib, M):
     """37 input rows: two 32-row steps in two row ranges, so most waves of a
