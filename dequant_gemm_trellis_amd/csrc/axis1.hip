@@ -320,6 +320,7 @@ __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__
                 for (int h = 0; h < 2; ++h)
                     raw[mt][line][h] =
                         *reinterpret_cast<const u32x4*>(xrows[mt][h] + b * kT + 64 * line);
+        wave_lds_sync();  // the previous block's reads of the slot come first
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -329,6 +330,7 @@ __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__
                     const int r = 8 * h + wr;
                     slot[((mt * 4 + line) * 16 + r) * 8 + (ws ^ (r & 7))] = raw[mt][line][h];
                 }
+        wave_lds_sync();
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -350,6 +352,7 @@ __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__
                         *reinterpret_cast<const u32x4*>(xrows[mt][h] + b * kT + 64 * (l0 + dl));
 #pragma unroll
         for (int dl = 0; dl < 2; ++dl) {
+            wave_lds_sync();  // earlier reads of the slot come first
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -357,6 +360,7 @@ __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__
                     const int r = 8 * h + wr;
                     slot[(mt * 16 + r) * 8 + (ws ^ (r & 7))] = raw[mt][dl][h];
                 }
+            wave_lds_sync();
             if (c == l0 + dl) {
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)

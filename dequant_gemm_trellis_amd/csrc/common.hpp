@@ -30,6 +30,18 @@ template <int K> struct Bits {
     static constexpr int wpb = kT * K / 32;   // 16 / 24 / 32
 };
 
+// Orders one wave's LDS stores before, and its loads after, the call, for
+// data that lanes of the wave pass to one another through LDS. The hardware
+// runs a wave's LDS instructions in order, so no wait is needed (wave-scope
+// fences emit none), but the compiler reasons per lane: without the fences it
+// may sink a store whose value no later load of the same lane reads into a
+// branch, or move it past another lane's load.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Word offset of block b of stored row r (CodeLayout).
 template <int K>
 __device__ __forceinline__ uint64_t block_word(const CodeLayout& lay, uint32_t r, uint32_t b) {
