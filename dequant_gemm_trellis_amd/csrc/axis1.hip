@@ -302,7 +302,8 @@ __device__ __forceinline__ void load_x_frags_opaque(XFrags<MT>& xn, const uint16
 // which measured slower than staging from M = 16 up. Instead instruction
 // (c, h) reads line c of rows 8h .. 8h + 7 (8 lanes per line, coalesced) and
 // the lines pass through the wave's LDS slot to the lanes of group c: all
-// four at once when the slot holds them, else one at a time. Chunk S of row r
+// four at once when the slot holds them, else two lines of one M tile at a
+// time (half the lanes read per round). Chunk S of row r
 // of a line sits at slot chunk 8 r + (S ^ (r & 7)), so the writes are
 // conflict-free and the reads at most 2-way.
 template <int MT, int LINES>
@@ -338,7 +339,10 @@ __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__
                 xf.v[mt][S] = slot[((mt * 4 + c) * 16 + j) * 8 + (S ^ (j & 7))];
         return;
     }
-    // Two lines at a time: fetching all four at once spills registers at k = 4.
+    // A one-line slot of both M tiles holds two lines of one: two lines are
+    // fetched at a time, then pass through the slot one M tile at a time, so
+    // that half the lanes (the two lines' groups) read at each round.
+    static_assert(MT == 2, "the one-line slot is sized for two M tiles");
 #pragma unroll
     for (int l0 = 0; l0 < 4; l0 += 2) {
         u32x4 raw[MT][2][2];
@@ -351,22 +355,20 @@ __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__
                     raw[mt][dl][h] =
                         *reinterpret_cast<const u32x4*>(xrows[mt][h] + b * kT + 64 * (l0 + dl));
 #pragma unroll
-        for (int dl = 0; dl < 2; ++dl) {
+        for (int mt = 0; mt < MT; ++mt) {
             wave_lds_sync();  // earlier reads of the slot come first
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int dl = 0; dl < 2; ++dl)
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int r = 8 * h + wr;
-                    slot[(mt * 16 + r) * 8 + (ws ^ (r & 7))] = raw[mt][dl][h];
+                    slot[(dl * 16 + r) * 8 + (ws ^ (r & 7))] = raw[mt][dl][h];
                 }
             wave_lds_sync();
-            if (c == l0 + dl) {
+            if ((c >> 1) == (l0 >> 1)) {
+                const int dl = c - l0;
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int S = 0; S < 8; ++S)
-                        xf.v[mt][S] = slot[(mt * 16 + j) * 8 + (S ^ (j & 7))];
+                for (int S = 0; S < 8; ++S) xf.v[mt][S] = slot[(dl * 16 + j) * 8 + (S ^ (j & 7))];
             }
         }
     }
