@@ -38,11 +38,12 @@
 //     global memory in A layout, a task ahead of use. Lanes of rows m >= M
 //     read row M - 1, so an instruction touches only M x 4 distinct cache
 //     lines, and nothing goes through the LDS, which the codebook gathers
-//     keep busy. At k = 3, 4 this path also leaves room for the
-//     bank-partitioned codebook copies;
+//     keep busy;
 //   - staged (two M tiles): coalesced loads of 16 rows, transposed through a
 //     per-wave LDS slot when the block changes (the two tiles' direct
 //     fragments, twice over for the fetch ahead, do not fit in registers).
+// At k = 3, 4 both use the bank-partitioned codebook copies (the staged path
+// with a one-line slot beside them).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -64,16 +65,18 @@ struct PrefillShape {
 };
 
 // Per-wave activation slot (staged path only): `lines` 128-byte lines (8
-// chunks of 16 bytes) of each of the 16 rows of each M tile. Beside the 128 KB
-// pair table only one line fits (2 KB per tile); beside the 16 KB codebook all
-// four do.
+// chunks of 16 bytes) of each of the 16 rows of each M tile. Beside a 128 KB
+// table (the pair table or the codebook copies) only one line fits (2 KB per
+// tile); beside the plain 16 KB codebook all four would.
 template <int K, int MT, bool DIRECT, int KG = kGroups>
 struct PrefillLds {
     static constexpr bool pair = K == 2;
-    // k = 3, 4 with activations loaded directly (one M tile, M <= 16): the bank-partitioned
-    // codebook copies (128 KB). Staged activations keep the 16 KB codebook:
-    // beside the copies only a one-line slot fits, which measured 0-2% slower.
-    static constexpr bool rep = !pair && DIRECT;
+    // k = 3, 4: the bank-partitioned codebook copies (128 KB), beside which a
+    // staged launch (two M tiles) has room for the one-line slot only; with two
+    // lines of one tile per round that measured 2.5% faster than the 16 KB
+    // codebook with the four-line slot. (A staged launch of one M tile does
+    // not occur; it would keep the plain codebook.)
+    static constexpr bool rep = !pair && (DIRECT || MT == 2);
     using Table = DecodeTable<PrefillShape<MT>::threads, pair, rep>;
     static constexpr int tab_floats = Table::floats;
     static constexpr int waves = PrefillShape<MT>::waves;
