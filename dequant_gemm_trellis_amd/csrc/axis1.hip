@@ -53,6 +53,11 @@ namespace {
 constexpr int kThreads = 256;    // expand kernel
 constexpr int kGroups = 5;       // 16-row groups per prefill workgroup (80 rows)
 constexpr int kDualGroups = 9;   // the same for the two-projection launch (144 rows)
+// Mixed gate/up groups: each projection's codebook in kMixedCopies
+// bank-partitioned copies, beside which a one-line activation slot fits.
+constexpr int kMixedCopies = 4;
+constexpr int kMixedLines = kMixedCopies > 1 ? 1 : 4;
+constexpr uint32_t kMixedSpan = kLutEntries * 4 * kMixedCopies;  // bytes per codebook
 
 // Prefill workgroup size: 8 waves, two per SIMD. For one M tile this
 // measured 2-7% faster than 16 waves (less contention in the LDS queue); two
@@ -206,6 +211,11 @@ __device__ __forceinline__ uint64_t task_word(const TaskCtx& cx, int rc, int b) 
     else return (static_cast<size_t>(rc) * cx.nb + b) * Bits<K>::wpb;
 }
 
+// This lane's copy of its codebook (mixed groups), as a byte offset.
+__device__ __forceinline__ uint32_t mixed_copy_offset() {
+    return (threadIdx.x & (kMixedCopies - 1)) << 2;
+}
+
 // Load the cursor's task: its code words (2k per lane) and scale. Past the
 // wave's last task it re-reads that task: every load is unconditional, so the
 // compiler's memory-counter waits never have to cover a skipped load.
@@ -219,7 +229,7 @@ __device__ __forceinline__ void load_task(Task<K>& t, const TaskCtx& cx, TaskCur
     if (FOLD && t.fold) fold_lane(cx, g, b, rc, bl, t.valid);
     t.b = b;
     t.g = g;
-    t.sel = second ? kLutEntries * 4 : 0;
+    if constexpr (MIXED) t.sel = (second ? kMixedSpan : 0u) | mixed_copy_offset();
     const uint32_t* codes = second ? cx.codes_b : cx.codes;
     const float* scales = second ? cx.scales_b : cx.scales;
     load_run64_words<K>(codes + task_word<K, PAIRS>(cx, rc, bl), cx.cp, t.w);
@@ -250,7 +260,7 @@ __device__ __forceinline__ void load_task_opaque(Task<K>& t, const TaskCtx& cx, 
     if (FOLD && t.fold) fold_lane(cx, g, b, rc, bl, t.valid);
     t.b = b;
     t.g = g;
-    t.sel = second ? kLutEntries * 4 : 0;
+    if constexpr (MIXED) t.sel = (second ? kMixedSpan : 0u) | mixed_copy_offset();
     const gu32 codes = second ? codes_b : codes_a;
     const gf32 scales = second ? scales_b : scales_a;
     const gu32 p = codes + task_word<K, PAIRS>(cx, rc, bl) + 2 * K * cx.cp;
@@ -432,9 +442,8 @@ __device__ __forceinline__ int lane_block(const XSource<MT>& xs, int b) {
 // for the loads it had just issued: 6-10% of the kernel.) A block a wave enters
 // unannounced (its first) is fetched at once. Staged path: through the LDS
 // slot, the one memory wait that covers the prefetched code words.
-// MIXED (staged activations, k = 3, 4): each lane reads the plain codebook of
-// its row's projection (Task::sel), and the activation slot holds all four
-// lines.
+// MIXED (staged activations, k = 3, 4): each lane reads its copy of the
+// codebook of its row's projection (Task::sel), beside a one-line slot.
 template <int K, int MT, bool DIRECT, int KG, bool MIXED = false, bool FOLD = false>
 __device__ __forceinline__ void run_task(Task<K> t, const Task<K>& tn, XFrags<MT>& xf,
                                          XFrags<MT>& xn, XCursor& xc,
@@ -443,7 +452,7 @@ __device__ __forceinline__ void run_task(Task<K> t, const Task<K>& tn, XFrags<MT
     static_assert(!MIXED || (K != 2 && !DIRECT), "mixed groups read two plain codebooks");
     constexpr bool P = PrefillLds<K, MT, DIRECT>::pair;
     constexpr bool REP = PrefillLds<K, MT, DIRECT>::rep;
-    constexpr int kLines = MIXED ? 4 : PrefillLds<K, MT, DIRECT>::lines;
+    constexpr int kLines = MIXED ? kMixedLines : PrefillLds<K, MT, DIRECT>::lines;
     // (Distinct empty asm statements open and close each fetch, so that the
     // compiler neither hoists its loads above the branch nor merges fetches
     // into one through a selected address.)
@@ -514,7 +523,7 @@ __device__ __forceinline__ void run_task(Task<K> t, const Task<K>& tn, XFrags<MT
     // lane, which thus has the whole task to arrive.
     auto gather = [&](auto sc) {
         constexpr int S = decltype(sc)::value;
-        if constexpr (MIXED) return gather_run64_sel<K, S>(t.w, tab, t.sel);
+        if constexpr (MIXED) return gather_run64_sel<K, S, kMixedCopies>(t.w, tab, t.sel);
         else return gather_tab<K, S, P, REP>(t.w, tab);
     };
     Gathered<P> g0 = gather(std::integral_constant<int, 7>{});
@@ -739,20 +748,22 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
 // Gate and up with the SwiGLU epilogue at k = 3, 4 and two M tiles (M = 17..32),
 // in mixed groups. Both projections read the same activations, so a 16-row
 // MFMA group may hold rows of either as long as each lane reads its own row's
-// codebook: the two plain 16 KB codebooks sit one after the other in LDS and a
-// lane's gather offset carries its projection (Task::sel). A workgroup owns
-// rows [r0, r1) of both, rm <= 72 of them, i.e. 2 rm virtual rows in at most
-// kDualGroups groups -- the slot count of the dual launch, where the two-phase
-// kernel runs two rounds of five -- with the four-line activation slots beside
-// the two codebooks (160 KB). The waves' tiles are reduced as in the prefill
+// codebook: the two codebooks, each in four bank-partitioned copies (64 KB),
+// sit one after the other in LDS and a lane's gather offset carries its
+// projection and its copy (Task::sel). A workgroup owns rows [r0, r1) of both,
+// rm <= 72 of them, i.e. 2 rm virtual rows in at most kDualGroups groups --
+// the slot count of the dual launch, where the two-phase kernel runs two
+// rounds of five -- with the one-line activation slots beside the codebooks
+// (160 KB). (Two plain codebooks with four-line slots measured 1.2% slower at
+// k = 4, M = 32.) The waves' tiles are reduced as in the prefill
 // epilogue; output (m, i) is bf16(silu(g) * u) with g the sum of virtual row
 // i and u that of virtual row rm + i.
 constexpr int kMixedRows = 16 * kDualGroups / 2;  // rows of each projection per workgroup
 
 struct MixedLds {
     static constexpr int threads = 512, waves = threads / kWave, MT = 2;
-    static constexpr int tab_floats = 2 * kLutEntries;
-    static constexpr int slot_chunks = MT * 4 * 16 * 8;
+    static constexpr int tab_floats = 2 * kLutEntries * kMixedCopies;
+    static constexpr int slot_chunks = MT * kMixedLines * 16 * 8;
     static constexpr int decode_floats = tab_floats + waves * slot_chunks * 4;
     static constexpr int part_floats = waves * kDualGroups * 256;
     static constexpr int floats = decode_floats > part_floats ? decode_floats : part_floats;
@@ -818,10 +829,22 @@ __global__ __launch_bounds__(MixedLds::threads) void axis1_swiglu_mixed_kernel(
     load_task_opaque<K, PAIRS, true>(ta, cx, cur, tend);
     load_task_opaque<K, PAIRS, true>(tb, cx, cur, tend);
     asm volatile("" ::: "memory");
+    {
+        constexpr int R = kMixedCopies, span = kMixedSpan / 4;  // floats per codebook
 #pragma unroll
-    for (int i = 0; i < RepSrc<kThreadsP>::n; ++i) {
-        tab[tid + kThreadsP * i] = src_g.a[i];
-        tab[kLutEntries + tid + kThreadsP * i] = src_u.a[i];
+        for (int i = 0; i < RepSrc<kThreadsP>::n; ++i) {
+            const int e = tid + kThreadsP * i;
+            const float a = src_g.a[i], b = src_u.a[i];
+            if constexpr (R == 1) {
+                tab[e] = a;
+                tab[span + e] = b;
+            } else if constexpr (R == 4) {
+                *reinterpret_cast<float4*>(tab + 4 * e) = float4{a, a, a, a};
+                *reinterpret_cast<float4*>(tab + span + 4 * e) = float4{b, b, b, b};
+            } else {
+                static_assert(R == 1 || R == 4, "staged for one or four copies");
+            }
+        }
     }
     __syncthreads();
 

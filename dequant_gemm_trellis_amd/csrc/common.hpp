@@ -268,20 +268,24 @@ __device__ __forceinline__ Gathered<false> gather_run64_rep(const uint32_t (&w)[
     return g;
 }
 
-// Gathers of fragment S from one of several plain codebooks laid out one after
-// another in LDS: `sel` is the byte offset of this lane's codebook (a multiple
-// of 16 KB), OR-ed into the window's offset as the copy offset is above.
-template <int K, int S>
+// Gathers of fragment S from one of several codebooks laid out one after
+// another in LDS, each in R bank-partitioned copies (entry e of copy c at byte
+// (e R + c) 4, R a power of two): `sel` is the byte offset of this lane's
+// codebook (a multiple of R 16 KB) OR-ed with that of its copy, merged into
+// the window's offset as the copy offset is above.
+template <int K, int S, int R = 1>
 __device__ __forceinline__ Gathered<false> gather_run64_sel(const uint32_t (&w)[2 * K + 1],
                                                             const float* __restrict__ tab,
                                                             uint32_t sel) {
+    constexpr int sh = 2 + (R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : 3);
+    static_assert(R == 1 || R == 2 || R == 4 || R == 8, "R copies, a power of two");
     Gathered<false> g;
     static_for<0, 4>([&](auto dc) {
         constexpr int d = decltype(dc)::value;
         constexpr int q0 = 63 - 8 * S - 2 * d;
-        constexpr uint32_t mask = (kLutEntries - 1u) << 2;
-        g.v[d].x = lds_lut(tab, and_or(field_raw<q0 * K, kL, 2>(w), mask, sel));
-        g.v[d].y = lds_lut(tab, and_or(field_raw<(q0 - 1) * K, kL, 2>(w), mask, sel));
+        constexpr uint32_t mask = (kLutEntries - 1u) << sh;
+        g.v[d].x = lds_lut(tab, and_or(field_raw<q0 * K, kL, sh>(w), mask, sel));
+        g.v[d].y = lds_lut(tab, and_or(field_raw<(q0 - 1) * K, kL, sh>(w), mask, sel));
     });
     return g;
 }
