@@ -363,8 +363,10 @@ def bench_all(T, torch, dev, timer: Timer, ceiling: dict | None, only=None, extr
             x = device_x(torch, dev, pl.shape, M, C["qwen_up_prefill"])
             y = torch.empty((M, QWEN_OUT), dtype=torch.bfloat16, device=dev)
             g = T.Geometry.of(pl.shape)
-            record(name, lambda i: T.prefill(x, *pl.set(i), g, y=y), pl.code_bytes, W, k,
-                   flops=2.0 * M * W, rotation_sets=pl.n)
+            nws = T.workspace_bytes(g, M, T.OP_PREFILL)
+            ws = torch.empty(nws // 4, dtype=torch.float32, device=dev) if nws else None
+            record(name, lambda i, ws=ws: T.prefill(x, *pl.set(i), g, workspace=ws, y=y),
+                   pl.code_bytes, W, k, flops=2.0 * M * W, rotation_sets=pl.n)
 
     # C5: MLP, gate + up in one launch, then down (axis 0), k = 4, M = 1 and 32
     for M in (1, 32):

@@ -71,12 +71,23 @@ int status_of(hipError_t e) { return e == hipSuccess ? TRELLIS_OK : TRELLIS_ERR_
 // the workgroups own at least 16 rows whose partials fit in LDS. Otherwise
 // the tiled kernel of 16-row groups.
 hipError_t launch_axis1_any(const uint16_t* x, int M, const uint32_t* codes, const float* scales,
-                            const float* lut, uint16_t* y, const Dims& d, int k, hipStream_t st) {
+                            const float* lut, uint16_t* y, const Dims& d, int k, hipStream_t st,
+                            float* workspace = nullptr, size_t workspace_bytes = 0) {
     if (M == 1 && d.nb <= trellis::gemv_max_blocks(k))
         return trellis::launch_gemv(x, codes, d.lay, scales, lut, y, d.rows, d.nb, k, st);
     if (trellis::gemv_rows_supported(M, d.rows, d.nb, k))
         return trellis::launch_gemv_rows(x, M, codes, d.lay, scales, lut, y, d.rows, d.nb, k, st);
-    return trellis::launch_axis1(x, M, codes, d.lay, scales, lut, y, d.rows, d.nb, k, st);
+    return trellis::launch_axis1(x, M, codes, d.lay, scales, lut, y, d.rows, d.nb, k, workspace,
+                                 workspace_bytes, st);
+}
+
+// Axis-1 workspace at M rows: the balanced plan's, when the 16-row-group
+// kernel serves M and the plan applies; else none.
+size_t axis1_workspace(const Dims& d, int M, int k) {
+    if (M < 1 || (M == 1 && d.nb <= trellis::gemv_max_blocks(k)) ||
+        trellis::gemv_rows_supported(M, d.rows, d.nb, k))
+        return 0;
+    return trellis::axis1_split_bytes(M, d.rows, d.nb, k);
 }
 
 }  // namespace
@@ -172,7 +183,15 @@ int trellis_prefill(const uint16_t* x, int32_t M, const uint32_t* codes, const f
     if (M < 0 || M > TRELLIS_MAX_M) return TRELLIS_ERR_GEOMETRY;
     if (M == 0) return TRELLIS_OK;
     if ((st = check_operands(codes, scales, lut)) || (st = check_io(x, y))) return st;
-    if (g->axis == 1) return status_of(launch_axis1_any(x, M, codes, scales, lut, y, d, g->k, stream));
+    if (g->axis == 1) {
+        // the workspace is optional here: without one, the unbalanced plan
+        if (workspace) {
+            if (!aligned(workspace, 16)) return TRELLIS_ERR_ALIGN;
+            if (workspace_bytes < axis1_workspace(d, M, g->k)) return TRELLIS_ERR_WORKSPACE;
+        }
+        return status_of(launch_axis1_any(x, M, codes, scales, lut, y, d, g->k, stream, workspace,
+                                          workspace ? workspace_bytes : 0));
+    }
     if (!workspace) return TRELLIS_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return TRELLIS_ERR_ALIGN;
     if (workspace_bytes < axis0_workspace(d, M)) return TRELLIS_ERR_WORKSPACE;
@@ -244,7 +263,8 @@ size_t trellis_workspace_bytes(const trellis_geometry* g, int32_t M, int32_t op)
         return (g->axis == 0 && M == 1) ? axis0_workspace(d, 1) : static_cast<size_t>(-1);
     case TRELLIS_OP_PREFILL:
         if (M < 0 || M > TRELLIS_MAX_M) return static_cast<size_t>(-1);
-        return (g->axis == 1 || M == 0) ? 0 : axis0_workspace(d, M);
+        if (M == 0) return 0;
+        return g->axis == 1 ? axis1_workspace(d, M, g->k) : axis0_workspace(d, M);
     default:
         return static_cast<size_t>(-1);
     }

@@ -44,6 +44,11 @@
 //     fragments, twice over for the fetch ahead, do not fit in registers).
 // At k = 3, 4 both use the bank-partitioned codebook copies (the staged path
 // with a one-line slot beside them).
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -106,6 +111,10 @@ struct TaskCtx {
     // Folded last group (gf >= 1; see task_place): the number of full groups
     // before it. -1: no folding.
     int gf = -1;
+    // Split leftover group (SPLIT; see SplitArgs): this workgroup's nq tasks
+    // of the 16-row group at rows [rs, rs + 16) (rows from rn on are padding),
+    // blocks qb0 .. qb0 + nq - 1, numbered first, in accumulator slot gc.
+    int nq = 0, qb0 = 0, rs = 0, rn = 0;
 };
 
 template <int K>
@@ -139,9 +148,14 @@ struct TaskCursor {
     int rem;  // its position within the block's gc or the pair's 2 gf + 1 tasks
 };
 
-template <bool FOLD>
+template <bool FOLD, bool SPLIT = false>
 __device__ __forceinline__ TaskCursor task_cursor(const TaskCtx& cx, int tau0, int tau_end) {
     const int tau = tau0 < tau_end ? tau0 : tau_end - 1;
+    if constexpr (SPLIT) {
+        if (tau < cx.nq) return {tau, 0, 0};
+        const int q = (tau - cx.nq) / cx.gc;
+        return {tau, q, tau - cx.nq - q * cx.gc};
+    }
     const bool fold = FOLD && cx.gf >= 0;
     const int per = fold ? 2 * cx.gf + 1 : cx.gc;
     const int q = tau / per;
@@ -150,9 +164,22 @@ __device__ __forceinline__ TaskCursor task_cursor(const TaskCtx& cx, int tau0, i
 
 // The cursor's task (block, group, folded?), then the cursor moves on unless
 // that was the last task before tau_end.
-template <bool FOLD>
+template <bool FOLD, bool SPLIT = false>
 __device__ __forceinline__ void task_place(const TaskCtx& cx, TaskCursor& k, int tau_end, int& b,
                                            int& g, bool& fold) {
+    if constexpr (SPLIT) {
+        // the split tasks first, then the full groups block-major; the
+        // block-major cursor starts moving past the first full task
+        const bool sp = k.tau < cx.nq;
+        b = sp ? cx.qb0 + k.tau : k.b0;
+        g = sp ? cx.gc : k.rem;
+        fold = false;
+        if (k.tau + 1 < tau_end && ++k.tau > cx.nq && ++k.rem == cx.gc) {
+            k.rem = 0;
+            ++k.b0;
+        }
+        return;
+    }
     const bool folding = FOLD && cx.gf >= 0;
     if (!folding) {
         b = k.b0;
@@ -186,8 +213,16 @@ __device__ __forceinline__ void fold_lane(const TaskCtx& cx, int g, int b, int& 
 
 // The stored row, code array and scales of lane row 16 g + j of a task, and
 // whether it is a real row (rows past the range re-read the last real one).
-template <bool MIXED>
+template <bool MIXED, bool SPLIT = false>
 __device__ __forceinline__ int task_row(const TaskCtx& cx, int g, bool& valid, bool& second) {
+    if constexpr (SPLIT) {
+        if (g == cx.gc) {  // the split group (a uniform test)
+            const int row = cx.rs + cx.j;
+            valid = row < cx.rn;
+            second = false;
+            return valid ? row : cx.rn - 1;
+        }
+    }
     const int v = 16 * g + cx.j;
     if constexpr (MIXED) {
         valid = v < 2 * cx.rm;
@@ -219,12 +254,12 @@ __device__ __forceinline__ uint32_t mixed_copy_offset() {
 // Load the cursor's task: its code words (2k per lane) and scale. Past the
 // wave's last task it re-reads that task: every load is unconditional, so the
 // compiler's memory-counter waits never have to cover a skipped load.
-template <int K, bool PAIRS, bool MIXED = false, bool FOLD = false>
+template <int K, bool PAIRS, bool MIXED = false, bool FOLD = false, bool SPLIT = false>
 __device__ __forceinline__ void load_task(Task<K>& t, const TaskCtx& cx, TaskCursor& k, int tau_end) {
     int b, g;
-    task_place<FOLD>(cx, k, tau_end, b, g, t.fold);
+    task_place<FOLD, SPLIT>(cx, k, tau_end, b, g, t.fold);
     bool second;
-    int rc = task_row<MIXED>(cx, g, t.valid, second);
+    int rc = task_row<MIXED, SPLIT>(cx, g, t.valid, second);
     int bl = b;
     if (FOLD && t.fold) fold_lane(cx, g, b, rc, bl, t.valid);
     t.b = b;
@@ -241,7 +276,7 @@ __device__ __forceinline__ void load_task(Task<K>& t, const TaskCtx& cx, TaskCur
 // through the restrict kernel pointers the loads count as invariant and the
 // compiler sinks them past the table stores and the barrier to their first
 // use, so the table stores and the code words no longer overlap.
-template <int K, bool PAIRS, bool MIXED = false, bool FOLD = false>
+template <int K, bool PAIRS, bool MIXED = false, bool FOLD = false, bool SPLIT = false>
 __device__ __forceinline__ void load_task_opaque(Task<K>& t, const TaskCtx& cx, TaskCursor& k,
                                                  int tau_end) {
     using gu32 = const __attribute__((address_space(1))) uint32_t*;
@@ -253,9 +288,9 @@ __device__ __forceinline__ void load_task_opaque(Task<K>& t, const TaskCtx& cx, 
     gf32 scales_b = (gf32)cx.scales_b;
     asm volatile("" : "+s"(codes_a), "+s"(scales_a), "+s"(codes_b), "+s"(scales_b));
     int b, g;
-    task_place<FOLD>(cx, k, tau_end, b, g, t.fold);
+    task_place<FOLD, SPLIT>(cx, k, tau_end, b, g, t.fold);
     bool second;
-    int rc = task_row<MIXED>(cx, g, t.valid, second);
+    int rc = task_row<MIXED, SPLIT>(cx, g, t.valid, second);
     int bl = b;
     if (FOLD && t.fold) fold_lane(cx, g, b, rc, bl, t.valid);
     t.b = b;
@@ -563,8 +598,40 @@ __device__ __forceinline__ void run_task(Task<K> t, const Task<K>& tn, XFrags<MT
     }
 }
 
+// Balanced plan of the single-projection launch (SPLIT). With ng 16-row
+// groups over G workgroups, each workgroup owns f = ng / G full groups, and
+// the L = ng % G leftover groups are each cut into p = G / L block ranges, one
+// per workgroup, so every workgroup decodes f nb + nb / p tasks instead of
+// (f + 1) nb. The parts of a leftover group meet through the workspace.
+constexpr int kSplitMaxParts = 8;  // parts per leftover group, at most
+
+struct SplitArgs {
+    unsigned long long* part;  // per workgroup: its part's tile, MT x 64 lanes x 4 tagged words
+    unsigned int tag;          // this call's tag (never 0)
+    int f;                     // full groups per workgroup
+    int p;                     // parts per leftover group
+    int pen;                   // tasks wave 0 takes fewer than an equal share
+};
+
 // silu(v) = v / (1 + e^-v) in float32: the gate nonlinearity of SwiGLU.
 __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)); }
+
+// The parts of a leftover group meet without counters or cache maintenance.
+// Each value travels as one 64-bit word, the call's tag above the float's
+// bits, stored and loaded with device-scope relaxed atomics (performed at the
+// device's coherence point, past the per-XCD L2; a 64-bit atomic is never
+// torn). A part stores its tile once its split tasks are done, goes on, and
+// at the end of its tasks waits for those stores and loads every part of
+// its group: if every word carries the tag, it sums them. The part that
+// checks last sees the others' stores, which completed before their own
+// checks, so at least one part sums; parts that find all words current at
+// the same time write the same bits. Words of another call, or whatever the
+// workspace held, carry another tag (tags repeat after 2^32 calls). A graph
+// replay would reuse its tag, so captured calls take the plan without the
+// split.
+__device__ __forceinline__ unsigned long long split_word(unsigned int tag, float v) {
+    return (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
+}
 
 // Two projections of the same geometry over the same activation rows (an
 // MLP's gate and up) can share one launch.
@@ -577,13 +644,14 @@ __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)
 //   restages the table from the up codebook, runs the same tasks on the up
 //   projection (b operands) and writes y_a[m][n] = bf16(silu(g) * u), the same
 //   thread reducing the same output in both phases.
-template <int K, int MT, bool DIRECT, bool PAIRS, int KG, bool SWIGLU, bool FOLD>
+template <int K, int MT, bool DIRECT, bool PAIRS, int KG, bool SWIGLU, bool FOLD, bool SPLIT>
 __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes_a,
     const float* __restrict__ scales_a, const float* __restrict__ lut_a,
     uint16_t* __restrict__ y_a, const uint32_t* __restrict__ codes_b,
     const float* __restrict__ scales_b, const float* __restrict__ lut_b,
-    uint16_t* __restrict__ y_b, int G0, CodeLayout lay, int N, int nb, int M) {
+    uint16_t* __restrict__ y_b, int G0, CodeLayout lay, int N, int nb, int M, SplitArgs sp) {
+    static_assert(!SPLIT || (!SWIGLU && !FOLD), "the split plan serves the single projection");
     constexpr int kThreadsP = PrefillShape<MT>::threads, kWaves = PrefillShape<MT>::waves;
     using Lds = PrefillLds<K, MT, DIRECT, KG>;
     __shared__ __attribute__((aligned(16))) float lds[Lds::floats];
@@ -596,18 +664,28 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     uint16_t* const y = second ? y_b : y_a;
     const int G = second ? static_cast<int>(gridDim.x) - G0 : G0;
     const int wg = second ? static_cast<int>(blockIdx.x) - G0 : static_cast<int>(blockIdx.x);
-    const int r0 = static_cast<int>(static_cast<long>(wg) * N / G);
-    const int r1 = static_cast<int>(static_cast<long>(wg + 1) * N / G);
+    // Split plan: sp.f full groups per workgroup, then part q of leftover
+    // group ell (blocks [q nb / p, (q + 1) nb / p)).
+    const int r0 = SPLIT ? 16 * sp.f * wg : static_cast<int>(static_cast<long>(wg) * N / G);
+    const int r1 = SPLIT ? r0 + 16 * sp.f : static_cast<int>(static_cast<long>(wg + 1) * N / G);
+    const int ell = SPLIT ? wg / sp.p : 0, q = SPLIT ? wg - ell * sp.p : 0;
+    const int qb0 = SPLIT ? q * nb / sp.p : 0;
+    const int nq = SPLIT ? (q + 1) * nb / sp.p - qb0 : 0;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, c = lane >> 4, cp = 3 - c;
-    const int gc = (r1 - r0 + 15) >> 4;  // groups in this workgroup, <= KG
+    const int gc = (r1 - r0 + 15) >> 4;  // full or own groups in this workgroup, <= KG
     // Folding (task_place): direct fragments, one M tile, M <= 8, a last group
     // of at most 8 rows after at least one full group.
     const bool fold = FOLD && M <= 8 && gc >= 2 && r1 - r0 - 16 * (gc - 1) <= 8;
-    const int tasks = fold ? (nb >> 1) * (2 * gc - 1) + (nb & 1) * gc : gc * nb;
-    const int tau0 = static_cast<int>(static_cast<long>(wave) * tasks / kWaves);
-    const int tau1 = static_cast<int>(static_cast<long>(wave + 1) * tasks / kWaves);
+    const int tasks = SPLIT ? nq + gc * nb : fold ? (nb >> 1) * (2 * gc - 1) + (nb & 1) * gc : gc * nb;
+    // Wave w takes tasks [w V / 8, (w + 1) V / 8) - pen, V = tasks + pen: with
+    // the split plan wave 0 publishes its part mid-way (memory round trips it
+    // waits for), so it takes pen tasks fewer than an equal share.
+    const int pen = SPLIT ? sp.pen : 0;
+    const int vt = tasks + pen;
+    const int tau0 = wave == 0 ? 0 : static_cast<int>(static_cast<long>(wave) * vt / kWaves) - pen;
+    const int tau1 = static_cast<int>(static_cast<long>(wave + 1) * vt / kWaves) - pen;
     const long in = static_cast<long>(nb) * kT;
 
     // Staged path, coalesced activation rows: half h of tile mt is rows
@@ -633,6 +711,15 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
 
     TaskCtx cx{codes, lay, scales, nb, gc > 0 ? gc : 1, r0, r1, j, cp, codes, scales, 0,
                fold ? gc - 1 : -1};
+    if constexpr (SPLIT) {
+        cx.nq = nq;
+        cx.qb0 = qb0;
+        cx.rs = 16 * (sp.f * G + ell);
+        cx.rn = N;
+    }
+    // the wave whose range holds the split tasks (wave 0; the launcher keeps
+    // them within its share) publishes the part after its last one
+    const int split_last = SPLIT && tau0 == 0 ? nq - 1 : -1;
     floatx4 al0[AccShape<KG>::lo], al1[AccShape<KG>::lo], ah0[AccShape<KG>::hi], ah1[AccShape<KG>::hi];
 #pragma unroll
     for (int g = 0; g < KG; ++g)
@@ -648,9 +735,9 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     asm volatile("" ::: "memory");
     Task<K> ta, tb, tc;
     const int tend = tau1 > 1 ? tau1 : 1;  // a wave without tasks re-reads a valid one
-    TaskCursor cur = task_cursor<FOLD>(cx, tau0, tend);
-    load_task_opaque<K, PAIRS, false, FOLD>(ta, cx, cur, tend);
-    load_task_opaque<K, PAIRS, false, FOLD>(tb, cx, cur, tend);
+    TaskCursor cur = task_cursor<FOLD, SPLIT>(cx, tau0, tend);
+    load_task_opaque<K, PAIRS, false, FOLD, SPLIT>(ta, cx, cur, tend);
+    load_task_opaque<K, PAIRS, false, FOLD, SPLIT>(tb, cx, cur, tend);
     XFrags<MT> xn;
     if constexpr (DIRECT) load_x_frags_opaque<MT>(xn, xs.xa, lane_block(xs, ta.b));
     asm volatile("" ::: "memory");
@@ -663,19 +750,107 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     XFrags<MT> xf;
     XCursor xc;
     xc.lb = ta.b;  // the prologue's fetch
+    // Split plan, in two steps of the wave that ran the split tasks (see
+    // split_word): after them it stores its part's tile (slot gc) to the
+    // workspace, [wg][mt][lane][4] tagged words in D layout, and goes on;
+    // after its last task it checks its group's parts and, if all are
+    // current, sums them in part order and writes the group's rows of y. The
+    // wave takes a task or two fewer than the others (SplitArgs::pen), which
+    // covers the round trip.
+    auto split_tile = [&](floatx4 (&mine)[MT]) {
+        // slot gc by uniform branches on constant indices: a dynamic index
+        // would move the accumulator arrays to scratch memory
+        static_for<0, KG>([&](auto gi) {
+            constexpr int Gs = decltype(gi)::value;
+            if (gc == Gs) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) mine[mt] = acc_at<KG>(al0, al1, ah0, ah1, Gs, mt);
+            }
+        });
+    };
+    auto split_store = [&]() {
+        floatx4 mine[MT];
+        split_tile(mine);
+        unsigned long long* const own = sp.part + (static_cast<size_t>(wg) * MT * kWave + lane) * 4;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                __hip_atomic_store(own + mt * kWave * 4 + v, split_word(sp.tag, mine[mt][v]),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto split_finish = [&]() {
+        __builtin_amdgcn_s_waitcnt(0);  // this part's stores complete before the check
+        // every part of the group, all loads in flight together (parts past
+        // p re-read this one and are not used)
+        unsigned long long w[kSplitMaxParts][MT][4];
+#pragma unroll
+        for (int pq = 0; pq < kSplitMaxParts; ++pq) {
+            unsigned long long* src =
+                sp.part + (static_cast<size_t>(ell * sp.p + (pq < sp.p ? pq : q)) * MT * kWave + lane) * 4;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    w[pq][mt][v] = __hip_atomic_load(src + mt * kWave * 4 + v, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        }
+        bool stale = false;
+#pragma unroll
+        for (int pq = 0; pq < kSplitMaxParts; ++pq)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    stale |= pq < sp.p && static_cast<unsigned int>(w[pq][mt][v] >> 32) != sp.tag;
+        if (__builtin_amdgcn_ballot_w64(stale) != 0) return;  // a later part sums
+        floatx4 mine[MT];
+        split_tile(mine);
+        floatx4 sum[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) sum[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pq = 0; pq < kSplitMaxParts; ++pq)
+            if (pq < sp.p) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        sum[mt][v] += pq == q ? mine[mt][v]
+                                              : __uint_as_float(static_cast<unsigned int>(w[pq][mt][v]));
+            }
+        // D[4 c + v][j] of tile mt: activation row 16 mt + 4 c + v, weight row rs + j
+        const int row = cx.rs + j;
+        if (row < N) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = 16 * mt + 4 * c + v;
+                    if (m < M) y[static_cast<size_t>(m) * N + row] = round_bf16(sum[mt][v]);
+                }
+        }
+    };
     auto run_tasks = [&]() {
         for (int t0 = tau0; t0 < tau1; t0 += 3) {
-            load_task<K, PAIRS, false, FOLD>(tc, cx, cur, tend);
+            load_task<K, PAIRS, false, FOLD, SPLIT>(tc, cx, cur, tend);
             run_task<K, MT, DIRECT, KG, false, FOLD>(ta, tb, xf, xn, xc, xs, al0, al1, ah0, ah1, tab, lane, j, c);
-            load_task<K, PAIRS, false, FOLD>(ta, cx, cur, tend);
+            load_task<K, PAIRS, false, FOLD, SPLIT>(ta, cx, cur, tend);
             if (t0 + 1 < tau1)
                 run_task<K, MT, DIRECT, KG, false, FOLD>(tb, tc, xf, xn, xc, xs, al0, al1, ah0, ah1, tab, lane, j, c);
-            load_task<K, PAIRS, false, FOLD>(tb, cx, cur, tend);
+            load_task<K, PAIRS, false, FOLD, SPLIT>(tb, cx, cur, tend);
             if (t0 + 2 < tau1)
                 run_task<K, MT, DIRECT, KG, false, FOLD>(tc, ta, xf, xn, xc, xs, al0, al1, ah0, ah1, tab, lane, j, c);
+            if constexpr (SPLIT) {
+                // once the batch holding the last split task is done
+                if (split_last >= t0 && split_last < t0 + 3) split_store();
+            }
         }
     };
     run_tasks();
+    if constexpr (SPLIT) {
+        if (split_last >= 0) split_finish();
+    }
     __syncthreads();  // the table is dead from here on; its space takes the partials
 
     // part[wave][group][m][j]: D[m = 4c + v][j] of each tile; untouched groups
@@ -941,28 +1116,95 @@ template <int K, int MT, bool DIRECT, int KG, bool SWIGLU>
 hipError_t launch_prefill(bool fold, int G, int G0, hipStream_t st, const uint16_t* x,
                           const uint32_t* codes_a, const float* scales_a, const float* lut_a,
                           uint16_t* y_a, const uint32_t* codes_b, const float* scales_b,
-                          const float* lut_b, uint16_t* y_b, CodeLayout lay, int N, int nb, int M) {
+                          const float* lut_b, uint16_t* y_b, CodeLayout lay, int N, int nb, int M,
+                          const SplitArgs* split = nullptr) {
+    const SplitArgs sp = split ? *split : SplitArgs{};
     auto go = [&](auto kernel) {
         return launch_kernel(kernel, dim3(G), dim3(PrefillShape<MT>::threads), st, x, codes_a,
-                             scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, G0, lay, N, nb, M);
+                             scales_a, lut_a, y_a, codes_b, scales_b, lut_b, y_b, G0, lay, N, nb, M,
+                             sp);
     };
     // Row-major iff a row's blocks are contiguous (with two blocks per row the
     // two layouts coincide).
     const bool rowmajor = lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb;
+    if constexpr (!SWIGLU && KG == kGroups && !(K == 2 && MT == 2)) {
+        if (split)
+            return rowmajor ? go(axis1_prefill_kernel<K, MT, DIRECT, false, KG, false, false, true>)
+                            : go(axis1_prefill_kernel<K, MT, DIRECT, true, KG, false, false, true>);
+    }
     if constexpr (DIRECT && MT == 1) {
         if (fold && M <= 8)
-            return rowmajor ? go(axis1_prefill_kernel<K, MT, DIRECT, false, KG, SWIGLU, true>)
-                            : go(axis1_prefill_kernel<K, MT, DIRECT, true, KG, SWIGLU, true>);
+            return rowmajor ? go(axis1_prefill_kernel<K, MT, DIRECT, false, KG, SWIGLU, true, false>)
+                            : go(axis1_prefill_kernel<K, MT, DIRECT, true, KG, SWIGLU, true, false>);
     }
-    return rowmajor ? go(axis1_prefill_kernel<K, MT, DIRECT, false, KG, SWIGLU, false>)
-                    : go(axis1_prefill_kernel<K, MT, DIRECT, true, KG, SWIGLU, false>);
+    return rowmajor ? go(axis1_prefill_kernel<K, MT, DIRECT, false, KG, SWIGLU, false, false>)
+                    : go(axis1_prefill_kernel<K, MT, DIRECT, true, KG, SWIGLU, false, false>);
+}
+
+// The balanced plan for N rows of nb blocks over G workgroups at M rows and
+// k bits (SplitArgs), or p = 0 where it does not apply: some groups left
+// over, cut into at least two and at most kSplitMaxParts (and nb) parts, one
+// more accumulator slot free, and the split tasks within wave 0's share of
+// every workgroup. Not at k = 2 with two M tiles: there wave 0's split tasks
+// (a block each) restage the activations at every task, and the plan measured
+// 2% slower (at 5120 -> 17408, M = 32). Wave 0's lighter share: one task at
+// M <= 8, two above, as measured best.
+struct SplitPlan {
+    int f = 0, p = 0, L = 0, pen = 0;
+};
+
+SplitPlan split_plan(int N, int nb, int G, int M, int k) {
+    const int ng = (N + 15) / 16;
+    if (G < 1 || (k == 2 && M > 16)) return {};
+    const int f = ng / G, L = ng % G;
+    if (L == 0 || f < 1 || f + 1 > kGroups || G % L != 0) return {};
+    const int p = G / L;
+    if (p < 2 || p > nb || p > kSplitMaxParts) return {};
+    const int nq_max = (nb + p - 1) / p, nq_min = nb / p;
+    const int waves = PrefillShape<1>::waves;
+    // wave 0's share, (tasks + pen) / 8 - pen, holds the split tasks
+    auto fits = [&](int pen) { return (f * nb + nq_min + pen) / waves - pen >= nq_max; };
+    int pen = M <= 8 ? 1 : 2;
+    while (pen > 0 && !fits(pen)) --pen;
+    if (!fits(pen)) return {};
+    return {f, p, L, pen};
+}
+
+// Workspace of the balanced plan: one part's tile per workgroup, 8-byte
+// tagged words.
+size_t split_bytes(const SplitPlan& sp, int G, int MT) {
+    return sp.p ? static_cast<size_t>(G) * MT * kWave * 4 * sizeof(unsigned long long) : 0;
+}
+
+// A fresh tag per call (32 bits, never 0), from a per-process start.
+unsigned int next_split_tag() {
+    static std::atomic<unsigned long long> next{
+        (static_cast<unsigned long long>(
+             std::chrono::steady_clock::now().time_since_epoch().count()) *
+         0x9E3779B97F4A7C15ull) ^
+        (static_cast<unsigned long long>(getpid()) << 32)};
+    for (;;) {
+        const unsigned int t = static_cast<unsigned int>(next.fetch_add(1, std::memory_order_relaxed));
+        if (t) return t;
+    }
 }
 
 template <int K, int MT, bool DIRECT>
 hipError_t launch_axis1_k(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                           const float* scales, const float* lut, uint16_t* y, int N, int nb,
-                          hipStream_t st) {
+                          float* workspace, size_t workspace_bytes, hipStream_t st) {
     const int G = axis1_grid(N);
+    const SplitPlan plan = split_plan(N, nb, G, M, K);
+    const size_t need = split_bytes(plan, G, MT);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (workspace && need && workspace_bytes >= need &&
+        hipStreamIsCapturing(st, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
+        const SplitArgs sp{reinterpret_cast<unsigned long long*>(workspace), next_split_tag(), plan.f,
+                           plan.p, plan.pen};
+        return launch_prefill<K, MT, DIRECT, kGroups, false>(false, G, G, st, x, codes, scales,
+                                                             lut, y, codes, scales, lut, y, lay, N,
+                                                             nb, M, &sp);
+    }
     return launch_prefill<K, MT, DIRECT, kGroups, false>(fold_pays(N, G), G, G, st, x, codes,
                                                          scales, lut, y, codes, scales, lut, y,
                                                          lay, N, nb, M);
@@ -1016,18 +1258,25 @@ hipError_t launch_expand_k(const uint32_t* codes, CodeLayout lay, const float* s
 
 hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                         const float* scales, const float* lut, uint16_t* y, int N, int nb, int k,
-                        hipStream_t st) {
+                        float* workspace, size_t workspace_bytes, hipStream_t st) {
     // One M tile (direct activation fragments) up to M = 16, two (staged) above.
     const int shape = M > 16 ? 2 : 0;
+    float* const ws = workspace;
+    const size_t wb = workspace_bytes;
     switch (k * 4 + shape) {
-    case 8: return launch_axis1_k<2, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
-    case 10: return launch_axis1_k<2, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
-    case 12: return launch_axis1_k<3, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
-    case 14: return launch_axis1_k<3, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
-    case 16: return launch_axis1_k<4, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, st);
-    case 18: return launch_axis1_k<4, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, st);
+    case 8: return launch_axis1_k<2, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, ws, wb, st);
+    case 10: return launch_axis1_k<2, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, ws, wb, st);
+    case 12: return launch_axis1_k<3, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, ws, wb, st);
+    case 14: return launch_axis1_k<3, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, ws, wb, st);
+    case 16: return launch_axis1_k<4, 1, true>(x, M, codes, lay, scales, lut, y, N, nb, ws, wb, st);
+    case 18: return launch_axis1_k<4, 2, false>(x, M, codes, lay, scales, lut, y, N, nb, ws, wb, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+size_t axis1_split_bytes(int M, int N, int nb, int k) {
+    const int G = axis1_grid(N);
+    return split_bytes(split_plan(N, nb, G, M, k), G, M > 16 ? 2 : 1);
 }
 
 bool axis1_dual_supported(int M, int N, int k) {

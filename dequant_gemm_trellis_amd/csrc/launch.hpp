@@ -76,10 +76,15 @@ hipError_t launch_gemv_rows(const uint16_t* x, int M, const uint32_t* codes, Cod
                             int k, hipStream_t st);
 
 // Axis 1, 1 <= M <= 32: y[M][N] from x[M][nb*256] and codes [N][nb][8k]
-// (16-row groups). Persistent workgroups of at most 80 rows; any nb.
+// (16-row groups). Persistent workgroups of at most 80 rows; any nb. Given a
+// workspace of at least axis1_split_bytes(M, N, nb, k) > 0 bytes, outside
+// stream capture, the balanced plan: whole groups per workgroup, the leftover
+// groups cut by blocks, their parts meeting through the workspace (any
+// initial contents; calls sharing a workspace must not overlap in time).
 hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                         const float* scales, const float* lut, uint16_t* y, int N, int nb, int k,
-                        hipStream_t st);
+                        float* workspace, size_t workspace_bytes, hipStream_t st);
+size_t axis1_split_bytes(int M, int N, int nb, int k);
 
 // Two axis-1 projections of one geometry over the same x[M][nb*256], 1 <= M
 // <= 32, in one launch of the 16-row-group kernel (half the compute units

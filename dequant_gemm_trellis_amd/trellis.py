@@ -195,12 +195,19 @@ def static_scratch_bytes() -> int:
     return int(_lib.trellis_static_scratch_bytes())
 
 
-def prefill(x, codes, scales, lut, g, workspace=None, y=None, stream=None) -> torch.Tensor:
+def prefill(x, codes, scales, lut, g, workspace=None, y=None, stream=None,
+            balanced=True) -> torch.Tensor:
+    """Without a workspace one of workspace_bytes is allocated. At axis 1 the
+    workspace is optional: balanced=False passes none (the plan whose last
+    16-row group of each workgroup may be partly empty)."""
     geom = _geom(g)
     M = x.shape[0] if x.dim() == 2 else 1
     if y is None:
         y = torch.empty((M, geom.out_features), dtype=torch.bfloat16, device=x.device)
-    nbytes = workspace_bytes(geom, M, OP_PREFILL)
+    if geom.axis == 1 and not balanced:
+        workspace, nbytes = None, 0
+    else:
+        nbytes = workspace_bytes(geom, M, OP_PREFILL)
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

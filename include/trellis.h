@@ -192,8 +192,17 @@ size_t trellis_static_scratch_bytes(void);
  *   axis 0: y[m][n] = bf16( sum_r x[m][r] * W[r][n] )   (page 59 splitk-prefill.ts:
  *           row splits with float32 partials, then an ordered sum)
  * x: bf16 [M][in]; y: bf16 [M][out]; codes/scales/lut as for the GEMVs.
- * workspace: float32 scratch of trellis_workspace_bytes(g, M, TRELLIS_OP_PREFILL)
- * bytes (0 on axis 1, where workspace may be null).
+ * workspace: scratch of trellis_workspace_bytes(g, M, TRELLIS_OP_PREFILL)
+ * bytes, 16-byte aligned; its contents on entry do not matter. On axis 0 it
+ * is required. On axis 1 it is optional: where that size is not 0 (16-row
+ * groups left over after whole groups per compute unit, e.g. 17408 output
+ * rows), a workspace of it lets the leftover groups be cut by blocks across
+ * workgroups, whose parts meet through it (each output still the float32
+ * sum of its products, in another order: results within the prefill's
+ * tolerance of the call without one, not bit-identical to it); a null
+ * workspace keeps whole groups per workgroup; a non-null one that is too
+ * small is TRELLIS_ERR_WORKSPACE. A call being captured into a graph does
+ * not use it. Calls sharing a workspace must not overlap in time.
  */
 int trellis_prefill(const uint16_t *x, int32_t M, const uint32_t *codes, const float *scales,
                     const float *lut, const trellis_geometry *g, float *workspace,
@@ -251,7 +260,10 @@ int trellis_gate_up_swiglu(const uint16_t *x, int32_t M, const uint32_t *codes_g
  * workspace holds the split-K float32 partials of the axis-0 operations
  * (page 59 splitk-prefill.ts sizes its workspace as splits x M x N floats
  * and keeps no dense weight buffer): S x M x 128 floats here, S <= 4096 the
- * (workgroup, column tile) partials of trellis_gemv_scatter's split.
+ * (workgroup, column tile) partials of trellis_gemv_scatter's split. For the
+ * axis-1 prefill it is the optional workspace of the leftover 16-row groups'
+ * parts (one 16 x 16 or 32 x 16 tile of 8-byte tagged words per compute
+ * unit), 0 where there is none to cut or where the cut does not pay.
  */
 size_t trellis_workspace_bytes(const trellis_geometry *g, int32_t M, int32_t op);
 

@@ -193,7 +193,12 @@ def test_prefill_validation(T):
     assert need > 0
     assert call(32, g0, ws=FAKE, nbytes=need - 1) == T.ERR_WORKSPACE
     assert call(32, g0) == T.ERR_WORKSPACE
-    assert T.workspace_bytes(g1, 32, T.OP_PREFILL) == 0
+    # axis 1: the workspace is optional; one given must hold the balanced plan
+    g1 = geom(T, axis=1, i=5120, o=17408, k=3)
+    need1 = T.workspace_bytes(g1, 32, T.OP_PREFILL)
+    assert need1 > 0
+    assert call(32, g1, ws=FAKE, nbytes=need1 - 1) == T.ERR_WORKSPACE
+    assert call(32, g1, ws=FAKE + 4, nbytes=need1) == T.ERR_ALIGN
 
 
 def test_workspace_bytes(T):
@@ -218,6 +223,22 @@ def test_workspace_bytes(T):
     wide = geom(T, axis=0, i=100, o=1 << 19, k=2)
     assert T.workspace_bytes(wide, 1, T.OP_GEMV_SCATTER) == T.static_scratch_bytes()
     assert T.workspace_bytes(geom(T), 1, T.OP_GEMV) == 0
+    # axis-1 prefill, 5120 -> 17408 on 256 compute units: 1088 16-row groups,
+    # 4 whole ones per workgroup and 64 left over, each cut into 4 block
+    # ranges: one part's tile per workgroup, 64 lanes x 4 tagged 8-byte words
+    # per M tile
+    g1 = geom(T, axis=1, i=5120, o=17408, k=3)
+    assert T.workspace_bytes(g1, 32, T.OP_PREFILL) == 256 * 2 * 64 * 4 * 8
+    assert T.workspace_bytes(g1, 16, T.OP_PREFILL) == 256 * 1 * 64 * 4 * 8
+    # k = 2 with two M tiles keeps the plan without the split
+    g2 = geom(T, axis=1, i=5120, o=17408, k=2)
+    assert T.workspace_bytes(g2, 16, T.OP_PREFILL) == 256 * 1 * 64 * 4 * 8
+    assert T.workspace_bytes(g2, 17, T.OP_PREFILL) == 0
+    assert T.workspace_bytes(g1, 1, T.OP_PREFILL) == 0  # the GEMV
+    # 16384 rows: four whole groups per workgroup, nothing left over
+    assert T.workspace_bytes(geom(T, axis=1, i=5120, o=16384, k=2), 32, T.OP_PREFILL) == 0
+    # 17000 rows: 39 groups left over do not divide 256 workgroups
+    assert T.workspace_bytes(geom(T, axis=1, i=5120, o=17000, k=2), 32, T.OP_PREFILL) == 0
     with pytest.raises(T.TrellisError):
         T.workspace_bytes(geom(T), 2, T.OP_GEMV)
     with pytest.raises(T.TrellisError):
