@@ -277,13 +277,17 @@ struct A0Bands {
     __host__ __device__ int tail_slot(int t) const { return nf * tiles + tw * t; }
 };
 
+constexpr int kFusedMaxBands = 8;  // bands per tile of the fused sum, at most
+
 // TAIL: the plan has a partial band (nr % nv != 0); without it every
 // workgroup is a whole band's.
-template <int K, int MT, bool VEC, bool BUF, bool TAIL>
+template <int K, int MT, bool VEC, bool BUF, bool TAIL, bool FUSED>
 __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
     const float* __restrict__ scales, const float* __restrict__ lut,
-    float* __restrict__ partial, CodeLayout lay, int R, int C, int M, int nr, int nv, int nf) {
+    float* __restrict__ partial, CodeLayout lay, int R, int C, int M, int nr, int nv, int nf,
+    uint16_t* __restrict__ y, unsigned int tag) {
+    static_assert(!FUSED || !TAIL, "the fused sum serves whole-band plans");
     constexpr int wpb = Bits<K>::wpb;
     __shared__ __attribute__((aligned(16))) float lds[A0Lds<K>::floats];
     float* const tab = lds;
@@ -430,7 +434,16 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
             if (band) {
 #pragma unroll
                 for (int w = 0; w < kA0Waves; ++w) sum += pv[w];
-                if (mm < M) dst[static_cast<size_t>(bslot) * mstride] = sum;
+                if constexpr (FUSED) {
+                    if (mm < M)
+                        __hip_atomic_store(reinterpret_cast<unsigned long long*>(partial) +
+                                               static_cast<size_t>(bslot) * mstride +
+                                               static_cast<size_t>(mm) * kTileCols + col,
+                                           tagged_word(slot_tag(tag, bslot), sum),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                } else {
+                    if (mm < M) dst[static_cast<size_t>(bslot) * mstride] = sum;
+                }
             } else {
 #pragma unroll
                 for (int w = 0; w < kA0Waves; ++w) {
@@ -446,6 +459,39 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
             }
         }
         __syncthreads();
+    }
+    if constexpr (FUSED) {
+        // Every band's partial of this tile, as tagged words: where all carry
+        // this call's tag, sum them in band order. The thread that checks a
+        // column last sees every band's store (each completed before its
+        // writer's own check), so every column is written at least once;
+        // threads that find all current at once write the same bits.
+        __builtin_amdgcn_s_waitcnt(0);
+        const unsigned long long* const pw = reinterpret_cast<const unsigned long long*>(partial);
+        const int t = L - kb * tiles;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            for (int idx = tid; idx < 16 * kTileCols; idx += kA0Threads) {
+                const int m = idx / kTileCols, col = idx % kTileCols;
+                const int mm = 16 * mt + m;
+                if (mm >= M) continue;
+                unsigned long long wv[kFusedMaxBands];
+#pragma unroll
+                for (int b = 0; b < kFusedMaxBands; ++b)
+                    wv[b] = __hip_atomic_load(pw + static_cast<size_t>(bd.band_slot(b < nf ? b : kb, t)) * mstride +
+                                                  static_cast<size_t>(mm) * kTileCols + col,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                bool stale = false;
+#pragma unroll
+                for (int b = 0; b < kFusedMaxBands; ++b)
+                    stale |= b < nf && static_cast<unsigned int>(wv[b] >> 32) != slot_tag(tag, bd.band_slot(b, t));
+                if (stale) continue;
+                float sum = 0.f;
+#pragma unroll
+                for (int b = 0; b < kFusedMaxBands; ++b)
+                    if (b < nf) sum += __uint_as_float(static_cast<unsigned int>(wv[b]));
+                y[static_cast<size_t>(mm) * C + t * kTileCols + col] = round_bf16(sum);
+            }
     }
 }
 
@@ -517,28 +563,31 @@ __global__ __launch_bounds__(kWave) void split_reduce_wave_kernel(
 template <int K, int MT, bool VEC, bool BUF>
 hipError_t launch_axis0_k(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                           const float* scales, const float* lut, float* partial, int R, int C,
-                          A0Plan pl, hipStream_t st) {
+                          A0Plan pl, uint16_t* y, unsigned int tag, hipStream_t st) {
     const dim3 grid(static_cast<unsigned>(pl.G)), block(kA0Threads);
     const int nf = pl.ranges / pl.waves;
     if (pl.ranges % pl.waves)
-        return launch_kernel(axis0_mma_kernel<K, MT, VEC, BUF, true>, grid, block, st, x, codes,
-                             scales, lut, partial, lay, R, C, M, pl.ranges, pl.waves, nf);
-    return launch_kernel(axis0_mma_kernel<K, MT, VEC, BUF, false>, grid, block, st, x, codes, scales,
-                         lut, partial, lay, R, C, M, pl.ranges, pl.waves, nf);
+        return launch_kernel(axis0_mma_kernel<K, MT, VEC, BUF, true, false>, grid, block, st, x, codes,
+                             scales, lut, partial, lay, R, C, M, pl.ranges, pl.waves, nf, y, 0u);
+    if (tag)
+        return launch_kernel(axis0_mma_kernel<K, MT, VEC, BUF, false, true>, grid, block, st, x, codes,
+                             scales, lut, partial, lay, R, C, M, pl.ranges, pl.waves, nf, y, tag);
+    return launch_kernel(axis0_mma_kernel<K, MT, VEC, BUF, false, false>, grid, block, st, x, codes, scales,
+                         lut, partial, lay, R, C, M, pl.ranges, pl.waves, nf, y, 0u);
 }
 
 template <int K, int MT>
 hipError_t launch_axis0_v(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                           const float* scales, const float* lut, float* partial, int R, int C,
-                          A0Plan pl, hipStream_t st) {
+                          A0Plan pl, uint16_t* y, unsigned int tag, hipStream_t st) {
     if (R % 8 == 0 && reinterpret_cast<uintptr_t>(scales) % 16 == 0) {
         // buffer loads when every byte offset they form fits in 31 bits
         const uint64_t lim = 1ull << 31;
         if (static_cast<uint64_t>(R) * lay.row_words * 4 < lim)
-            return launch_axis0_k<K, MT, true, true>(x, M, codes, lay, scales, lut, partial, R, C, pl, st);
-        return launch_axis0_k<K, MT, true, false>(x, M, codes, lay, scales, lut, partial, R, C, pl, st);
+            return launch_axis0_k<K, MT, true, true>(x, M, codes, lay, scales, lut, partial, R, C, pl, y, tag, st);
+        return launch_axis0_k<K, MT, true, false>(x, M, codes, lay, scales, lut, partial, R, C, pl, y, tag, st);
     }
-    return launch_axis0_k<K, MT, false, false>(x, M, codes, lay, scales, lut, partial, R, C, pl, st);
+    return launch_axis0_k<K, MT, false, false>(x, M, codes, lay, scales, lut, partial, R, C, pl, y, tag, st);
 }
 
 }  // namespace
@@ -585,10 +634,23 @@ A0Plan axis0_plan(int R, int C) {
     return A0Plan{(waves + v - 1) / v, nr, v};
 }
 
+// Whether the scatter (M = 1) sums its partials in the partial kernel itself
+// (whole bands only, at most kFusedMaxBands per tile, and at most half the
+// static array's partials, so that its 8-byte tagged words still fit there).
+// The plan depends on R, C and M only.
+bool axis0_fused(int R, int C, int M) {
+    if (M != 1) return false;  // at M = 32 the tagged words measured 3 us slower per layer
+    const A0Plan pl = axis0_plan(R, C);
+    const A0Bands bd(pl.ranges, pl.waves, pl.ranges / pl.waves, C / kTileCols);
+    return pl.ranges % pl.waves == 0 && pl.ranges / pl.waves <= kFusedMaxBands &&
+           static_cast<size_t>(bd.slots()) * kTileCols * 2 <= kStaticScratchFloats;
+}
+
 size_t axis0_partial_floats(int R, int C, int M) {
     const A0Plan pl = axis0_plan(R, C);
     const A0Bands bd(pl.ranges, pl.waves, pl.ranges / pl.waves, C / kTileCols);
-    return static_cast<size_t>(bd.slots()) * static_cast<size_t>(M) * kTileCols;
+    const size_t n = static_cast<size_t>(bd.slots()) * static_cast<size_t>(M) * kTileCols;
+    return axis0_fused(R, C, M) ? 2 * n : n;
 }
 
 hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
@@ -596,20 +658,26 @@ hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, CodeLay
                         int C, int k, hipStream_t st) {
     const bool two = M > 16;
     const A0Plan pl = axis0_plan(R, C);
+    const unsigned int tag = axis0_fused(R, C, M) && !stream_capturing(st) ? next_call_tag() : 0u;
     hipError_t e;
     switch (k) {
-    case 2: e = two ? launch_axis0_v<2, 2>(x, M, codes, lay, scales, lut, partial, R, C, pl, st)
-                    : launch_axis0_v<2, 1>(x, M, codes, lay, scales, lut, partial, R, C, pl, st); break;
-    case 3: e = two ? launch_axis0_v<3, 2>(x, M, codes, lay, scales, lut, partial, R, C, pl, st)
-                    : launch_axis0_v<3, 1>(x, M, codes, lay, scales, lut, partial, R, C, pl, st); break;
-    case 4: e = two ? launch_axis0_v<4, 2>(x, M, codes, lay, scales, lut, partial, R, C, pl, st)
-                    : launch_axis0_v<4, 1>(x, M, codes, lay, scales, lut, partial, R, C, pl, st); break;
+    case 2: e = two ? launch_axis0_v<2, 2>(x, M, codes, lay, scales, lut, partial, R, C, pl, y, tag, st)
+                    : launch_axis0_v<2, 1>(x, M, codes, lay, scales, lut, partial, R, C, pl, y, tag, st); break;
+    case 3: e = two ? launch_axis0_v<3, 2>(x, M, codes, lay, scales, lut, partial, R, C, pl, y, tag, st)
+                    : launch_axis0_v<3, 1>(x, M, codes, lay, scales, lut, partial, R, C, pl, y, tag, st); break;
+    case 4: e = two ? launch_axis0_v<4, 2>(x, M, codes, lay, scales, lut, partial, R, C, pl, y, tag, st)
+                    : launch_axis0_v<4, 1>(x, M, codes, lay, scales, lut, partial, R, C, pl, y, tag, st); break;
     default: return hipErrorInvalidValue;
     }
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || tag) return e;
     const int MC = M * C;  // a multiple of 128
     const int nf = pl.ranges / pl.waves;
     const int terms = nf + (pl.ranges % pl.waves ? (pl.ranges % pl.waves > 1 ? 2 : 1) : 0);
+    // a fused plan under stream capture: the same sum in band order as the
+    // fused kernel's (bit-identical to an uncaptured call)
+    if (axis0_fused(R, C, M))
+        return launch_kernel(split_reduce_wave_kernel, dim3(MC / 64), dim3(kWave), st, partial, y, M,
+                             C, pl.ranges, pl.waves, nf);
     // One wave per 64 outputs where there are enough of them to fill the chip
     // several times over (measured: M = 32 at 5120 outputs 0.7 us faster per
     // MLP layer); below that, four waves per 64 outputs keep fewer dependent

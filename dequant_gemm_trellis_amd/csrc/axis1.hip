@@ -626,12 +626,9 @@ __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)
 // checks last sees the others' stores, which completed before their own
 // checks, so at least one part sums; parts that find all words current at
 // the same time write the same bits. Words of another call, or whatever the
-// workspace held, carry another tag (tags repeat after 2^32 calls). A graph
-// replay would reuse its tag, so captured calls take the plan without the
-// split.
-__device__ __forceinline__ unsigned long long split_word(unsigned int tag, float v) {
-    return (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
-}
+// workspace held, carry another tag (tags repeat after 2^32 calls; each
+// slot's expected tag differs, see slot_tag). A graph replay would reuse its
+// tag, so captured calls take the plan without the split.
 
 // Two projections of the same geometry over the same activation rows (an
 // MLP's gate and up) can share one launch.
@@ -776,7 +773,7 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                __hip_atomic_store(own + mt * kWave * 4 + v, split_word(sp.tag, mine[mt][v]),
+                __hip_atomic_store(own + mt * kWave * 4 + v, tagged_word(slot_tag(sp.tag, wg), mine[mt][v]),
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     auto split_finish = [&]() {
@@ -802,7 +799,8 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    stale |= pq < sp.p && static_cast<unsigned int>(w[pq][mt][v] >> 32) != sp.tag;
+                    stale |= pq < sp.p &&
+                             static_cast<unsigned int>(w[pq][mt][v] >> 32) != slot_tag(sp.tag, ell * sp.p + pq);
         if (__builtin_amdgcn_ballot_w64(stale) != 0) return;  // a later part sums
         floatx4 mine[MT];
         split_tile(mine);
@@ -1176,19 +1174,6 @@ size_t split_bytes(const SplitPlan& sp, int G, int MT) {
     return sp.p ? static_cast<size_t>(G) * MT * kWave * 4 * sizeof(unsigned long long) : 0;
 }
 
-// A fresh tag per call (32 bits, never 0), from a per-process start.
-unsigned int next_split_tag() {
-    static std::atomic<unsigned long long> next{
-        (static_cast<unsigned long long>(
-             std::chrono::steady_clock::now().time_since_epoch().count()) *
-         0x9E3779B97F4A7C15ull) ^
-        (static_cast<unsigned long long>(getpid()) << 32)};
-    for (;;) {
-        const unsigned int t = static_cast<unsigned int>(next.fetch_add(1, std::memory_order_relaxed));
-        if (t) return t;
-    }
-}
-
 template <int K, int MT, bool DIRECT>
 hipError_t launch_axis1_k(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                           const float* scales, const float* lut, uint16_t* y, int N, int nb,
@@ -1196,10 +1181,8 @@ hipError_t launch_axis1_k(const uint16_t* x, int M, const uint32_t* codes, CodeL
     const int G = axis1_grid(N);
     const SplitPlan plan = split_plan(N, nb, G, M, K);
     const size_t need = split_bytes(plan, G, MT);
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (workspace && need && workspace_bytes >= need &&
-        hipStreamIsCapturing(st, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
-        const SplitArgs sp{reinterpret_cast<unsigned long long*>(workspace), next_split_tag(), plan.f,
+    if (workspace && need && workspace_bytes >= need && !stream_capturing(st)) {
+        const SplitArgs sp{reinterpret_cast<unsigned long long*>(workspace), next_call_tag(), plan.f,
                            plan.p, plan.pen};
         return launch_prefill<K, MT, DIRECT, kGroups, false>(false, G, G, st, x, codes, scales,
                                                              lut, y, codes, scales, lut, y, lay, N,
@@ -1255,6 +1238,24 @@ hipError_t launch_expand_k(const uint32_t* codes, CodeLayout lay, const float* s
 }
 
 }  // namespace
+
+unsigned int next_call_tag() {
+    static std::atomic<unsigned long long> next{
+        (static_cast<unsigned long long>(
+             std::chrono::steady_clock::now().time_since_epoch().count()) *
+         0x9E3779B97F4A7C15ull) ^
+        (static_cast<unsigned long long>(getpid()) << 32)};
+    for (;;) {
+        const unsigned int t = static_cast<unsigned int>(next.fetch_add(1, std::memory_order_relaxed));
+        if (t) return t;
+    }
+}
+
+bool stream_capturing(hipStream_t st) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    // a query that fails counts as capturing: the plans without tags are safe everywhere
+    return hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone;
+}
 
 hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                         const float* scales, const float* lut, uint16_t* y, int N, int nb, int k,

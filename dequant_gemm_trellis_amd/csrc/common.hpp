@@ -42,6 +42,17 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Tagged partials: workgroups that meet through a workspace pass each float
+// as one 64-bit word, a per-call tag above the float's bits. The tag is mixed
+// with the word's slot, so that a workspace filled with one constant never
+// carries the expected tag in two slots at once.
+__device__ __forceinline__ unsigned int slot_tag(unsigned int tag, int slot) {
+    return tag ^ (static_cast<unsigned int>(slot) * 0x9E3779B9u);
+}
+__device__ __forceinline__ unsigned long long tagged_word(unsigned int tag, float v) {
+    return (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
+}
+
 // Word offset of block b of stored row r (CodeLayout).
 template <int K>
 __device__ __forceinline__ uint64_t block_word(const CodeLayout& lay, uint32_t r, uint32_t b) {

@@ -86,6 +86,12 @@ hipError_t launch_axis1(const uint16_t* x, int M, const uint32_t* codes, CodeLay
                         float* workspace, size_t workspace_bytes, hipStream_t st);
 size_t axis1_split_bytes(int M, int N, int nb, int k);
 
+// Tags of calls whose workgroups meet through tagged words in a workspace:
+// a fresh 32-bit value per call (never 0), from a per-process start. Such
+// plans are not used under stream capture (a replay would repeat the tag).
+unsigned int next_call_tag();
+bool stream_capturing(hipStream_t st);
+
 // Two axis-1 projections of one geometry over the same x[M][nb*256], 1 <= M
 // <= 32, in one launch of the 16-row-group kernel (half the compute units
 // each, at most 144 rows per workgroup); axis1_dual_supported says whether

@@ -155,10 +155,17 @@ int trellis_gemv_dual(const uint16_t *x, const uint32_t *codes_a, const float *s
  * count only changes the float32 summation order, which is free.)
  * x: bf16 [in]; codes: uint32 [in][out*k/32]; scales: float32 [in];
  * lut: float32 [4096]; y: bf16 [out]. g->axis must be 0.
- * workspace: float32 scratch of at least
- * trellis_workspace_bytes(g, 1, TRELLIS_OP_GEMV_SCATTER) bytes (one 128-float
+ * workspace: scratch of at least
+ * trellis_workspace_bytes(g, 1, TRELLIS_OP_GEMV_SCATTER) bytes (one 128-wide
  * partial per workgroup and column tile it sums, at most 4096 of them); its
- * contents on entry do not matter and are overwritten.
+ * contents on entry do not matter and are overwritten. Where every
+ * workgroup owns a whole band of ranges of one tile and a tile has at most
+ * 8 bands (e.g. 17408 -> 5120), the bands meet in the same launch: each
+ * partial travels as 8-byte words tagged with the call, and a workgroup that
+ * finds all of its tile's partials current sums them in range order (the
+ * partials take 8 bytes per value then); otherwise, and under stream
+ * capture, a second launch sums float32 partials. Calls sharing a workspace
+ * must not overlap in time.
  */
 int trellis_gemv_scatter(const uint16_t *x, const uint32_t *codes, const float *scales,
                          const float *lut, const trellis_geometry *g, float *workspace,
@@ -167,11 +174,11 @@ int trellis_gemv_scatter(const uint16_t *x, const uint32_t *codes, const float *
 /*
  * trellis_gemv_scatter without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid allocation): the float32 partials go to a static
- * device array of trellis_static_scratch_bytes() bytes (2 MB; one per device,
- * held until the process ends), which covers the scatter of every accepted
- * geometry (at most 4096 partials of 128 floats); a geometry needing more
- * would return TRELLIS_ERR_WORKSPACE. The call allocates nothing: the array's device
+ * harnesses that forbid allocation): the partials go to a static device
+ * array of trellis_static_scratch_bytes() bytes (2 MB; one per device, held
+ * until the process ends), which covers the scatter of every accepted
+ * geometry (at most 4096 partials of 128 floats, or 2048 of 128 tagged
+ * words); a geometry needing more would return TRELLIS_ERR_WORKSPACE. The call allocates nothing: the array's device
  * address is looked up once per device on the first call there. Outputs are
  * bit-identical to trellis_gemv_scatter's. Every call on a device shares that
  * device's array, so calls that overlap on one device (concurrent streams,
@@ -260,7 +267,9 @@ int trellis_gate_up_swiglu(const uint16_t *x, int32_t M, const uint32_t *codes_g
  * workspace holds the split-K float32 partials of the axis-0 operations
  * (page 59 splitk-prefill.ts sizes its workspace as splits x M x N floats
  * and keeps no dense weight buffer): S x M x 128 floats here, S <= 4096 the
- * (workgroup, column tile) partials of trellis_gemv_scatter's split. For the
+ * (workgroup, column tile) partials of trellis_gemv_scatter's split (8-byte
+ * tagged words instead of floats where the scatter sums them in one
+ * launch). For the
  * axis-1 prefill it is the optional workspace of the leftover 16-row groups'
  * parts (one 16 x 16 or 32 x 16 tile of 8-byte tagged words per compute
  * unit), 0 where there is none to cut or where the cut does not pay.

@@ -205,8 +205,10 @@ def test_workspace_bytes(T):
     g0 = geom(T, axis=0, i=17408, o=5120, k=3)
     # 40 tiles of 128 output columns, each tile's 544 32-row steps cut into
     # 256 // 40 = 6 bands of 8 ranges, one per wave: 240 workgroups of one
-    # (band, tile) each, one M x 128 float32 partial per workgroup
-    assert T.workspace_bytes(g0, 1, T.OP_GEMV_SCATTER) == 240 * 128 * 4
+    # (band, tile) each, one M x 128 partial per workgroup; the scatter
+    # (M = 1) sums its bands in the same launch, the partials as 8-byte
+    # tagged words, the prefill in a reduce launch from float32 partials
+    assert T.workspace_bytes(g0, 1, T.OP_GEMV_SCATTER) == 240 * 128 * 8
     assert T.workspace_bytes(g0, 32, T.OP_PREFILL) == 240 * 32 * 128 * 4
     # 136 tiles (5120 x 17408 stored): one band per tile would leave 120 of
     # 256 compute units idle, so the finer plan: 15 ranges per tile, one whole
@@ -215,11 +217,12 @@ def test_workspace_bytes(T):
     up = geom(T, axis=0, i=5120, o=17408, k=3)
     assert T.workspace_bytes(up, 1, T.OP_GEMV_SCATTER) == 3 * 136 * 128 * 4
     # 2 tiles, ranges capped by the 32-row steps (37 rows: 2 steps): 4 ranges,
-    # one wave per workgroup
+    # one wave per workgroup (whole bands: summed in the launch, tagged words)
     small = geom(T, axis=0, i=37, o=256, k=3)
-    assert T.workspace_bytes(small, 1, T.OP_GEMV_SCATTER) == 4 * 128 * 4
+    assert T.workspace_bytes(small, 1, T.OP_GEMV_SCATTER) == 4 * 128 * 8
     # the widest geometry still fits the no-allocation scatter's 2 MB: 4096
-    # tiles of one range each, 4096 partial rows of 128
+    # tiles of one range each, 4096 float32 partial rows of 128 (too many to
+    # sum in the launch as tagged words)
     wide = geom(T, axis=0, i=100, o=1 << 19, k=2)
     assert T.workspace_bytes(wide, 1, T.OP_GEMV_SCATTER) == T.static_scratch_bytes()
     assert T.workspace_bytes(geom(T), 1, T.OP_GEMV) == 0

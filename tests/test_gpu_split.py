@@ -158,3 +158,68 @@ def test_split_not_captured(gpu_lib):
         T.prefill(d.x, d.codes, d.scales, d.lut, d.shape, workspace=ws, y=y)
         torch.cuda.synchronize()
         assert np.array_equal(bf16_bits(y), balanced), r
+
+
+# ------------------------------------------------ the scatter's in-launch sum
+FUSED = synth.Shape(0, 256, L, 3, 1000, 5120)  # 40 tiles x 6 bands of whole-band workgroups
+
+
+@pytest.mark.parametrize("fill", [None, 0x00, 0xFF, 0x7FC00000])
+def test_scatter_tagged_sum_any_contents(gpu_lib, fill):
+    """The scatter whose bands meet through tagged words (whole bands, few
+    per tile): a fresh workspace, one of zero bytes, of all-ones bytes, or of
+    quiet NaNs gives the same bits, within tolerance of the oracle, on three
+    calls in a row."""
+    T = gpu_lib
+    n = T.workspace_bytes(FUSED, 1, T.OP_GEMV_SCATTER)
+    assert n == 240 * 128 * 8, n  # the tagged-word plan
+    p = synth.make_problem(FUSED, 1, CFG["test"], proj=2500)
+    d = Dev(p, T)
+    say(f"scatter tagged sum, workspace fill {fill}")
+    ref = bf16_bits(T.gemv_scatter(d.x.reshape(-1), d.codes, d.scales, d.lut, FUSED,
+                                   workspace=torch.empty(n // 4, dtype=torch.float32, device="cuda")))
+    if fill is None:
+        ws = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    elif fill == 0x7FC00000:
+        ws = torch.full((n // 4,), fill, dtype=torch.int32, device="cuda").view(torch.float32)
+    else:
+        ws = torch.full((n,), fill, dtype=torch.uint8, device="cuda").view(torch.float32)
+    for _ in range(3):
+        y = T.gemv_scatter(d.x.reshape(-1), d.codes, d.scales, d.lut, FUSED, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(y), ref)
+    assert gate(bf16_to_f64(y.reshape(1, -1)), oracle_y(p)) <= TOL
+
+
+def test_scatter_tagged_sum_under_capture(gpu_lib):
+    """Under stream capture the scatter takes float32 partials and a reduce
+    launch summing the bands in the same order: every replay, with eager
+    calls on the same workspace in between, equals the eager bits."""
+    T = gpu_lib
+    n = T.workspace_bytes(FUSED, 1, T.OP_GEMV_SCATTER)
+    p = synth.make_problem(FUSED, 1, CFG["test"], proj=2501)
+    d = Dev(p, T)
+    ws = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty(5120, dtype=torch.bfloat16, device="cuda")
+    xv = d.x.reshape(-1)
+    say("scatter tagged sum under stream capture")
+    T.gemv_scatter(xv, d.codes, d.scales, d.lut, FUSED, workspace=ws, y=y)
+    torch.cuda.synchronize()
+    eager = bf16_bits(y)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        T.gemv_scatter(xv, d.codes, d.scales, d.lut, FUSED, workspace=ws, y=y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        T.gemv_scatter(xv, d.codes, d.scales, d.lut, FUSED, workspace=ws, y=y)
+    for r in range(3):
+        y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(y), eager), r
+        T.gemv_scatter(xv, d.codes, d.scales, d.lut, FUSED, workspace=ws, y=y)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(y), eager), r
