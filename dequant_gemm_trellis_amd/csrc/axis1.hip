@@ -602,21 +602,8 @@ __device__ __forceinline__ void run_task(Task<K> t, const Task<K>& tn, XFrags<MT
 // groups over G workgroups, each workgroup owns f = ng / G full groups, and
 // the L = ng % G leftover groups are each cut into p = G / L block ranges, one
 // per workgroup, so every workgroup decodes f nb + nb / p tasks instead of
-// (f + 1) nb. The parts of a leftover group meet through the workspace.
-constexpr int kSplitMaxParts = 8;  // parts per leftover group, at most
-
-struct SplitArgs {
-    unsigned long long* part;  // per workgroup: its part's tile, MT x 64 lanes x 4 tagged words
-    unsigned int tag;          // this call's tag (never 0)
-    int f;                     // full groups per workgroup
-    int p;                     // parts per leftover group
-    int pen;                   // tasks wave 0 takes fewer than an equal share
-};
-
-// silu(v) = v / (1 + e^-v) in float32: the gate nonlinearity of SwiGLU.
-__device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)); }
-
-// The parts of a leftover group meet without counters or cache maintenance.
+// (f + 1) nb. The parts of a leftover group meet through the workspace,
+// without counters or cache maintenance.
 // Each value travels as one 64-bit word, the call's tag above the float's
 // bits, stored and loaded with device-scope relaxed atomics (performed at the
 // device's coherence point, past the per-XCD L2; a 64-bit atomic is never
@@ -629,6 +616,18 @@ __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)
 // workspace held, carry another tag (tags repeat after 2^32 calls; each
 // slot's expected tag differs, see slot_tag). A graph replay would reuse its
 // tag, so captured calls take the plan without the split.
+constexpr int kSplitMaxParts = 8;  // parts per leftover group, at most
+
+struct SplitArgs {
+    unsigned long long* part;  // per workgroup: its part's tile, MT x 64 lanes x 4 tagged words
+    unsigned int tag;          // this call's tag (never 0)
+    int f;                     // full groups per workgroup
+    int p;                     // parts per leftover group
+    int pen;                   // tasks wave 0 takes fewer than an equal share
+};
+
+// silu(v) = v / (1 + e^-v) in float32: the gate nonlinearity of SwiGLU.
+__device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)); }
 
 // Two projections of the same geometry over the same activation rows (an
 // MLP's gate and up) can share one launch.
@@ -748,7 +747,7 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     XCursor xc;
     xc.lb = ta.b;  // the prologue's fetch
     // Split plan, in two steps of the wave that ran the split tasks (see
-    // split_word): after them it stores its part's tile (slot gc) to the
+    // SplitArgs): after them it stores its part's tile (slot gc) to the
     // workspace, [wg][mt][lane][4] tagged words in D layout, and goes on;
     // after its last task it checks its group's parts and, if all are
     // current, sums them in part order and writes the group's rows of y. The
