@@ -6,8 +6,10 @@ with a second call checked bit-identical to the first; and axis 0 at wide
 outputs, where the row split changes plan.
 
 The geometry of case c is drawn from its own generator (seed 20000 + c,
-40000 + c for the dual-prefill cases, 50000 + c for the wide axis-0 ones), so
-a failing case is named by its index alone and reruns unchanged.
+40000 + c for the dual-prefill cases, 50000 + c for the wide axis-0 ones,
+60000 + c for the balanced prefill, 70000 + c for the scatter whose bands
+meet in one launch), so a failing case is named by its index alone and
+reruns unchanged.
 """
 import numpy as np
 import pytest
@@ -88,6 +90,55 @@ def draw_axis0_case(c):
 @pytest.mark.parametrize("c", range(32))
 def test_random_geometry_axis0_splits(gpu_lib, c):
     run_case(gpu_lib, 2000 + c, *draw_axis0_case(c))
+
+
+def draw_balanced_case(c):
+    """Axis-1 prefill where the balanced plan applies on 256 compute units:
+    ceil(N / 16) = 256 f + L groups with L dividing 256 (f whole groups per
+    workgroup, the L leftover groups cut into p = 256 / L <= 8 parts of one or
+    more blocks), a ragged last group, random k, batch and layout; drawn again
+    until wave 0's share holds a part's tasks (the launcher's condition)."""
+    rng = np.random.default_rng(60000 + c)
+    while True:
+        k = int(rng.integers(2, 5))
+        f = int(rng.integers(1, 5))
+        L = int(rng.choice([32] if f == 1 else [32, 64, 128]))
+        p = 256 // L
+        nb = int(rng.integers(p, p + 7))
+        nq_max, nq_min = -(-nb // p), nb // p
+        if (f * nb + nq_min) // 8 >= nq_max:
+            break
+    N = 16 * (256 * f + L) - int(rng.integers(0, 16))
+    # 5 rows or more (fewer take the GEMV-mapped kernel), two M tiles only at k = 3, 4
+    M = int(rng.integers(5, 17 if k == 2 else 21))
+    M = max(5, min(M, 200_000_000 // (N * nb * 256)))
+    il = 2 if (nb % 2 == 0 and rng.random() < 0.3) else 0
+    return synth.Shape(1, 256, 12, k, 256 * nb, N, il), "prefill", M
+
+
+@pytest.mark.parametrize("c", range(16))
+def test_random_geometry_balanced_prefill(gpu_lib, c):
+    sh, op, M = draw_balanced_case(c)
+    if gpu_lib.workspace_bytes(sh, M, gpu_lib.OP_PREFILL) == 0:
+        pytest.skip("the balanced plan does not apply with this device's compute-unit count")
+    run_case(gpu_lib, 3000 + c, sh, op, M)
+
+
+def draw_scatter_tagged_case(c):
+    """The scatter at 32 to 120 column tiles (whole bands of at most 8 per
+    tile, summed in the partial launch through tagged words where the plan
+    keeps whole bands), random stored rows, k and layout."""
+    rng = np.random.default_rng(70000 + c)
+    k = int(rng.integers(2, 5))
+    nb = int(rng.integers(16, 61))
+    rows = int(rng.choice([33, 96, 300, 1000, 2050, 4111]))
+    il = 2 if (nb % 2 == 0 and rng.random() < 0.3) else 0
+    return synth.Shape(0, 256, 12, k, rows, 256 * nb, il), "scatter", 1
+
+
+@pytest.mark.parametrize("c", range(12))
+def test_random_geometry_scatter_tagged(gpu_lib, c):
+    run_case(gpu_lib, 4000 + c, *draw_scatter_tagged_case(c))
 
 
 def run_case(gpu_lib, c, sh, op, M):
