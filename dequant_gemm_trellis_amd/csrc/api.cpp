@@ -101,9 +101,7 @@ int trellis_lut_upload(const float* host_lut, int32_t entries, float* dev_lut, h
     for (int i = 0; i < entries; ++i)
         if (!isfinite(host_lut[i])) return TRELLIS_ERR_LUT;
     const size_t bytes = static_cast<size_t>(entries) * sizeof(float);
-    if (hipMemcpyAsync(dev_lut, host_lut, bytes, hipMemcpyHostToDevice, stream) != hipSuccess)
-        return TRELLIS_ERR_HIP;
-    return status_of(hipStreamSynchronize(stream));
+    return status_of(hipMemcpyAsync(dev_lut, host_lut, bytes, hipMemcpyHostToDevice, stream));
 }
 
 int trellis_gemv(const uint16_t* x, const uint32_t* codes, const float* scales, const float* lut,

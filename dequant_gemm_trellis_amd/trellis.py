@@ -138,8 +138,10 @@ def lut_upload(host_lut, dev_lut: torch.Tensor | None = None, device=None,
     h = np.ascontiguousarray(host_lut, dtype=np.float32)
     if dev_lut is None:
         dev_lut = torch.empty(h.size, dtype=torch.float32, device=device or "cuda")
+    s = stream if stream is not None else torch.cuda.current_stream()
     _check("trellis_lut_upload", _lib.trellis_lut_upload(
-        _vp(h.ctypes.data), h.size, _dev(dev_lut), _stream(stream)))
+        _vp(h.ctypes.data), h.size, _dev(dev_lut), _vp(s.cuda_stream)))
+    s.synchronize()  # the copy is stream-ordered and h is this call's own array
     return dev_lut
 
 

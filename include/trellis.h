@@ -104,8 +104,11 @@ enum {
  * buffer `dev_lut` (4 * entries bytes, 16-byte aligned). The codebook plays
  * the part of the pages' precise host LUT (page 59 scatter.ts stages `lut`
  * into threadgroup memory). entries must be 4096 (2^L with L = 12) and every
- * entry finite, else TRELLIS_ERR_LUT. The copy is ordered on `stream`; the
- * call waits for it, so `host_lut` may be freed on return.
+ * entry finite, else TRELLIS_ERR_LUT (checked on the host before anything is
+ * enqueued). The copy is enqueued on `stream` like any other work and the
+ * call returns without waiting: `host_lut` must stay valid and unchanged
+ * until the stream has run the copy (synchronise it before freeing or
+ * reusing the host array).
  */
 int trellis_lut_upload(const float *host_lut, int32_t entries, float *dev_lut,
                        hipStream_t stream);
