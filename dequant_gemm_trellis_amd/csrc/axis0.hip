@@ -634,12 +634,14 @@ A0Plan axis0_plan(int R, int C) {
     return A0Plan{(waves + v - 1) / v, nr, v};
 }
 
-// Whether the scatter (M = 1) sums its partials in the partial kernel itself
-// (whole bands only, at most kFusedMaxBands per tile, and at most half the
-// static array's partials, so that its 8-byte tagged words still fit there).
-// The plan depends on R, C and M only.
+// Whether the partial kernel sums its partials itself (M <= 8; whole bands
+// only, at most kFusedMaxBands per tile, and at most half the static array's
+// partials, so that the scatter's 8-byte tagged words still fit there). The
+// plan depends on R, C and M only.
 bool axis0_fused(int R, int C, int M) {
-    if (M != 1) return false;  // at M = 32 the tagged words measured 3 us slower per layer
+    // measured at 17408 x 5120: M = 2 / 4 / 8 1.2 / 1.3 / 0.5 us faster than
+    // the reduce launch, M = 16 0.8 us and M = 32 3 us slower
+    if (M > 8) return false;
     const A0Plan pl = axis0_plan(R, C);
     const A0Bands bd(pl.ranges, pl.waves, pl.ranges / pl.waves, C / kTileCols);
     return pl.ranges % pl.waves == 0 && pl.ranges / pl.waves <= kFusedMaxBands &&

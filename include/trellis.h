@@ -163,7 +163,8 @@ int trellis_gemv_dual(const uint16_t *x, const uint32_t *codes_a, const float *s
  * partial per workgroup and column tile it sums, at most 4096 of them); its
  * contents on entry do not matter and are overwritten. Where every
  * workgroup owns a whole band of ranges of one tile and a tile has at most
- * 8 bands (e.g. 17408 -> 5120), the bands meet in the same launch: each
+ * 8 bands (e.g. 17408 -> 5120), the bands meet in the same launch (here and
+ * in the axis-0 prefill up to M = 8): each
  * partial travels as 8-byte words tagged with the call, and a workgroup that
  * finds all of its tile's partials current sums them in range order (the
  * partials take 8 bytes per value then); otherwise, and under stream

@@ -210,6 +210,9 @@ def test_workspace_bytes(T):
     # tagged words, the prefill in a reduce launch from float32 partials
     assert T.workspace_bytes(g0, 1, T.OP_GEMV_SCATTER) == 240 * 128 * 8
     assert T.workspace_bytes(g0, 32, T.OP_PREFILL) == 240 * 32 * 128 * 4
+    # the prefill sums in the launch too up to M = 8
+    assert T.workspace_bytes(g0, 8, T.OP_PREFILL) == 240 * 8 * 128 * 8
+    assert T.workspace_bytes(g0, 9, T.OP_PREFILL) == 240 * 9 * 128 * 4
     # 136 tiles (5120 x 17408 stored): one band per tile would leave 120 of
     # 256 compute units idle, so the finer plan: 15 ranges per tile, one whole
     # band of 8 per tile, then 7 per tile packed 8 to a workgroup (a tile's 7

@@ -223,3 +223,40 @@ def test_scatter_tagged_sum_under_capture(gpu_lib):
         T.gemv_scatter(xv, d.codes, d.scales, d.lut, FUSED, workspace=ws, y=y)
         torch.cuda.synchronize()
         assert np.array_equal(bf16_bits(y), eager), r
+
+
+@pytest.mark.parametrize("M", [2, 5, 8])
+def test_axis0_prefill_tagged_sum(gpu_lib, M):
+    """The axis-0 prefill at M <= 8 sums its bands in the partial launch too:
+    against the oracle, on a workspace of all-ones bytes, bit-identical over
+    three calls and to a call under stream capture (float partials, then the
+    reduce launch in the same band order)."""
+    T = gpu_lib
+    n = T.workspace_bytes(FUSED, M, T.OP_PREFILL)
+    assert n == 240 * M * 128 * 8, n  # tagged words
+    p = synth.make_problem(FUSED, M, CFG["test"], proj=2600 + M)
+    d = Dev(p, T)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda").view(torch.float32)
+    y = torch.empty((M, 5120), dtype=torch.bfloat16, device="cuda")
+    say(f"axis-0 prefill tagged sum M={M}")
+    T.prefill(d.x, d.codes, d.scales, d.lut, FUSED, workspace=ws, y=y)
+    torch.cuda.synchronize()
+    first = bf16_bits(y)
+    assert gate(bf16_to_f64(y), oracle_y(p)) <= TOL
+    for _ in range(2):
+        T.prefill(d.x, d.codes, d.scales, d.lut, FUSED, workspace=ws, y=y)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(y), first)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        T.prefill(d.x, d.codes, d.scales, d.lut, FUSED, workspace=ws, y=y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        T.prefill(d.x, d.codes, d.scales, d.lut, FUSED, workspace=ws, y=y)
+    y.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(y), first)
