@@ -462,17 +462,22 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
     }
     if constexpr (FUSED) {
         // Every band's partial of this tile, as tagged words: where all carry
-        // this call's tag, sum them in band order. The thread that checks a
-        // column last sees every band's store (each completed before its
-        // writer's own check), so every column is written at least once;
-        // threads that find all current at once write the same bits.
+        // this call's tag, sum them in band order. The workgroup that checks
+        // last sees every band's store (each completed before its writer's
+        // own check), so every output is written at least once; workgroups
+        // that find all current at once write the same bits. A wave sums only
+        // when all its outputs are current (the writers are the same for all
+        // of a tile's outputs), so a stale word could pass only if a whole
+        // wave's words matched this call's tags.
         __builtin_amdgcn_s_waitcnt(0);
         const unsigned long long* const pw = reinterpret_cast<const unsigned long long*>(partial);
         const int t = L - kb * tiles;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-            for (int idx = tid; idx < 16 * kTileCols; idx += kA0Threads) {
-                const int m = idx / kTileCols, col = idx % kTileCols;
+#pragma unroll
+            for (int it = 0; it < 16 * kTileCols / kA0Threads; ++it) {
+                const int idx = tid + it * kA0Threads;
+                const int m = idx / kTileCols, col = idx % kTileCols;  // m uniform in a wave
                 const int mm = 16 * mt + m;
                 if (mm >= M) continue;
                 unsigned long long wv[kFusedMaxBands];
@@ -485,7 +490,7 @@ __global__ __launch_bounds__(kA0Threads) void axis0_mma_kernel(
 #pragma unroll
                 for (int b = 0; b < kFusedMaxBands; ++b)
                     stale |= b < nf && static_cast<unsigned int>(wv[b] >> 32) != slot_tag(tag, bd.band_slot(b, t));
-                if (stale) continue;
+                if (__builtin_amdgcn_ballot_w64(stale) != 0) continue;  // a later workgroup sums
                 float sum = 0.f;
 #pragma unroll
                 for (int b = 0; b < kFusedMaxBands; ++b)
