@@ -24,7 +24,9 @@
 //
 // Work mapping. The grid is persistent (one workgroup per compute unit),
 // workgroup g owning rows [g N / G, (g+1) N / G), at most kGroups
-// 16-row groups. A task is one group x one 256-weight block; the workgroup's
+// 16-row groups; or, given a workspace, whole groups only plus a block range
+// of one leftover group (the balanced plan, SplitArgs). A task is one group x
+// one 256-weight block; the workgroup's
 // tasks are numbered block-major (all groups of block 0, then block 1, ...)
 // and each wave takes a contiguous range of them. A wave thus meets only a
 // few blocks and loads their activation fragments once per block, reusing
