@@ -33,8 +33,9 @@
 // so neighbouring tiles, whose code rows share cache lines, read the same rows
 // at the same time. A workgroup sums its waves' tiles in LDS in wave order, one
 // partial per run of waves on one tile, and the reduce kernel sums a tile's
-// partials in range order. Every order is fixed, so repeated calls give
-// identical bits.
+// partials in range order; at M <= 8 with whole bands the partial kernel does
+// that sum itself (FUSED: the bands meet as call-tagged words in the
+// workspace). Every order is fixed, so repeated calls give identical bits.
 //
 // The decode table (the k = 2 pair table, or eight bank-partitioned copies of
 // the codebook for k = 3, 4) is staged once per workgroup, and the next
