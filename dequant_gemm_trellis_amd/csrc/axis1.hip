@@ -94,7 +94,12 @@ struct PrefillLds {
     static constexpr int waves = PrefillShape<MT>::waves;
     static constexpr int lines = tab_floats > kLutEntries ? 1 : 4;
     static constexpr int slot_chunks = DIRECT ? 0 : MT * lines * 16 * 8;
-    static constexpr int decode_floats = tab_floats + waves * slot_chunks * 4;
+    // direct activations: a per-wave area for the first block's fragments,
+    // fetched coalesced and passed through LDS two lines at a time (at
+    // M = 9..16 the per-lane A-layout loads touch 64 cache lines per
+    // instruction, which cost the prologue about 1 us)
+    static constexpr int pro_chunks = DIRECT ? 2 * 16 * 8 : 0;
+    static constexpr int decode_floats = tab_floats + waves * (slot_chunks + pro_chunks) * 4;
     static constexpr int part_floats = waves * KG * 256;  // one M tile of wave partials
     static constexpr int floats = decode_floats > part_floats ? decode_floats : part_floats;
 };
@@ -396,7 +401,8 @@ __device__ __forceinline__ void load_x_block(XFrags<MT>& xf, u32x4* __restrict__
     // A one-line slot of both M tiles holds two lines of one: two lines are
     // fetched at a time, then pass through the slot one M tile at a time, so
     // that half the lanes (the two lines' groups) read at each round.
-    static_assert(MT == 2, "the one-line slot is sized for two M tiles");
+    // (the slot holds two lines of 16 rows: the one-line slot of two M tiles,
+    // or the prologue area of one)
 #pragma unroll
     for (int l0 = 0; l0 < 4; l0 += 2) {
         u32x4 raw[MT][2][2];
@@ -646,7 +652,8 @@ __device__ __forceinline__ float silu_f32(float v) { return v / (1.0f + expf(-v)
 //   restages the table from the up codebook, runs the same tasks on the up
 //   projection (b operands) and writes y_a[m][n] = bf16(silu(g) * u), the same
 //   thread reducing the same output in both phases.
-template <int K, int MT, bool DIRECT, bool PAIRS, int KG, bool SWIGLU, bool FOLD, bool SPLIT>
+template <int K, int MT, bool DIRECT, bool PAIRS, int KG, bool SWIGLU, bool FOLD, bool SPLIT,
+          bool STAGE1 = false>
 __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes_a,
     const float* __restrict__ scales_a, const float* __restrict__ lut_a,
@@ -654,6 +661,7 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     const float* __restrict__ scales_b, const float* __restrict__ lut_b,
     uint16_t* __restrict__ y_b, int G0, CodeLayout lay, int N, int nb, int M, SplitArgs sp) {
     static_assert(!SPLIT || (!SWIGLU && !FOLD), "the split plan serves the single projection");
+    static_assert(!STAGE1 || (DIRECT && !FOLD), "the staged first block serves the direct layout");
     constexpr int kThreadsP = PrefillShape<MT>::threads, kWaves = PrefillShape<MT>::waves;
     using Lds = PrefillLds<K, MT, DIRECT, KG>;
     __shared__ __attribute__((aligned(16))) float lds[Lds::floats];
@@ -742,10 +750,18 @@ __global__ __launch_bounds__(PrefillShape<MT>::threads) void axis1_prefill_kerne
     load_task_opaque<K, PAIRS, false, FOLD, SPLIT>(ta, cx, cur, tend);
     load_task_opaque<K, PAIRS, false, FOLD, SPLIT>(tb, cx, cur, tend);
     XFrags<MT> xn;
-    if constexpr (DIRECT) load_x_frags_opaque<MT>(xn, xs.xa, lane_block(xs, ta.b));
+    // The first block's fragments: loaded directly here, or (STAGE1, M > 8,
+    // where a direct load touches 64 cache lines per instruction) coalesced
+    // through this wave's LDS area after the barrier.
+    constexpr bool kStagedFirst = STAGE1;
+    if constexpr (DIRECT && !kStagedFirst) load_x_frags_opaque<MT>(xn, xs.xa, lane_block(xs, ta.b));
     asm volatile("" ::: "memory");
     Lds::Table::store(tsrc, tab);
     __syncthreads();
+    if constexpr (kStagedFirst) {
+        u32x4* const area = reinterpret_cast<u32x4*>(lds + Lds::tab_floats) + wave * Lds::pro_chunks;
+        load_x_block<MT, 2>(xn, area, xs.xrows, ta.b, lane, j, c);
+    }
 
     // Three register sets rotate: the words of the next two tasks are in
     // flight while one is decoded. (No branch around the loop: the prologue's
@@ -1131,15 +1147,27 @@ hipError_t launch_prefill(bool fold, int G, int G0, hipStream_t st, const uint16
     // Row-major iff a row's blocks are contiguous (with two blocks per row the
     // two layouts coincide).
     const bool rowmajor = lay.row_words == static_cast<uint64_t>(nb) * Bits<K>::wpb;
+    // the first block staged (coalesced) with direct activations at M = 9..16:
+    // measured 0.2-0.55 us faster there, 0.3-0.8 us slower at M = 5..8
+    const bool stage1 = DIRECT && M > 8;
     if constexpr (!SWIGLU && KG == kGroups && !(K == 2 && MT == 2)) {
-        if (split)
+        if (split) {
+            if constexpr (DIRECT) {
+                if (stage1)
+                    return rowmajor ? go(axis1_prefill_kernel<K, MT, DIRECT, false, KG, false, false, true, true>)
+                                    : go(axis1_prefill_kernel<K, MT, DIRECT, true, KG, false, false, true, true>);
+            }
             return rowmajor ? go(axis1_prefill_kernel<K, MT, DIRECT, false, KG, false, false, true>)
                             : go(axis1_prefill_kernel<K, MT, DIRECT, true, KG, false, false, true>);
+        }
     }
     if constexpr (DIRECT && MT == 1) {
         if (fold && M <= 8)
             return rowmajor ? go(axis1_prefill_kernel<K, MT, DIRECT, false, KG, SWIGLU, true, false>)
                             : go(axis1_prefill_kernel<K, MT, DIRECT, true, KG, SWIGLU, true, false>);
+        if (stage1)
+            return rowmajor ? go(axis1_prefill_kernel<K, MT, DIRECT, false, KG, SWIGLU, false, false, true>)
+                            : go(axis1_prefill_kernel<K, MT, DIRECT, true, KG, SWIGLU, false, false, true>);
     }
     return rowmajor ? go(axis1_prefill_kernel<K, MT, DIRECT, false, KG, SWIGLU, false, false>)
                     : go(axis1_prefill_kernel<K, MT, DIRECT, true, KG, SWIGLU, false, false>);
