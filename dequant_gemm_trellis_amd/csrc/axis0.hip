@@ -566,6 +566,36 @@ __global__ __launch_bounds__(kWave) void split_reduce_wave_kernel(
     y[i0 + lane] = round_bf16(s);
 }
 
+// The same sum with four adjacent outputs per lane (16-byte partial loads,
+// 8-byte stores): one wave per 256 outputs of one activation row, i.e. two
+// column tiles, C a multiple of 256.
+__global__ __launch_bounds__(kWave) void split_reduce_wave4_kernel(
+    const float* __restrict__ partial, uint16_t* __restrict__ y, int M, int C, int nr, int nv,
+    int nf) {
+    const int lane = threadIdx.x;
+    const int i0 = blockIdx.x * 256;
+    const int m = i0 / C, col = i0 - m * C + 4 * lane;
+    const int tiles = C / kTileCols, t = col / kTileCols;
+    const A0Bands bd(nr, nv, nf, tiles);
+    const size_t mstride = static_cast<size_t>(M) * kTileCols;
+    const float* const src = partial + static_cast<size_t>(m) * kTileCols + col % kTileCols;
+    const int n = bd.nf + (bd.rr ? bd.tw : 0);  // <= kReduceOneWave
+    floatx4 v[kReduceOneWave];
+#pragma unroll
+    for (int u = 0; u < kReduceOneWave; ++u) {
+        const int sl = u < bd.nf ? bd.band_slot(u, t) : bd.tail_slot(t) + (u - bd.nf);
+        v[u] = u < n ? *reinterpret_cast<const floatx4*>(src + static_cast<size_t>(sl) * mstride)
+                     : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kReduceOneWave; ++u)
+        if (u < n) s += v[u];
+    const uint32_t lo = round_bf16(s[0]) | (static_cast<uint32_t>(round_bf16(s[1])) << 16);
+    const uint32_t hi = round_bf16(s[2]) | (static_cast<uint32_t>(round_bf16(s[3])) << 16);
+    *reinterpret_cast<uint2*>(y + i0 + 4 * lane) = make_uint2(lo, hi);
+}
+
 template <int K, int MT, bool VEC, bool BUF>
 hipError_t launch_axis0_k(const uint16_t* x, int M, const uint32_t* codes, CodeLayout lay,
                           const float* scales, const float* lut, float* partial, int R, int C,
@@ -688,8 +718,13 @@ hipError_t launch_axis0(const uint16_t* x, int M, const uint32_t* codes, CodeLay
                              C, pl.ranges, pl.waves, nf);
     // One wave per 64 outputs where there are enough of them to fill the chip
     // several times over (measured: M = 32 at 5120 outputs 0.7 us faster per
-    // MLP layer); below that, four waves per 64 outputs keep fewer dependent
-    // loads per lane (M = 1: the one-wave form was 0.2 us slower).
+    // MLP layer), four adjacent outputs per lane where a wave's 256 stay in
+    // one activation row (a further 0.1-0.2 us there); below that, four waves
+    // per 64 outputs keep fewer dependent loads per lane (M = 1: the one-wave
+    // form was 0.2 us slower).
+    if (terms <= kReduceOneWave && MC / 64 >= 1024 && C % 256 == 0)
+        return launch_kernel(split_reduce_wave4_kernel, dim3(MC / 256), dim3(kWave), st, partial, y,
+                             M, C, pl.ranges, pl.waves, nf);
     if (terms <= kReduceOneWave && MC / 64 >= 1024)
         return launch_kernel(split_reduce_wave_kernel, dim3(MC / 64), dim3(kWave), st, partial, y, M,
                              C, pl.ranges, pl.waves, nf);
